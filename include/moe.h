@@ -1,0 +1,158 @@
+/*
+ * moe.h -- C ABI of the MoE-layer forward on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer (DeepSeek-V3/R1 style), as stated in Perplexity's "Lower latency
+ * and higher throughput with multi-node DeepSeek deployment", section
+ * "Expert parallelism": every token is sent to k *different* routed experts,
+ * their outputs are summed with weights, and the output of one shared expert,
+ * which every token also goes through, is added.  The router is, after the
+ * vLLM DeepSeek-V4.1-Flash article (section "Kernels", item "Mega-Gate"),
+ * gate GEMM -> expert scoring -> bias -> top-k.  Dense per-expert execution
+ * needs the routing aggregated per expert (Perplexity, section "MoE
+ * router"), and every kernel reads the per-expert token counts on the device
+ * instead of syncing them to the host (Perplexity, section "Quantization",
+ * paragraph on the MoE router under CUDA graphs).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *   never allocates, frees or synchronises, and keeps no state between calls
+ *   apart from a thread-local error string.  Arrays are dense row-major.
+ * - Work is enqueued on `hip_stream` (a hipStream_t; NULL = default stream)
+ *   and the call returns; faults inside kernels surface at the caller's next
+ *   synchronisation.  No call reads device memory on the host.
+ * - Every argument is validated on the host BEFORE anything is enqueued: a
+ *   call that returns an error has launched nothing and written nothing.
+ * - T == 0 returns MOE_OK and enqueues nothing.
+ * - "Pairs": p = t*k + j is the j-th chosen expert of token t; P = T*k.
+ * - Weight matrices are [out_features, in_features] row-major.
+ * - The library never prints, throws across the ABI or aborts.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null required pointer, bad shape, k out of range, misaligned */
+  MOE_ERR_UNSUPPORTED = 2, /* valid layer the kernels do not implement (listed per field) */
+  MOE_ERR_WORKSPACE = 3,   /* ws_bytes smaller than moe_workspace_size() */
+  MOE_ERR_HIP = 4          /* a HIP launch failed; moe_last_error() has the detail */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/* Expert scoring applied to the gate logits (a reading of "expert scoring"):
+ * softmax over all E experts, or an elementwise sigmoid. */
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
+
+typedef struct {
+  int32_t T;           /* tokens, >= 0 */
+  int32_t H;           /* hidden size; multiple of 64 (of quant_block for FP8) */
+  int32_t E;           /* routed experts in this call, 1..256 */
+  int32_t k;           /* experts per token, 1..min(E, 32) */
+  int32_t I;           /* routed-expert intermediate size; multiple of 64 (quant_block for FP8) */
+  int32_t I_shared;    /* shared-expert intermediate size: 0 (none) or I */
+  int32_t score;       /* moe_score */
+  int32_t act_dtype;   /* x, gate weight and y: MOE_F32 or MOE_BF16 */
+  int32_t w_dtype;     /* expert weights: MOE_F32 (with act F32), MOE_BF16 (act BF16),
+                          MOE_FP8_E4M3 (act BF16) */
+  int32_t quant_block; /* FP8 block width along K: 128; ignored otherwise */
+  float routed_scale;  /* multiplies the renormalised combine weights (1.0) */
+  int32_t n_group;     /* group-limited routing: only n_group = topk_group = 1 */
+  int32_t topk_group;
+} moe_cfg;
+
+/* Expert weights.  Routed: w13 [E, 2I, H] (rows [0,I) = gate projection W1,
+ * rows [I,2I) = up projection W3), w2 [E, H, I].  Shared: ws13 [2I, H],
+ * ws2 [H, I] (NULL when I_shared == 0).  For MOE_FP8_E4M3 the *_scale arrays
+ * hold one fp32 scale per row per quant_block columns ([.., rows, cols/128]);
+ * the value of a weight is e4m3(code) * scale.  Scales are NULL otherwise. */
+typedef struct {
+  const void* w13;
+  const float* w13_scale;
+  const void* w2;
+  const float* w2_scale;
+  const void* ws13;
+  const float* ws13_scale;
+  const void* ws2;
+  const float* ws2_scale;
+} moe_weights;
+
+/* Human-readable name of a moe_status value (static string). */
+const char* moe_status_str(int status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Bytes of device workspace that every call below needs for this layer
+ * (an upper bound independent of the routing).  Returns a moe_status. */
+int moe_workspace_size(const moe_cfg* cfg, size_t* bytes);
+
+/* Router (steps: gate GEMM, scoring, selection bias, top-k, weights).
+ *   x        [T, H] act_dtype          w_gate [E, H] act_dtype
+ *   sel_bias [E] fp32 or NULL: added to the scores for choosing experts only
+ *   topk_idx [T, k] int32 out: chosen experts, descending biased score,
+ *            equal scores ordered by the lower expert index
+ *   topk_w   [T, k] fp32 out: unbiased scores of the chosen experts divided
+ *            by their sum, times routed_scale
+ * Logits accumulate in fp32 in a fixed order (bitwise reproducible). */
+int moe_route(const moe_cfg* cfg, const void* x, const void* w_gate, const float* sel_bias,
+              int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Dispatch: per-expert aggregation of the routing (Perplexity, "MoE router").
+ *   topk_idx    [T, k] int32 in, every value in [0, E)
+ *   counts      [E] int32 out: pairs routed to each expert
+ *   offsets     [E+1] int32 out: exclusive running sum, offsets[E] = T*k
+ *   sorted_pair [T*k] int32 out: for each expert, its pair ids in ascending
+ *               order, at positions offsets[e] .. offsets[e+1]-1
+ *   pair_slot   [T*k] int32 out: inverse permutation (sorted_pair[pair_slot[p]] = p)
+ * Bitwise deterministic. */
+int moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                 int32_t* sorted_pair, int32_t* pair_slot, void* ws, size_t ws_bytes,
+                 void* hip_stream);
+
+/* Per-row block quantisation to OCP FP8 E4M3 (Perplexity, "Quantization":
+ * activations get one scale per 128-element block, computed on the fly).
+ *   in     [rows, cols] MOE_BF16 or MOE_F32 (in_dtype); cols % block == 0
+ *   codes  [rows, cols] uint8 out; scales [rows, cols/block] fp32 out
+ * scale = fp32(amax/448) (1 for an all-zero block); code = e4m3 of
+ * fp32(v/scale), round to nearest even, saturating at +-448. */
+int moe_quantize_fp8(int32_t rows, int32_t cols, int32_t block, const void* in, int32_t in_dtype,
+                     uint8_t* codes, float* scales, void* hip_stream);
+
+/* Expert FFNs: every routed expert's SwiGLU over its dispatched rows (a
+ * grouped GEMM; Perplexity, "GroupGEMM"), and the shared expert over all T
+ * rows.  SwiGLU(a) = (SiLU(a W1^T) * (a W3^T)) W2^T.  For FP8 weights, x and
+ * the SwiGLU output are block-quantised per row per quant_block first.
+ *   x           [T, H] act_dtype; offsets / sorted_pair from moe_dispatch
+ *   y_sorted    [T*k, H] fp32 out: row s = expert output of pair sorted_pair[s]
+ *   y_shared    [T, H] fp32 out (NULL iff I_shared == 0)
+ * Per-expert row counts are read on the device (no host sync). */
+int moe_expert_ffn(const moe_cfg* cfg, const void* x, const int32_t* offsets,
+                   const int32_t* sorted_pair, const moe_weights* w, float* y_sorted,
+                   float* y_shared, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Combine: y[t] = y_shared[t] + sum_j topk_w[t,j] * y_sorted[pair_slot[t*k+j]],
+ * accumulated in fp32 in the order shared, j = 0..k-1 (deterministic).
+ *   y_shared may be NULL (treated as 0); y [T, H] act_dtype out. */
+int moe_combine(const moe_cfg* cfg, const float* y_sorted, const float* y_shared,
+                const int32_t* pair_slot, const float* topk_w, void* y, void* hip_stream);
+
+/* The whole layer: route -> dispatch -> expert FFN -> combine, on one stream.
+ *   y [T, H] act_dtype out.  topk_idx_out [T,k], topk_w_out [T,k] and
+ *   counts_out [E] are optional copies of the routing (NULL to skip). */
+int moe_forward(const moe_cfg* cfg, const void* x, const void* w_gate, const float* sel_bias,
+                const moe_weights* w, void* y, int32_t* topk_idx_out, float* topk_w_out,
+                int32_t* counts_out, void* ws, size_t ws_bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,240 @@
+"""Thin ctypes binding of libmoe.so (include/moe.h).
+
+Argument marshalling only: dtype/shape/device checks, output allocation with
+torch, and the call on torch's current HIP stream.  Every step of the layer
+runs in the library's HIP kernels; there is no fallback.  If the library has
+not been built, every call raises ``MoELibraryMissing``.
+"""
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("MOE_LIB", os.path.join(_PKG, "libmoe.so"))
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = range(2)
+
+EXPORTS = ("moe_status_str", "moe_last_error", "moe_workspace_size", "moe_route", "moe_dispatch",
+           "moe_quantize_fp8", "moe_expert_ffn", "moe_combine", "moe_forward")
+
+
+class MoELibraryMissing(RuntimeError):
+    pass
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__(f"{status_str(status)}: {detail}")
+        self.status = status
+
+
+class MoeCfg(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("I", ctypes.c_int32), ("I_shared", ctypes.c_int32), ("score", ctypes.c_int32),
+                ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32), ("quant_block", ctypes.c_int32),
+                ("routed_scale", ctypes.c_float), ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32)]
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [("w13", ctypes.c_void_p), ("w13_scale", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("w2_scale", ctypes.c_void_p), ("ws13", ctypes.c_void_p), ("ws13_scale", ctypes.c_void_p),
+                ("ws2", ctypes.c_void_p), ("ws2_scale", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmoe.so once and declare its prototypes (works without a GPU)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise MoELibraryMissing(f"{path} is not built; run `python -m mixture_experts_layer_11_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    cfgp = ctypes.POINTER(MoeCfg)
+    wp = ctypes.POINTER(MoeWeights)
+    lib.moe_status_str.restype = ctypes.c_char_p
+    lib.moe_status_str.argtypes = [ctypes.c_int]
+    lib.moe_last_error.restype = ctypes.c_char_p
+    lib.moe_last_error.argtypes = []
+    lib.moe_workspace_size.argtypes = [cfgp, ctypes.POINTER(SZ)]
+    lib.moe_route.argtypes = [cfgp, P, P, P, P, P, P, SZ, P]
+    lib.moe_dispatch.argtypes = [cfgp, P, P, P, P, P, P, SZ, P]
+    lib.moe_quantize_fp8.argtypes = [I32, I32, I32, P, I32, P, P, P]
+    lib.moe_expert_ffn.argtypes = [cfgp, P, P, P, wp, P, P, P, SZ, P]
+    lib.moe_combine.argtypes = [cfgp, P, P, P, P, P, P]
+    lib.moe_forward.argtypes = [cfgp, P, P, P, wp, P, P, P, P, P, SZ, P]
+    for name in EXPORTS[2:]:
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().moe_status_str(status).decode()
+
+
+def last_error() -> str:
+    return load_library().moe_last_error().decode()
+
+
+def _check(status):
+    if status != MOE_OK:
+        raise MoEError(status, last_error())
+
+
+# --------------------------------------------------------------------------- configuration
+
+_DT = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
+_SCORE = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}
+
+
+def make_cfg(T, H, E, k, I, I_shared, score="sigmoid", act_dtype="bf16", w_dtype="bf16", quant_block=128,
+             routed_scale=1.0, n_group=1, topk_group=1) -> MoeCfg:
+    return MoeCfg(int(T), int(H), int(E), int(k), int(I), int(I_shared), _SCORE[score] if isinstance(score, str) else score,
+                  _DT[act_dtype] if isinstance(act_dtype, str) else act_dtype,
+                  _DT[w_dtype] if isinstance(w_dtype, str) else w_dtype, int(quant_block), float(routed_scale),
+                  int(n_group), int(topk_group))
+
+
+def cfg_from(c) -> MoeCfg:
+    """MoeCfg from any object with the layer's fields (T, H, E, k, I, I_shared, score, act_dtype, w_dtype)."""
+    return make_cfg(c.T, c.H, c.E, c.k, c.I, c.I_shared, c.score, c.act_dtype, c.w_dtype,
+                    getattr(c, "quant_block", 128))
+
+
+def workspace_size(cfg: MoeCfg) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().moe_workspace_size(ctypes.byref(cfg), ctypes.byref(n)))
+    return n.value
+
+
+def alloc_workspace(cfg: MoeCfg, device="cuda") -> torch.Tensor:
+    return torch.empty(max(workspace_size(cfg), 16), dtype=torch.uint8, device=device)
+
+
+# --------------------------------------------------------------------------- tensors
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoe must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+@dataclass
+class Weights:
+    """Expert weights in the library's layout (see include/moe.h)."""
+    w13: torch.Tensor
+    w2: torch.Tensor
+    ws13: Optional[torch.Tensor] = None
+    ws2: Optional[torch.Tensor] = None
+    w13_scale: Optional[torch.Tensor] = None
+    w2_scale: Optional[torch.Tensor] = None
+    ws13_scale: Optional[torch.Tensor] = None
+    ws2_scale: Optional[torch.Tensor] = None
+
+    @staticmethod
+    def from_inputs(inp) -> "Weights":
+        return Weights(inp.w13, inp.w2, inp.ws13, inp.ws2, inp.w13_scale, inp.w2_scale, inp.ws13_scale,
+                       inp.ws2_scale)
+
+    def c_struct(self) -> MoeWeights:
+        return MoeWeights(_ptr(self.w13), _ptr(self.w13_scale), _ptr(self.w2), _ptr(self.w2_scale),
+                          _ptr(self.ws13), _ptr(self.ws13_scale), _ptr(self.ws2), _ptr(self.ws2_scale))
+
+
+def _out(shape, dtype, device):
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _act_torch(cfg: MoeCfg):
+    return torch.float32 if cfg.act_dtype == MOE_F32 else torch.bfloat16
+
+
+# --------------------------------------------------------------------------- entry points
+
+def moe_route(cfg: MoeCfg, x, w_gate, sel_bias=None, ws=None, topk_idx=None, topk_w=None, stream=None):
+    lib = load_library()
+    dev = x.device
+    topk_idx = topk_idx if topk_idx is not None else _out((cfg.T, cfg.k), torch.int32, dev)
+    topk_w = topk_w if topk_w is not None else _out((cfg.T, cfg.k), torch.float32, dev)
+    ws = ws if ws is not None else alloc_workspace(cfg, dev)
+    _check(lib.moe_route(ctypes.byref(cfg), _ptr(x), _ptr(w_gate), _ptr(sel_bias), _ptr(topk_idx), _ptr(topk_w),
+                         _ptr(ws), ws.numel(), _stream(stream)))
+    return topk_idx, topk_w
+
+
+def moe_dispatch(cfg: MoeCfg, topk_idx, ws=None, stream=None):
+    lib = load_library()
+    dev = topk_idx.device
+    P = cfg.T * cfg.k
+    counts = _out((cfg.E,), torch.int32, dev)
+    offsets = _out((cfg.E + 1,), torch.int32, dev)
+    sorted_pair = _out((P,), torch.int32, dev)
+    pair_slot = _out((P,), torch.int32, dev)
+    ws = ws if ws is not None else alloc_workspace(cfg, dev)
+    _check(lib.moe_dispatch(ctypes.byref(cfg), _ptr(topk_idx), _ptr(counts), _ptr(offsets), _ptr(sorted_pair),
+                            _ptr(pair_slot), _ptr(ws), ws.numel(), _stream(stream)))
+    return counts, offsets, sorted_pair, pair_slot
+
+
+def moe_quantize_fp8(inp: torch.Tensor, block: int = 128, stream=None):
+    lib = load_library()
+    rows, cols = inp.shape
+    codes = _out((rows, cols), torch.uint8, inp.device)
+    scales = _out((rows, cols // block), torch.float32, inp.device)
+    dt = MOE_BF16 if inp.dtype == torch.bfloat16 else MOE_F32 if inp.dtype == torch.float32 else -1
+    _check(lib.moe_quantize_fp8(rows, cols, block, _ptr(inp), dt, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def moe_expert_ffn(cfg: MoeCfg, x, offsets, sorted_pair, weights: Weights, ws=None, stream=None):
+    lib = load_library()
+    dev = x.device
+    y_sorted = _out((cfg.T * cfg.k, cfg.H), torch.float32, dev)
+    y_shared = _out((cfg.T, cfg.H), torch.float32, dev) if cfg.I_shared > 0 else None
+    ws = ws if ws is not None else alloc_workspace(cfg, dev)
+    w = weights.c_struct()
+    _check(lib.moe_expert_ffn(ctypes.byref(cfg), _ptr(x), _ptr(offsets), _ptr(sorted_pair), ctypes.byref(w),
+                              _ptr(y_sorted), _ptr(y_shared), _ptr(ws), ws.numel(), _stream(stream)))
+    return y_sorted, y_shared
+
+
+def moe_combine(cfg: MoeCfg, y_sorted, y_shared, pair_slot, topk_w, stream=None):
+    lib = load_library()
+    y = _out((cfg.T, cfg.H), _act_torch(cfg), y_sorted.device)
+    _check(lib.moe_combine(ctypes.byref(cfg), _ptr(y_sorted), _ptr(y_shared), _ptr(pair_slot), _ptr(topk_w),
+                           _ptr(y), _stream(stream)))
+    return y
+
+
+def moe_forward(cfg: MoeCfg, x, w_gate, sel_bias, weights: Weights, ws=None, y=None, return_routing=False,
+                stream=None):
+    lib = load_library()
+    dev = x.device
+    y = y if y is not None else _out((cfg.T, cfg.H), _act_torch(cfg), dev)
+    ws = ws if ws is not None else alloc_workspace(cfg, dev)
+    idx = wt = counts = None
+    if return_routing:
+        idx = _out((cfg.T, cfg.k), torch.int32, dev)
+        wt = _out((cfg.T, cfg.k), torch.float32, dev)
+        counts = _out((cfg.E,), torch.int32, dev)
+    w = weights.c_struct()
+    _check(lib.moe_forward(ctypes.byref(cfg), _ptr(x), _ptr(w_gate), _ptr(sel_bias), ctypes.byref(w), _ptr(y),
+                           _ptr(idx), _ptr(wt), _ptr(counts), _ptr(ws), ws.numel(), _stream(stream)))
+    return (y, idx, wt, counts) if return_routing else y

@@ -1,0 +1,122 @@
+// Dispatch: per-expert aggregation of the routing as an on-device counting sort.
+//
+// Perplexity's "Lower latency and higher throughput with multi-node DeepSeek
+// deployment" (section "MoE router") notes that dense dispatch consumes the
+// routing aggregated per expert rather than per token.  Three small kernels:
+//   1. count:   LDS-atomic histogram of each segment of 256 pairs;
+//   2. scan:    per expert, running sum over segments (segment bases and the
+//               totals), then an exclusive scan over experts (offsets);
+//   3. scatter: one wave per segment walks its pairs in order, 64 at a time;
+//               a pair's rank among equal experts of lower lane comes from a
+//               64-step register scan of the wave's expert ids, so the
+//               placement is stable (ascending pair id inside each expert).
+// Integer atomics only feed the histogram, so the result is deterministic.
+// Expert ids outside [0, E) are skipped (never used as an address).
+
+#include "moe_common.h"
+#include "moe_launch.h"
+
+namespace {
+
+constexpr int kSeg = moe::kDispatchSeg;
+
+__global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __restrict__ idx, int P, int E,
+                                                             int32_t* __restrict__ seg_counts) {
+  __shared__ int hist[256];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int p = blockIdx.x * kSeg + threadIdx.x;
+  if (p < P) {
+    const int e = idx[p];
+    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) seg_counts[(size_t)blockIdx.x * E + e] = hist[e];
+}
+
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(const int32_t* __restrict__ seg_counts, int nseg, int E,
+                                                            int32_t* __restrict__ seg_base,
+                                                            int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets) {
+  __shared__ int tot[256];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    for (int s = 0; s < nseg; ++s) {
+      seg_base[(size_t)s * E + e] = run;
+      run += seg_counts[(size_t)s * E + e];
+    }
+    counts[e] = run;
+  }
+  tot[e] = e < E ? run : 0;
+  __syncthreads();
+  // inclusive Hillis-Steele scan over 256 entries
+  for (int d = 1; d < 256; d <<= 1) {
+    const int v = e >= d ? tot[e - d] : 0;
+    __syncthreads();
+    tot[e] += v;
+    __syncthreads();
+  }
+  if (e < E) offsets[e] = tot[e] - run;
+  if (e == E - 1) offsets[E] = tot[e];
+}
+
+__global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* __restrict__ idx, int P, int E,
+                                                              const int32_t* __restrict__ offsets,
+                                                              const int32_t* __restrict__ seg_base,
+                                                              int32_t* __restrict__ sorted_pair,
+                                                              int32_t* __restrict__ pair_slot) {
+  __shared__ int run[256];
+  const int lane = threadIdx.x;
+  const int s = blockIdx.x;
+  for (int e = lane; e < E; e += 64) run[e] = offsets[e] + seg_base[(size_t)s * E + e];
+  __syncthreads();
+  for (int c = 0; c < kSeg; c += 64) {
+    const int p = s * kSeg + c + lane;
+    int e = p < P ? idx[p] : -1;
+    if (e < 0 || e >= E) e = -1;
+    int rank = 0, same = 0;
+    for (int j = 0; j < 64; ++j) {
+      const int ej = __builtin_amdgcn_readlane(e, j);
+      const int eq = (ej == e) ? 1 : 0;
+      same += eq;
+      rank += (j < lane) ? eq : 0;
+    }
+    if (e >= 0) {
+      const int slot = run[e] + rank;
+      sorted_pair[slot] = p;
+      pair_slot[p] = slot;
+    }
+    __syncthreads();
+    if (e >= 0 && rank == same - 1) run[e] += same;
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+namespace moe {
+
+static int dispatch_nseg(const moe_cfg& c) { return ceil_div((long long)c.T * c.k, kSeg); }
+
+size_t dispatch_ws_bytes(const moe_cfg& c) { return 2 * (size_t)dispatch_nseg(c) * c.E * sizeof(int32_t); }
+
+hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                           int32_t* sorted_pair, int32_t* pair_slot, int32_t* seg_ws, hipStream_t st) {
+  const int P = c.T * c.k;
+  const int nseg = dispatch_nseg(c);
+  int32_t* seg_counts = seg_ws;
+  int32_t* seg_base = seg_ws + (size_t)nseg * c.E;
+  hipLaunchKernelGGL(dispatch_count_kernel, dim3(nseg), dim3(kSeg), 0, st, idx, P, c.E, seg_counts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(256), 0, st, seg_counts, nseg, c.E, seg_base, counts,
+                     offsets);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(nseg), dim3(64), 0, st, idx, P, c.E, offsets, seg_base,
+                     sorted_pair, pair_slot);
+  return hipGetLastError();
+}
+
+}  // namespace moe

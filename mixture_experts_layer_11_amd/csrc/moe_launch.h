@@ -1,0 +1,47 @@
+// Host-side launch functions of the individual stages (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ---- router
+int route_splits(const moe_cfg& c);
+size_t route_ws_bytes(const moe_cfg& c);
+hipError_t launch_route(const moe_cfg& c, const void* x, const void* wg, const float* bias, int32_t* idx,
+                        float* w, float* part, hipStream_t st);
+
+// ---- dispatch
+constexpr int kDispatchSeg = 256;  // pairs per scatter segment (one wave each)
+size_t dispatch_ws_bytes(const moe_cfg& c);
+hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                           int32_t* sorted_pair, int32_t* pair_slot, int32_t* seg_ws, hipStream_t st);
+
+// ---- fp8 block quantisation
+hipError_t launch_quant_fp8(int rows, int cols, int block, const void* in, int in_dtype, uint8_t* codes,
+                            float* scales, hipStream_t st);
+
+// ---- expert FFN
+struct FfnWs {
+  int32_t* plan;  // work lists built on the device from the offsets
+  void* h;        // SwiGLU output [P + T, I]: bf16 for bf16 weights, fp32 otherwise
+  uint8_t* hq;    // fp8: codes of h [P + T, I]
+  float* hs;      // fp8: scales of h [P + T, I / qb]
+  uint8_t* xq;    // fp8: codes of x [T, H]
+  float* xs;      // fp8: scales of x [T, H / qb]
+};
+size_t ffn_plan_ints(const moe_cfg& c);
+size_t ffn_h_elem_bytes(const moe_cfg& c);
+hipError_t launch_expert_ffn(const moe_cfg& c, const void* x, const int32_t* offsets,
+                             const int32_t* sorted_pair, const moe_weights& w, float* y_sorted,
+                             float* y_shared, const FfnWs& ws, hipStream_t st);
+
+// ---- combine
+hipError_t launch_combine(const moe_cfg& c, const float* y_sorted, const float* y_shared,
+                          const int32_t* pair_slot, const float* topk_w, void* y, hipStream_t st);
+
+}  // namespace moe

@@ -8,4 +8,4 @@ here; nothing else is shared between them.
 """
 
 from .configs import CONFIGS, MoEConfig, get_config  # noqa: F401
-from .generate import MoEInputs, make_inputs  # noqa: F401
+from .generate import MoEInputs, make_inputs, make_router_inputs  # noqa: F401

@@ -116,15 +116,11 @@ def _expert_weights(cfg: MoEConfig, device, tensor: str, e: int, rows: int, cols
         w_out.copy_(w.to(_TORCH_DT[cfg.w_dtype]))
 
 
-def make_inputs(cfg: MoEConfig, device="cpu") -> MoEInputs:
-    """Draw every input of one layer call for ``cfg`` directly on ``device``.
-
-    Draws on different devices use different torch generators and therefore
-    give different (equally distributed) values; a test always feeds both the
-    oracle and the library from one draw.
-    """
+def make_router_inputs(cfg: MoEConfig, device="cpu"):
+    """x [T,H], wg [E,H] (activation dtype) and bias [E] fp32: the router's
+    inputs, identical to the ones ``make_inputs`` draws for the same config."""
     device = torch.device(device)
-    T, H, E, I, Is = cfg.T, cfg.H, cfg.E, cfg.I, cfg.I_shared
+    T, H, E = cfg.T, cfg.H, cfg.E
     adt = _TORCH_DT[cfg.act_dtype]
     seed = cfg.seed
 
@@ -148,9 +144,19 @@ def make_inputs(cfg: MoEConfig, device="cpu") -> MoEInputs:
         wg[:, H - nc:] = cfg.cluster_boost * torch.nn.functional.one_hot(ce, nc).to(torch.float32)
     elif cfg.routing != "random":
         raise ValueError(f"unknown routing structure {cfg.routing!r}")
+    return x.to(adt).contiguous(), wg.to(adt).contiguous(), bias.contiguous()
 
-    x = x.to(adt).contiguous()
-    wg = wg.to(adt).contiguous()
+
+def make_inputs(cfg: MoEConfig, device="cpu") -> MoEInputs:
+    """Draw every input of one layer call for ``cfg`` directly on ``device``.
+
+    Draws on different devices use different torch generators and therefore
+    give different (equally distributed) values; a test always feeds both the
+    oracle and the library from one draw.
+    """
+    device = torch.device(device)
+    T, H, E, I, Is = cfg.T, cfg.H, cfg.E, cfg.I, cfg.I_shared
+    x, wg, bias = make_router_inputs(cfg, device)
 
     fp8 = cfg.w_dtype == "fp8"
     wdt = torch.uint8 if fp8 else _TORCH_DT[cfg.w_dtype]
@@ -172,5 +178,4 @@ def make_inputs(cfg: MoEConfig, device="cpu") -> MoEInputs:
         _expert_weights(cfg, device, "ws13", 0, 2 * Is, H, H, ws13, ws13_s)
         _expert_weights(cfg, device, "ws2", 0, H, Is, Is, ws2, ws2_s)
 
-    return MoEInputs(cfg, x, wg, bias.contiguous(), w13, w2, ws13, ws2,
-                     w13_s, w2_s, ws13_s, ws2_s)
+    return MoEInputs(cfg, x, wg, bias, w13, w2, ws13, ws2, w13_s, w2_s, ws13_s, ws2_s)

@@ -1,0 +1,265 @@
+"""GPU parity: the HIP library, called through its C ABI, against the fp64 oracle.
+
+Inputs are seeded and synthetic (moe_inputs).  Every expected value comes from
+oracle/ alone; when a stage is tested on its own, its upstream inputs come
+from the oracle (or from the seeded generators), never from the GPU.
+
+Sizes: small layers the oracle finishes in seconds but that still span
+several tiles and ragged tails of both expert-FFN regimes, plus the five
+named workloads at full size, where the oracle checks every token's routing
+and a sample of tokens' outputs one by one.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import mixture_experts_layer_11_amd as moe
+from moe_inputs import CONFIGS, get_config, make_inputs, make_router_inputs
+from parity import (assert_outputs_close, compare_routing, output_errors, to_np, tol_key)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_and_library():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.load_library()          # fails loudly when the HIP library is missing
+
+
+def _log(*a):
+    print(*a, flush=True)
+
+
+# Small layers: several tiles, ragged tails, both FFN regimes.
+SMALL = {
+    "tiny_f32": get_config("tiny_f32"),
+    "small_bf16": get_config("decode16").with_(name="small_bf16", T=200, H=1024, E=32, k=4, I=256, I_shared=256),
+    "small_fp8": get_config("clustered2048_fp8").with_(name="small_fp8", T=150, H=512, E=16, k=4, I=256,
+                                                      I_shared=256),
+    "softmax_e10_f32": get_config("tiny_f32").with_(name="softmax_e10_f32", T=37, E=10, k=3, I=192, I_shared=0),
+    "k_eq_E_bf16": get_config("decode16").with_(name="k_eq_E_bf16", T=33, H=256, E=4, k=4, I=128, I_shared=128),
+    "one_expert_bf16": get_config("decode16").with_(name="one_expert_bf16", T=70, H=384, E=1, k=1, I=128,
+                                                   I_shared=128),
+    "one_token_bf16": get_config("decode16").with_(name="one_token_bf16", T=1, H=512, E=64, k=8, I=128,
+                                                  I_shared=128),
+}
+
+
+def _small_inputs(cfg):
+    inp = make_inputs(cfg, "cpu")
+    gpu = make_inputs(cfg, "cpu")
+    for f in ("x", "wg", "bias", "w13", "w2", "ws13", "ws2", "w13_scale", "w2_scale", "ws13_scale", "ws2_scale"):
+        t = getattr(gpu, f)
+        if t is not None:
+            setattr(gpu, f, t.to(DEV))
+    return inp, gpu
+
+
+# ------------------------------------------------------------------ quantiser
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_quantize_fp8_bit_exact(dtype):
+    g = torch.Generator().manual_seed(5)
+    a = torch.randn(37, 1024, generator=g) * torch.logspace(-6, 3, 1024)[None, :]
+    a[3, 256:384] = 0.0
+    a[4, :128] = 1e-30
+    a = a.to(dtype)
+    codes, scales = moe.moe_quantize_fp8(a.to(DEV), 128)
+    torch.cuda.synchronize()
+    oc, os_, _ = oracle.quantize_rows_fp8(oracle.to_f64(a), 128)
+    np.testing.assert_array_equal(to_np(codes), oc)
+    np.testing.assert_array_equal(to_np(scales).astype(np.float64), os_)
+
+
+# ------------------------------------------------------------------ router
+
+def _route_check(cfg, x, wg, bias):
+    mc = moe.cfg_from(cfg)
+    idx, w = moe.moe_route(mc, x.to(DEV), wg.to(DEV), bias.to(DEV))
+    torch.cuda.synchronize()
+    r = oracle.route(oracle.to_f64(x), oracle.to_f64(wg), oracle.to_f64(bias), cfg.k, cfg.score)
+    near, mism = compare_routing(idx, w, r, cfg.k)
+    _log(f"[route {cfg.name}] T={cfg.T} near-ties={near} differing near-tie tokens={len(mism)}")
+    return idx, w, r
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_route_small(name):
+    cfg = SMALL[name]
+    x, wg, bias = make_router_inputs(cfg, "cpu")
+    _route_check(cfg, x, wg, bias)
+
+
+@pytest.mark.parametrize("name", ["decode16", "decode256", "prefill8192_ep8", "clustered2048_fp8"])
+def test_route_full_size(name):
+    cfg = get_config(name)
+    x, wg, bias = make_router_inputs(cfg, DEV)
+    _route_check(cfg, x.cpu(), wg.cpu(), bias.cpu())
+
+
+# ------------------------------------------------------------------ dispatch
+
+def _distinct_topk(rng, T, E, k):
+    return np.argsort(rng.random((T, E)), axis=1)[:, :k]
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (33, 4, 4), (200, 32, 4), (1000, 256, 8), (8192, 32, 8),
+                                   (2048, 256, 8), (16, 256, 8)])
+def test_dispatch_exact(T, E, k):
+    rng = np.random.default_rng(T * 7 + E)
+    idx = _distinct_topk(rng, T, E, k)
+    cfg = moe.make_cfg(T, 128, E, k, 64, 64)
+    got = moe.moe_dispatch(cfg, torch.from_numpy(idx.astype(np.int32)).to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.dispatch(idx, E)
+    for name, g in zip(("counts", "offsets", "sorted_pair", "pair_slot"), got):
+        np.testing.assert_array_equal(to_np(g), ref[name], err_msg=name)
+
+
+def test_dispatch_all_pairs_to_one_expert():
+    T, E, k = 65536, 8, 1
+    idx = np.full((T, k), 5)
+    cfg = moe.make_cfg(T, 128, E, k, 64, 64)
+    got = moe.moe_dispatch(cfg, torch.from_numpy(idx.astype(np.int32)).to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.dispatch(idx, E)
+    for name, g in zip(("counts", "offsets", "sorted_pair", "pair_slot"), got):
+        np.testing.assert_array_equal(to_np(g), ref[name], err_msg=name)
+
+
+# ------------------------------------------------------------------ expert FFN and combine (stage by stage)
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_expert_ffn_small(name):
+    cfg = SMALL[name]
+    inp, gin = _small_inputs(cfg)
+    ref = oracle.forward(inp)
+    d = ref["dispatch"]
+    mc = moe.cfg_from(cfg)
+    off = torch.from_numpy(d["offsets"].astype(np.int32)).to(DEV)
+    sp = torch.from_numpy(d["sorted_pair"].astype(np.int32)).to(DEV)
+    ys, ysh = moe.moe_expert_ffn(mc, gin.x, off, sp, moe.Weights.from_inputs(gin))
+    torch.cuda.synchronize()
+    key = tol_key(cfg)
+    e1 = assert_outputs_close(ys, ref["y_sorted"], key, "y_sorted")
+    if cfg.I_shared:
+        e2 = assert_outputs_close(ysh, ref["y_shared"], key, "y_shared")
+    else:
+        e2 = None
+    _log(f"[expert_ffn {name}] y_sorted err {e1} y_shared err {e2}")
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_combine_small(name):
+    cfg = SMALL[name]
+    inp, _ = _small_inputs(cfg)
+    ref = oracle.forward(inp)
+    ys32 = ref["y_sorted"].astype(np.float32)
+    ysh32 = ref["y_shared"].astype(np.float32)
+    w32 = ref["route"]["w"].astype(np.float32)
+    expect = oracle.combine(ys32.astype(np.float64), ysh32.astype(np.float64) if cfg.I_shared else np.zeros_like(ref["y_shared"]),
+                            ref["dispatch"]["pair_slot"], w32.astype(np.float64), cfg.k)
+    mc = moe.cfg_from(cfg)
+    y = moe.moe_combine(mc, torch.from_numpy(ys32).to(DEV),
+                        torch.from_numpy(ysh32).to(DEV) if cfg.I_shared else None,
+                        torch.from_numpy(ref["dispatch"]["pair_slot"].astype(np.int32)).to(DEV),
+                        torch.from_numpy(w32).to(DEV))
+    torch.cuda.synchronize()
+    key = "f32" if cfg.act_dtype == "f32" else "bf16"
+    assert_outputs_close(y, expect, key, "combine")
+
+
+# ------------------------------------------------------------------ whole layer
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_forward_small(name):
+    cfg = SMALL[name]
+    inp, gin = _small_inputs(cfg)
+    ref = oracle.forward(inp)
+    mc = moe.cfg_from(cfg)
+    y, idx, w, counts = moe.moe_forward(mc, gin.x, gin.wg, gin.bias, moe.Weights.from_inputs(gin),
+                                        return_routing=True)
+    torch.cuda.synchronize()
+    near, mism = compare_routing(idx, w, ref["route"], cfg.k)
+    keep = np.setdiff1d(np.arange(cfg.T), mism)
+    if len(mism) == 0:
+        np.testing.assert_array_equal(to_np(counts), ref["dispatch"]["counts"])
+    err = assert_outputs_close(to_np(y)[keep], ref["y"][keep], tol_key(cfg), "y")
+    _log(f"[forward {name}] near-ties={near} excluded={len(mism)} err={err}")
+
+
+def test_forward_is_deterministic():
+    cfg = SMALL["small_bf16"]
+    _, gin = _small_inputs(cfg)
+    mc = moe.cfg_from(cfg)
+    ws = moe.alloc_workspace(mc)
+    outs = [moe.moe_forward(mc, gin.x, gin.wg, gin.bias, moe.Weights.from_inputs(gin), ws=ws, return_routing=True)
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert torch.equal(a, b)
+
+
+def test_zero_input_gives_zero_output():
+    cfg = SMALL["small_bf16"]
+    _, gin = _small_inputs(cfg)
+    gin.x.zero_()
+    y = moe.moe_forward(moe.cfg_from(cfg), gin.x, gin.wg, gin.bias, moe.Weights.from_inputs(gin))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y) == 0
+
+
+def test_all_tokens_to_one_expert():
+    """A +10 selection bias on one expert sends every token there (k = 1): one
+    group with all T rows takes the tiled regime with a ragged last tile."""
+    cfg = SMALL["small_bf16"].with_(name="hot_expert", T=300, k=1)
+    inp, gin = _small_inputs(cfg)
+    inp.bias[7] = 10.0
+    gin.bias[7] = 10.0
+    ref = oracle.forward(inp)
+    assert (ref["route"]["idx"] == 7).all()
+    y, idx, w, counts = moe.moe_forward(moe.cfg_from(cfg), gin.x, gin.wg, gin.bias, moe.Weights.from_inputs(gin),
+                                        return_routing=True)
+    torch.cuda.synchronize()
+    assert (to_np(idx) == 7).all()
+    np.testing.assert_array_equal(to_np(counts), ref["dispatch"]["counts"])
+    assert_outputs_close(y, ref["y"], "bf16", "y")
+
+
+# ------------------------------------------------------------------ full-size workloads (sampled outputs)
+
+FULL = ["decode16", "decode256", "prefill8192_ep8", "clustered2048_fp8"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_forward_full_size_sampled(name):
+    cfg = get_config(name)
+    _log(f"[full {name}] drawing inputs on the GPU")
+    gin = make_inputs(cfg, DEV)
+    mc = moe.cfg_from(cfg)
+    y, idx, w, counts = moe.moe_forward(mc, gin.x, gin.wg, gin.bias, moe.Weights.from_inputs(gin),
+                                        return_routing=True)
+    torch.cuda.synchronize()
+    _log(f"[full {name}] GPU forward done; oracle routing of all {cfg.T} tokens")
+    r = oracle.route(oracle.to_f64(gin.x), oracle.to_f64(gin.wg), oracle.to_f64(gin.bias), cfg.k, cfg.score)
+    near, mism = compare_routing(idx, w, r, cfg.k)
+    if len(mism) == 0:
+        np.testing.assert_array_equal(to_np(counts), np.bincount(r["idx"].ravel(), minlength=cfg.E))
+    rng = np.random.default_rng(0)
+    cand = np.setdiff1d(np.arange(cfg.T), mism)
+    toks = np.unique(np.concatenate([[cand[0], cand[-1]], rng.choice(cand, size=min(4, len(cand)), replace=False)]))
+    _log(f"[full {name}] oracle outputs of tokens {toks.tolist()}")
+    yo, _ = oracle.forward_tokens(gin, toks)
+    err = assert_outputs_close(to_np(y)[toks], yo, tol_key(cfg), "y")
+    touched = int((to_np(counts) > 0).sum())
+    _log(f"[full {name}] near-ties={near} excluded={len(mism)} touched experts={touched} err={err}")
+    del gin
+    torch.cuda.empty_cache()
