@@ -152,6 +152,23 @@ int moe_forward(const moe_cfg* cfg, const void* x, const void* w_gate, const flo
                 const moe_weights* w, void* y, int32_t* topk_idx_out, float* topk_w_out,
                 int32_t* counts_out, void* ws, size_t ws_bytes, void* hip_stream);
 
+/* ---- Per-kernel timing (measurement tools; not part of the layer).
+ * Between moe_profile_start() and moe_profile_stop(), every kernel the
+ * library launches is bracketed by two HIP events recorded on the stream it
+ * is launched on.  moe_profile_stop() waits for those events and returns, per
+ * kernel name, the launch count and the summed event-to-event time; entries
+ * beyond max_entries are dropped (*n_entries still counts them).  Events are
+ * pooled by the library and reused.  Do not enable while capturing a graph.
+ * Process-wide state, guarded by a mutex. */
+typedef struct {
+  char name[48];
+  int32_t launches;
+  double total_ms;
+} moe_kernel_time;
+
+int moe_profile_start(void);
+int moe_profile_stop(moe_kernel_time* out, int32_t max_entries, int32_t* n_entries);
+
 #ifdef __cplusplus
 }
 #endif

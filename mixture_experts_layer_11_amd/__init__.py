@@ -23,6 +23,8 @@ from .binding import (  # noqa: F401
     moe_dispatch,
     moe_expert_ffn,
     moe_forward,
+    moe_profile_start,
+    moe_profile_stop,
     moe_quantize_fp8,
     moe_route,
     status_str,

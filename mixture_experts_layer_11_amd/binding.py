@@ -21,7 +21,8 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = range(2)
 
 EXPORTS = ("moe_status_str", "moe_last_error", "moe_workspace_size", "moe_route", "moe_dispatch",
-           "moe_quantize_fp8", "moe_expert_ffn", "moe_combine", "moe_forward")
+           "moe_quantize_fp8", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_profile_start",
+           "moe_profile_stop")
 
 
 class MoELibraryMissing(RuntimeError):
@@ -39,6 +40,10 @@ class MoeCfg(ctypes.Structure):
                 ("I", ctypes.c_int32), ("I_shared", ctypes.c_int32), ("score", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32), ("quant_block", ctypes.c_int32),
                 ("routed_scale", ctypes.c_float), ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32)]
+
+
+class MoeKernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -72,6 +77,8 @@ def load_library(path: str = LIB_PATH):
     lib.moe_expert_ffn.argtypes = [cfgp, P, P, P, wp, P, P, P, SZ, P]
     lib.moe_combine.argtypes = [cfgp, P, P, P, P, P, P]
     lib.moe_forward.argtypes = [cfgp, P, P, P, wp, P, P, P, P, P, SZ, P]
+    lib.moe_profile_start.argtypes = []
+    lib.moe_profile_stop.argtypes = [P, I32, ctypes.POINTER(I32)]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -238,3 +245,16 @@ def moe_forward(cfg: MoeCfg, x, w_gate, sel_bias, weights: Weights, ws=None, y=N
     _check(lib.moe_forward(ctypes.byref(cfg), _ptr(x), _ptr(w_gate), _ptr(sel_bias), ctypes.byref(w), _ptr(y),
                            _ptr(idx), _ptr(wt), _ptr(counts), _ptr(ws), ws.numel(), _stream(stream)))
     return (y, idx, wt, counts) if return_routing else y
+
+
+def moe_profile_start():
+    _check(load_library().moe_profile_start())
+
+
+def moe_profile_stop() -> dict:
+    """{kernel name: (launches, total ms)} of the kernels launched since moe_profile_start()."""
+    lib = load_library()
+    n = ctypes.c_int32(0)
+    buf = (MoeKernelTime * 64)()
+    _check(lib.moe_profile_stop(ctypes.cast(buf, ctypes.c_void_p), 64, ctypes.byref(n)))
+    return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(min(n.value, 64))}

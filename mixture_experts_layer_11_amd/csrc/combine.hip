@@ -52,10 +52,10 @@ namespace moe {
 hipError_t launch_combine(const moe_cfg& c, const float* y_sorted, const float* y_shared,
                           const int32_t* pair_slot, const float* topk_w, void* y, hipStream_t st) {
   if (c.act_dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_kernel<MOE_BF16>, dim3(c.T), dim3(256), 0, st, y_sorted, y_shared, pair_slot, topk_w,
+    MOE_LAUNCH("combine", combine_kernel<MOE_BF16>, dim3(c.T), dim3(256), 0, st, y_sorted, y_shared, pair_slot, topk_w,
                        c.H, c.k, y);
   else
-    hipLaunchKernelGGL(combine_kernel<MOE_F32>, dim3(c.T), dim3(256), 0, st, y_sorted, y_shared, pair_slot, topk_w,
+    MOE_LAUNCH("combine", combine_kernel<MOE_F32>, dim3(c.T), dim3(256), 0, st, y_sorted, y_shared, pair_slot, topk_w,
                        c.H, c.k, y);
   return hipGetLastError();
 }

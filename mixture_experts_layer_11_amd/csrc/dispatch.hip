@@ -107,14 +107,14 @@ hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, int32_t* counts
   const int nseg = dispatch_nseg(c);
   int32_t* seg_counts = seg_ws;
   int32_t* seg_base = seg_ws + (size_t)nseg * c.E;
-  hipLaunchKernelGGL(dispatch_count_kernel, dim3(nseg), dim3(kSeg), 0, st, idx, P, c.E, seg_counts);
+  MOE_LAUNCH("dispatch_count", dispatch_count_kernel, dim3(nseg), dim3(kSeg), 0, st, idx, P, c.E, seg_counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(256), 0, st, seg_counts, nseg, c.E, seg_base, counts,
+  MOE_LAUNCH("dispatch_scan", dispatch_scan_kernel, dim3(1), dim3(256), 0, st, seg_counts, nseg, c.E, seg_base, counts,
                      offsets);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(nseg), dim3(64), 0, st, idx, P, c.E, offsets, seg_base,
+  MOE_LAUNCH("dispatch_scatter", dispatch_scatter_kernel, dim3(nseg), dim3(64), 0, st, idx, P, c.E, offsets, seg_base,
                      sorted_pair, pair_slot);
   return hipGetLastError();
 }

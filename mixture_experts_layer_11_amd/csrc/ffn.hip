@@ -481,7 +481,7 @@ __global__ __launch_bounds__(256) void ffn_fat_kernel(Args a, int ntn) {
 template <int DT>
 hipError_t run_ffn(const moe_cfg& c, Args a, hipStream_t st) {
   const int G = a.G;
-  hipLaunchKernelGGL(ffn_plan_kernel, dim3(1), dim3(512), 0, st, a);
+  MOE_LAUNCH("ffn_plan", ffn_plan_kernel, dim3(1), dim3(512), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int P = a.P;
@@ -499,13 +499,13 @@ hipError_t run_ffn(const moe_cfg& c, Args a, hipStream_t st) {
     const int ntn = mode == 1 ? c.I / (kBN / 2) : c.H / kBN;
     const int fat_grid = max_fat * ntn;
     if (mode == 1) {
-      hipLaunchKernelGGL((ffn_skinny_kernel<DT, 1>), dim3(sk_grid), dim3(256), 0, st, a);
+      MOE_LAUNCH("ffn_gemm1_skinny", (ffn_skinny_kernel<DT, 1>), dim3(sk_grid), dim3(256), 0, st, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      if (fat_grid > 0) hipLaunchKernelGGL((ffn_fat_kernel<DT, 1>), dim3(fat_grid), dim3(256), 0, st, a, ntn);
+      if (fat_grid > 0) MOE_LAUNCH("ffn_gemm1_tiled", (ffn_fat_kernel<DT, 1>), dim3(fat_grid), dim3(256), 0, st, a, ntn);
     } else {
-      hipLaunchKernelGGL((ffn_skinny_kernel<DT, 2>), dim3(sk_grid), dim3(256), 0, st, a);
+      MOE_LAUNCH("ffn_gemm2_skinny", (ffn_skinny_kernel<DT, 2>), dim3(sk_grid), dim3(256), 0, st, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      if (fat_grid > 0) hipLaunchKernelGGL((ffn_fat_kernel<DT, 2>), dim3(fat_grid), dim3(256), 0, st, a, ntn);
+      if (fat_grid > 0) MOE_LAUNCH("ffn_gemm2_tiled", (ffn_fat_kernel<DT, 2>), dim3(fat_grid), dim3(256), 0, st, a, ntn);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

@@ -9,6 +9,26 @@
 
 namespace moe {
 
+// Brackets one kernel launch with HIP events while moe_profile_start() is on.
+class ProfScope {
+ public:
+  ProfScope(const char* name, hipStream_t stream);
+  ~ProfScope();
+  ProfScope(const ProfScope&) = delete;
+  ProfScope& operator=(const ProfScope&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t stream_;
+  hipEvent_t start_ = nullptr;
+};
+
+#define MOE_LAUNCH(NAME, KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)            \
+  do {                                                                      \
+    ::moe::ProfScope moe_prof_scope_((NAME), (STREAM));                     \
+    hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);    \
+  } while (0)
+
 // ---- router
 int route_splits(const moe_cfg& c);
 size_t route_ws_bytes(const moe_cfg& c);

@@ -60,9 +60,9 @@ hipError_t launch_quant_fp8(int rows, int cols, int block, const void* in, int i
   const int grid = (int)((nb + 3) / 4);
   if (grid == 0) return hipSuccess;
   if (in_dtype == MOE_BF16)
-    hipLaunchKernelGGL(quant_fp8_kernel<MOE_BF16>, dim3(grid), dim3(256), 0, st, in, rows, cols, block, codes, scales);
+    MOE_LAUNCH("quant_fp8", quant_fp8_kernel<MOE_BF16>, dim3(grid), dim3(256), 0, st, in, rows, cols, block, codes, scales);
   else
-    hipLaunchKernelGGL(quant_fp8_kernel<MOE_F32>, dim3(grid), dim3(256), 0, st, in, rows, cols, block, codes, scales);
+    MOE_LAUNCH("quant_fp8", quant_fp8_kernel<MOE_F32>, dim3(grid), dim3(256), 0, st, in, rows, cols, block, codes, scales);
   return hipGetLastError();
 }
 

@@ -222,18 +222,18 @@ hipError_t launch_route(const moe_cfg& c, const void* x, const void* wg, const f
   const uint8_t* wb = static_cast<const uint8_t*>(wg);
   if (s == 1) {
     if (c.act_dtype == MOE_F32)
-      hipLaunchKernelGGL((gate_kernel<MOE_F32, true>), grid, block, 0, st, xb, wb, c.T, c.H, 1, nullptr, o);
+      MOE_LAUNCH("route_gate_fused", (gate_kernel<MOE_F32, true>), grid, block, 0, st, xb, wb, c.T, c.H, 1, nullptr, o);
     else
-      hipLaunchKernelGGL((gate_kernel<MOE_BF16, true>), grid, block, 0, st, xb, wb, c.T, c.H, 1, nullptr, o);
+      MOE_LAUNCH("route_gate_fused", (gate_kernel<MOE_BF16, true>), grid, block, 0, st, xb, wb, c.T, c.H, 1, nullptr, o);
     return hipGetLastError();
   }
   if (c.act_dtype == MOE_F32)
-    hipLaunchKernelGGL((gate_kernel<MOE_F32, false>), grid, block, 0, st, xb, wb, c.T, c.H, s, part, o);
+    MOE_LAUNCH("route_gate_split", (gate_kernel<MOE_F32, false>), grid, block, 0, st, xb, wb, c.T, c.H, s, part, o);
   else
-    hipLaunchKernelGGL((gate_kernel<MOE_BF16, false>), grid, block, 0, st, xb, wb, c.T, c.H, s, part, o);
+    MOE_LAUNCH("route_gate_split", (gate_kernel<MOE_BF16, false>), grid, block, 0, st, xb, wb, c.T, c.H, s, part, o);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(route_reduce_kernel, dim3(ceil_div(c.T, 4)), block, 0, st, part, c.T, s, o);
+  MOE_LAUNCH("route_reduce_select", route_reduce_kernel, dim3(ceil_div(c.T, 4)), block, 0, st, part, c.T, s, o);
   return hipGetLastError();
 }
 
