@@ -1,0 +1,279 @@
+"""Benchmark of the MoE-layer forward on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode16]
+
+One step = one moe_forward call (router, dispatch, expert FFNs with the
+shared expert, combine) over one batch of seeded synthetic input already
+resident in HBM.  Prints ONE JSON line:
+
+* value      whole-layer tokens/s = T * K / (wall time of the K timed steps)
+* roofline   for the kernel with the largest share of GPU time: algorithmic
+             bytes (or FLOPs) per launch, from the step's real per-expert
+             counts, divided by the kernel's mean launch time measured with
+             HIP events on its own stream during the timed steps; the peak is
+             MI355X's published HBM3E bandwidth (8 TB/s) or dense MFMA rate.
+             `traffic` is the measured HBM bytes per launch from rocprofv3
+             counters (profiles/traffic_<kernel>_<workload>.json) when those
+             were taken on the current kernel source, else null.
+* cpu_baseline  the fp64 oracle timed on the host on a bounded sample of the
+             same workload (first n tokens, single thread), as tokens/s.
+
+Only one GPU is used; --gpus above 1 exits with a message.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at 1 GPU + achieved HBM GB/s (decode) / MFMA % (prefill)"
+HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+SKINNY_ROWS = 32          # groups with at most this many rows take the streaming (skinny) kernels
+KERNEL_SOURCES = {        # the source file each kernel is built from (for the counter freshness check)
+    **{f"ffn_gemm{g}_skinny_m{m}": "ffn.hip" for g in (1, 2) for m in (8, 16, 32)}, "ffn_gemm1_tiled": "ffn.hip",
+    "ffn_gemm1_shared_skinny": "ffn.hip", "ffn_gemm2_shared_skinny": "ffn.hip",
+    "ffn_gemm2_tiled": "ffn.hip", "ffn_plan": "ffn.hip", "route_gate_fused": "route.hip",
+    "route_gate_split": "route.hip", "route_reduce_select": "route.hip", "dispatch_count": "dispatch.hip",
+    "dispatch_scan": "dispatch.hip", "dispatch_scatter": "dispatch.hip", "quant_fp8": "quant.hip",
+    "combine": "combine.hip",
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_layer_11_amd", "csrc")
+    for f in (KERNEL_SOURCES.get(kernel, ""), "moe_common.h"):
+        p = os.path.join(csrc, f)
+        if os.path.isfile(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def kernel_models(cfg, counts):
+    """Algorithmic bytes and FLOPs of each kernel per launch, from the counts.
+
+    Bytes count what the operation must move at least once: the weights of
+    the groups it serves (with fp8 scales), the activation rows it reads and
+    the outputs it writes.  h is bf16 for bf16 weights and fp32 otherwise (the
+    fp8 layer reads h as e4m3 codes plus scales in the down projection).
+    """
+    T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
+    fp8 = cfg.w_dtype == "fp8"
+    wb = 1 if fp8 else (4 if cfg.w_dtype == "f32" else 2)
+    ab = 4 if cfg.act_dtype == "f32" else 2
+    hb_out = 2 if cfg.w_dtype == "bf16" else 4
+    a1b = 1 if fp8 else ab
+    a2b = 1 if fp8 else hb_out
+    qb = cfg.quant_block
+    sc13 = (2 * I * H // qb) * 4 if fp8 else 0
+    sc2 = (H * I // qb) * 4 if fp8 else 0
+    groups = [int(c) for c in counts]
+    m = {f"ffn_gemm{g}_{r}": {"bytes": 0, "flops": 0} for g in (1, 2)
+         for r in ("skinny_m8", "skinny_m16", "skinny_m32", "tiled", "shared_skinny")}
+    items = [(mg, ("skinny_m8" if mg <= 8 else "skinny_m16" if mg <= 16 else "skinny_m32")
+              if mg <= SKINNY_ROWS else "tiled") for mg in groups]
+    if cfg.I_shared:
+        items.append((T, "shared_skinny" if T <= SKINNY_ROWS else "tiled"))
+    for mg, reg in items:
+        if mg == 0:
+            continue
+        g1, g2 = m[f"ffn_gemm1_{reg}"], m[f"ffn_gemm2_{reg}"]
+        g1["bytes"] += 2 * I * H * wb + sc13 + mg * H * a1b + mg * I * hb_out + (mg * H // qb * 4 if fp8 else 0)
+        g1["flops"] += 2 * mg * 2 * I * H
+        g2["bytes"] += H * I * wb + sc2 + mg * I * a2b + mg * H * 4 + (mg * I // qb * 4 if fp8 else 0)
+        g2["flops"] += 2 * mg * H * I
+    touched = sum(1 for c in counts if int(c) > 0)
+    layer_bytes = (touched + (1 if cfg.I_shared else 0)) * (3 * H * I * wb + sc13 + sc2) \
+        + E * H * ab + E * 4 + 2 * T * H * ab
+    layer_flops = (T * k + (T if cfg.I_shared else 0)) * 6 * H * I + 2 * T * H * E
+    return m, dict(bytes=layer_bytes, flops=layer_flops, touched=touched)
+
+
+def kernel_line(name, prof_entry, models):
+    """us per launch (with events around every kernel) and, for modelled kernels, GB/s or TFLOP/s."""
+    launches, tot_ms = prof_entry
+    us = tot_ms / max(launches, 1) * 1e3
+    d = {"us": round(us, 2)}
+    mm = models.get(name)
+    if mm and us > 0 and (mm["bytes"] or mm["flops"]):
+        d["GBps"] = round(mm["bytes"] / (us * 1e-6) / 1e9, 1)
+        d["TFLOPs"] = round(mm["flops"] / (us * 1e-6) / 1e12, 2)
+    return d
+
+
+def traffic_for(kernel, workload):
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.isfile(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != kernel_source_hash(kernel):
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(inp_gpu, n_tokens):
+    """Time the fp64 oracle, single-threaded, on the first n tokens."""
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from moe_inputs import MoEInputs
+
+    host = MoEInputs(inp_gpu.cfg, *[getattr(inp_gpu, f).cpu() if getattr(inp_gpu, f) is not None else None
+                                    for f in ("x", "wg", "bias", "w13", "w2", "ws13", "ws2", "w13_scale",
+                                              "w2_scale", "ws13_scale", "ws2_scale")])
+    toks = list(range(n_tokens))
+    nthreads = torch.get_num_threads()
+    torch.set_num_threads(1)
+    try:
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            oracle.forward_tokens(host, toks)
+            dt = time.perf_counter() - t0
+    finally:
+        torch.set_num_threads(nthreads)
+    return dt
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode16")
+    ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="no CPU baseline (tuning sweeps)")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr, flush=True)
+        return 2
+
+    import torch
+
+    import mixture_experts_layer_11_amd as moe
+    from moe_inputs import get_config, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    moe.load_library()
+    cfg = get_config(args.workload)
+    inp = make_inputs(cfg, "cuda")
+    mc = moe.cfg_from(cfg)
+    ws = moe.alloc_workspace(mc)
+    w = moe.Weights.from_inputs(inp)
+    y = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16 if cfg.act_dtype == "bf16" else torch.float32,
+                    device="cuda")
+    step = lambda: moe.moe_forward(mc, inp.x, inp.wg, inp.bias, w, ws=ws, y=y)   # noqa: E731
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # untimed pass: routing of this batch (for the byte model) and the per-kernel
+    # breakdown of one instrumented step (every kernel bracketed by events)
+    _, idx, _, counts = moe.moe_forward(mc, inp.x, inp.wg, inp.bias, w, ws=ws, return_routing=True)
+    torch.cuda.synchronize()
+    counts_h = counts.cpu().tolist()
+    moe.moe_profile_start()
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    breakdown = moe.moe_profile_stop()
+    dom = max(breakdown, key=lambda n: breakdown[n][1])
+
+    # timed region: K steps; the dominant kernel is bracketed by HIP events on its launch stream
+    moe.moe_profile_start(dom)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    prof = moe.moe_profile_stop()
+    gpu_ms = ev0.elapsed_time(ev1)
+
+    ms_per_step = wall_ms / args.steps
+    tokens_per_s = cfg.T * args.steps / (wall_ms / 1e3)
+
+    models, layer = kernel_models(cfg, counts_h)
+    launches, tot_ms = prof[dom]
+    avg_ms = tot_ms / max(launches, 1)
+    wdt = "fp8" if cfg.w_dtype == "fp8" else cfg.act_dtype
+    if dom in models:
+        mm = models[dom]
+        if "skinny" in dom:
+            achieved = mm["bytes"] / (avg_ms * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4)}
+        else:
+            achieved = mm["flops"] / (avg_ms * 1e-3) / 1e12
+            peak = MFMA_PEAK_TFLOPS[wdt]
+            roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4)}
+        roof["traffic"] = traffic_for(dom, cfg.name)
+    else:
+        roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": None,
+                "traffic": None}
+    roof["kernel"] = dom
+    roof["kernel_avg_us"] = round(avg_ms * 1e3, 2)
+    roof["algorithmic_per_launch"] = models.get(dom, {})
+
+    layer_gbps = layer["bytes"] / (ms_per_step * 1e-3) / 1e9
+    layer_tflops = layer["flops"] / (ms_per_step * 1e-3) / 1e12
+
+    cpu = None
+    if not (args.no_cpu_baseline or args.quick):
+        n = min(args.cpu_tokens, cfg.T)
+        dt = cpu_baseline(inp, n)
+        cpu = {"value": round(n / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {n} of {cfg.T} tokens of {cfg.name}: fp64 numpy oracle, token by token "
+                         f"(routing, fp64 upcast of each touched expert, SwiGLU, weighted sum), 1 thread, "
+                         f"inputs already in host memory; {dt:.2f} s"}
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wdt,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
+                   "I_shared": cfg.I_shared, "score": cfg.score, "weights": cfg.w_dtype,
+                   "touched_experts": layer["touched"], "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "layer": {"algorithmic_bytes": layer["bytes"], "flops": layer["flops"], "GBps": round(layer_gbps, 1),
+                  "hbm_frac": round(layer_gbps / HBM_PEAK_GBPS, 4), "TFLOPs": round(layer_tflops, 2),
+                  "gpu_event_ms_per_step": round(gpu_ms / args.steps, 4)},
+        "kernels": {n: kernel_line(n, v, models) for n, v in sorted(breakdown.items())},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -153,9 +153,9 @@ int moe_forward(const moe_cfg* cfg, const void* x, const void* w_gate, const flo
                 int32_t* counts_out, void* ws, size_t ws_bytes, void* hip_stream);
 
 /* ---- Per-kernel timing (measurement tools; not part of the layer).
- * Between moe_profile_start() and moe_profile_stop(), every kernel the
- * library launches is bracketed by two HIP events recorded on the stream it
- * is launched on.  moe_profile_stop() waits for those events and returns, per
+ * Between moe_profile_start(only) and moe_profile_stop(), every kernel the
+ * library launches (or, when `only` is not NULL, every kernel of that name)
+ * is bracketed by two HIP events recorded on the stream it is launched on.  moe_profile_stop() waits for those events and returns, per
  * kernel name, the launch count and the summed event-to-event time; entries
  * beyond max_entries are dropped (*n_entries still counts them).  Events are
  * pooled by the library and reused.  Do not enable while capturing a graph.
@@ -166,7 +166,7 @@ typedef struct {
   double total_ms;
 } moe_kernel_time;
 
-int moe_profile_start(void);
+int moe_profile_start(const char* only);
 int moe_profile_stop(moe_kernel_time* out, int32_t max_entries, int32_t* n_entries);
 
 #ifdef __cplusplus

@@ -77,7 +77,7 @@ def load_library(path: str = LIB_PATH):
     lib.moe_expert_ffn.argtypes = [cfgp, P, P, P, wp, P, P, P, SZ, P]
     lib.moe_combine.argtypes = [cfgp, P, P, P, P, P, P]
     lib.moe_forward.argtypes = [cfgp, P, P, P, wp, P, P, P, P, P, SZ, P]
-    lib.moe_profile_start.argtypes = []
+    lib.moe_profile_start.argtypes = [ctypes.c_char_p]
     lib.moe_profile_stop.argtypes = [P, I32, ctypes.POINTER(I32)]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = ctypes.c_int
@@ -247,8 +247,9 @@ def moe_forward(cfg: MoeCfg, x, w_gate, sel_bias, weights: Weights, ws=None, y=N
     return (y, idx, wt, counts) if return_routing else y
 
 
-def moe_profile_start():
-    _check(load_library().moe_profile_start())
+def moe_profile_start(only: Optional[str] = None):
+    """Time every library kernel (or only the kernel named `only`) with HIP events."""
+    _check(load_library().moe_profile_start(only.encode() if only else None))
 
 
 def moe_profile_stop() -> dict:

@@ -38,9 +38,9 @@
 namespace {
 
 constexpr int kSkinnyRows = 32;  // groups with <= this many rows take the skinny path
+constexpr int kPlanHead = 4;     // plan: [0..2] skinny list sizes (<=8, <=16, <=32 rows), [3] fat tiles
 constexpr int kBM = 128;         // fat tile rows
 constexpr int kBN = 128;         // fat tile columns (GEMM1: 64 gate + 64 up)
-constexpr int kSkNT = 4;         // skinny: 16-row weight tiles per wave
 
 struct Args {
   int T, H, E, k, I, P;
@@ -63,7 +63,7 @@ struct Args {
   const float* a2s;             // fp8: h scales [P+T, I/qb]
   float* y_sorted;
   float* y_shared;
-  const int32_t* plan;          // [0] n_skinny, [1] n_fat, [2..2+G) skinny groups, then fat (group,row0)
+  const int32_t* plan;          // see ffn_plan_kernel: list sizes, 3 skinny lists of G, fat (group,row0) pairs
   int G;
 };
 
@@ -108,32 +108,40 @@ __device__ __forceinline__ void store_h(uint8_t* h, size_t idx, float v) {
 // ------------------------------------------------------------------ plan
 
 __global__ __launch_bounds__(512) void ffn_plan_kernel(Args a) {
-  __shared__ int sk[512];
+  __shared__ int sk[3][512];
   __shared__ int ft[512];
   const int g = threadIdx.x;
   int m = 0;
   if (g < a.G) m = g < a.E ? a.offsets[g + 1] - a.offsets[g] : a.T;
-  const int is_sk = (m > 0 && m <= kSkinnyRows) ? 1 : 0;
+  // skinny class: 0 for 1..8 rows, 1 for 9..16, 2 for 17..32 (a skinny shared
+  // expert has a launch of its own and is in no list)
+  const bool shared = g == a.E;
+  const int cls = (m > 0 && m <= kSkinnyRows && !shared) ? (m <= 8 ? 0 : m <= 16 ? 1 : 2) : -1;
   const int tiles = m > kSkinnyRows ? (m + kBM - 1) / kBM : 0;
-  sk[g] = is_sk;
+#pragma unroll
+  for (int c = 0; c < 3; ++c) sk[c][g] = cls == c ? 1 : 0;
   ft[g] = tiles;
   __syncthreads();
   for (int d = 1; d < 512; d <<= 1) {
-    const int v1 = g >= d ? sk[g - d] : 0;
+    int v[3];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) v[c] = g >= d ? sk[c][g - d] : 0;
     const int v2 = g >= d ? ft[g - d] : 0;
     __syncthreads();
-    sk[g] += v1;
+#pragma unroll
+    for (int c = 0; c < 3; ++c) sk[c][g] += v[c];
     ft[g] += v2;
     __syncthreads();
   }
   int32_t* plan = const_cast<int32_t*>(a.plan);
   if (g == 511) {
-    plan[0] = sk[511];
-    plan[1] = ft[511];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) plan[c] = sk[c][511];
+    plan[3] = ft[511];
   }
-  if (is_sk) plan[2 + sk[g] - 1] = g;
+  if (cls >= 0) plan[kPlanHead + cls * a.G + sk[cls][g] - 1] = g;
   const int t0 = ft[g] - tiles;
-  int32_t* fat = plan + 2 + a.G;
+  int32_t* fat = plan + kPlanHead + 3 * a.G;
   for (int i = 0; i < tiles; ++i) {
     fat[2 * (t0 + i)] = g;
     fat[2 * (t0 + i) + 1] = i * kBM;
@@ -141,156 +149,264 @@ __global__ __launch_bounds__(512) void ffn_plan_kernel(Args a) {
 }
 
 // ------------------------------------------------------------------ skinny grouped GEMM
+//
+// Streaming layout.  A weight row is read in 128-byte windows (one cache
+// line).  One wave load instruction covers 8 weight rows x one window: lane l
+// reads row (l % 8), 16-byte chunk c(l) = 4 * ((l >> 3) & 1) + (l >> 4).  Fed
+// as the B operand of a 16x16 MFMA, column n (lane l % 16) thus holds weight
+// row n % 8, and columns n and n + 8 hold the two complementary 64-byte halves
+// of the window.  The A operand mirrors this: M row m holds token m % 8 with
+// the same chunk rule.  The diagonal 8x8 blocks of the 16x16 result are then
+// the two K halves of the same (token, row) dot products and the off-diagonal
+// blocks are discarded: out[t][r] = C[t][r] + C[t+8][r+8], which sits in lanes
+// L and L ^ 40.  Half of each MFMA is wasted, which costs nothing in this
+// bandwidth-bound regime, and every load instruction reads whole cache lines.
 
-// One wave = one work item: kSkNT weight tiles of 16 rows over the full K,
-// against up to 32 activation rows (two 16-row M tiles).
-template <int DT, int MODE>
-__global__ __launch_bounds__(256) void ffn_skinny_kernel(Args a) {
+#ifndef MOE_SK_NT
+#define MOE_SK_NT 8
+#endif
+#ifndef MOE_SK_U
+#define MOE_SK_U 1
+#endif
+constexpr int kSkNT = MOE_SK_NT;  // 8-row weight tiles per wave (even: gate/up halves in GEMM1)
+constexpr int kSkU = MOE_SK_U;    // 128-byte K windows per loop trip
+
+// Weights are read exactly once: nontemporal loads keep them from displacing
+// the reused activation rows in the caches.
+__device__ __forceinline__ i32x4 ldw16(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
+}
+
+__device__ __forceinline__ int sk_chunk(int lane) { return 4 * ((lane >> 3) & 1) + (lane >> 4); }
+
+// One pass over the full K for NTP of the wave's kSkNT weight tiles (pass p),
+// against MT M tiles of 8 tokens (MT * 8 >= group rows).  Rows beyond the
+// group's count are clamped to its last row: their results are never stored,
+// so the K loop carries no per-lane predicates or branches.  U windows per
+// loop trip give NTP * U = 8 independent weight loads per lane.
+//
+// Split K (KS > 1): the KS waves of a workgroup share the item, wave `ks`
+// takes windows [ks*nwin/KS, (ks+1)*nwin/KS); partial accumulators meet in
+// LDS and wave 0 adds them in slice order (fixed order: reproducible) before
+// the epilogue.
+template <int DT, int MODE, int MT, int NT, int NTP, int U, int KS>
+__device__ __forceinline__ void skinny_pass(const Args& a, const Group& gr, int g, int it, int p, int lane,
+                                            int ks, f32x4* red) {
   using F = Frag<DT>;
-  constexpr int NT = kSkNT;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = lane & 15, grp = lane >> 4;
-  const int cols_per_item = MODE == 1 ? 8 * NT : 16 * NT;   // h columns (mode 1) or y columns (mode 2)
-  const int N = MODE == 1 ? a.I : a.H;
-  const int items = N / cols_per_item;
-  const int item = blockIdx.x * 4 + wave;
-  const int gi = item / items;
-  if (gi >= a.plan[0]) return;
-  const int g = a.plan[2 + gi];
-  const int it = item - gi * items;
-  const Group gr = group_of(a, g);
+  constexpr bool FP8 = DT == MOE_FP8_E4M3;
+  const int r8 = lane & 7;
+  const int ch16 = sk_chunk(lane) * 16;
+  const int cols_per_item = MODE == 1 ? 4 * NT : 8 * NT;   // h columns (GEMM1) or y columns (GEMM2)
   const int K = MODE == 1 ? a.H : a.I;
   const size_t krow = (size_t)K * F::ESZ;
-  const int nmt = (gr.m + 15) >> 4;   // 1 or 2 (uniform)
+  const int nwin = (int)(krow / 128);
+  const int w_begin = KS > 1 ? (int)((long long)nwin * ks / KS) : 0;
+  const int w_end = KS > 1 ? (int)((long long)nwin * (ks + 1) / KS) : nwin;
 
-  // A rows (this lane loads row `row` of each M tile)
-  const uint8_t* pa[2];
-  bool av[2];
+  const uint8_t* abase = MODE == 1 ? a.a1 : a.a2;
+  int arow[MT];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int r = mt * 16 + row;
-    av[mt] = r < gr.m;
-    int src = 0;
-    if (av[mt]) src = MODE == 1 ? gemm1_src_row(a, gr, r) : gr.slot0 + r;
-    pa[mt] = (MODE == 1 ? a.a1 : a.a2) + (size_t)src * krow + grp * 16;
+  for (int mt = 0; mt < MT; ++mt) {
+    const int r = min(mt * 8 + r8, gr.m - 1);
+    arow[mt] = MODE == 1 ? gemm1_src_row(a, gr, r) : gr.slot0 + r;
   }
-  // B rows (weight rows of the kSkNT tiles)
   const uint8_t* wbase;
   const float* wsbase = nullptr;
   if (MODE == 1) {
     wbase = gr.routed ? a.w13 + (size_t)g * 2 * a.I * krow : a.ws13;
-    if (DT == MOE_FP8_E4M3) wsbase = gr.routed ? a.w13s + (size_t)g * 2 * a.I * (K / a.qb) : a.ws13s;
+    if (FP8) wsbase = gr.routed ? a.w13s + (size_t)g * 2 * a.I * nwin : a.ws13s;
   } else {
     wbase = gr.routed ? a.w2 + (size_t)g * a.H * krow : a.ws2;
-    if (DT == MOE_FP8_E4M3) wsbase = gr.routed ? a.w2s + (size_t)g * a.H * (K / a.qb) : a.ws2s;
+    if (FP8) wsbase = gr.routed ? a.w2s + (size_t)g * a.H * nwin : a.ws2s;
   }
-  int wrow[NT];
+  // tile j of this pass -> tile index in the item (GEMM1: first half gate, second half up)
+  int wrow[NTP];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
+  for (int j = 0; j < NTP; ++j) {
     if (MODE == 1) {
-      const int c0 = it * cols_per_item;
-      wrow[j] = (j < NT / 2 ? 0 : a.I) + c0 + 16 * (j % (NT / 2)) + row;
+      const int jg = j < NTP / 2 ? p * (NTP / 2) + j : p * (NTP / 2) + j - NTP / 2;   // gate-tile index
+      wrow[j] = (j < NTP / 2 ? 0 : a.I) + it * cols_per_item + 8 * jg + r8;
     } else {
-      wrow[j] = it * cols_per_item + 16 * j + row;
+      wrow[j] = it * cols_per_item + 8 * (p * NTP + j) + r8;
     }
   }
-  const uint8_t* pb[NT];
+  const uint8_t* pb[NTP];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) pb[j] = wbase + (size_t)wrow[j] * krow + grp * 16;
+  for (int j = 0; j < NTP; ++j) pb[j] = wbase + (size_t)wrow[j] * krow + ch16;
+  const uint8_t* pa[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) pa[mt] = abase + (size_t)arow[mt] * krow + ch16;
 
-  f32x4 acc[2][NT];
+  f32x4 acc[MT][NTP];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int j = 0; j < NT; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NTP; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if constexpr (DT != MOE_FP8_E4M3) {
-    const int nfrag = K / F::KF;
-#pragma unroll 4
-    for (int f = 0; f < nfrag; ++f) {
-      const size_t off = (size_t)f * 64;
-      i32x4 b[NT];
+  if constexpr (!FP8) {
+    int w = w_begin;
+    for (; w + U <= w_end; w += U) {
+      i32x4 b[U][NTP], av[U][MT];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) b[j] = ld16(pb[j] + off);
-      const i32x4 a0 = av[0] ? ld16(pa[0] + off) : zero16();
+      for (int u = 0; u < U; ++u) {
+        const size_t off = (size_t)(w + u) * 128;
 #pragma unroll
-      for (int j = 0; j < NT; ++j) F::mma(acc[0][j], a0, b[j]);
-      if (nmt > 1) {
-        const i32x4 a1 = av[1] ? ld16(pa[1] + off) : zero16();
+        for (int j = 0; j < NTP; ++j) b[u][j] = ldw16(pb[j] + off);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) F::mma(acc[1][j], a1, b[j]);
+        for (int mt = 0; mt < MT; ++mt) av[u][mt] = ld16(pa[mt] + off);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int j = 0; j < NTP; ++j) F::mma(acc[mt][j], av[u][mt], b[u][j]);
+    }
+    for (; w < w_end; ++w) {
+      const size_t off = (size_t)w * 128;
+      i32x4 b[NTP];
+#pragma unroll
+      for (int j = 0; j < NTP; ++j) b[j] = ldw16(pb[j] + off);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const i32x4 av = ld16(pa[mt] + off);
+#pragma unroll
+        for (int j = 0; j < NTP; ++j) F::mma(acc[mt][j], av, b[j]);
       }
     }
   } else {
-    // Scales of the C rows this lane holds (rows 4*grp+i of each M tile) and of its B rows.
-    const int nkb = K / a.qb;
-    const float* sa_row[2][4];
+    // One 128-byte window is one fp8 scale block.  Scales of the C rows this
+    // lane holds (token (4*(lane>>4)+i) % 8 of each M tile) and of its column's row.
+    const float* sbase = MODE == 1 ? a.a1s : a.a2s;
+    int sa_row[MT][4];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = mt * 16 + 4 * grp + i;
-        int src = 0;
-        if (r < gr.m) src = MODE == 1 ? gemm1_src_row(a, gr, r) : gr.slot0 + r;
-        sa_row[mt][i] = (MODE == 1 ? a.a1s : a.a2s) + (size_t)src * nkb;
+        const int r = min(mt * 8 + ((4 * (lane >> 4) + i) & 7), gr.m - 1);
+        sa_row[mt][i] = (MODE == 1 ? gemm1_src_row(a, gr, r) : gr.slot0 + r) * nwin;
       }
-    const float* sw_row[NT];
+    for (int w = w_begin; w < w_end; ++w) {
+      const size_t off = (size_t)w * 128;
+      i32x4 b[NTP], av[MT];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) sw_row[j] = wsbase + (size_t)wrow[j] * nkb;
-#pragma unroll 2
-    for (int kb = 0; kb < nkb; ++kb) {
-      const size_t off = (size_t)kb * 128;
-      i32x4 b0[NT], b1[NT];
+      for (int j = 0; j < NTP; ++j) b[j] = ldw16(pb[j] + off);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        b0[j] = ld16(pb[j] + off);
-        b1[j] = ld16(pb[j] + off + 64);
-      }
-      float sw[NT];
+      for (int mt = 0; mt < MT; ++mt) av[mt] = ld16(pa[mt] + off);
+      float sw[NTP], sa[MT][4];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) sw[j] = sw_row[j][kb];
+      for (int j = 0; j < NTP; ++j) sw[j] = wsbase[(size_t)wrow[j] * nwin + w];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        if (mt < nmt) {
-          const i32x4 a0 = av[mt] ? ld16(pa[mt] + off) : zero16();
-          const i32x4 a1 = av[mt] ? ld16(pa[mt] + off + 64) : zero16();
-          float sa[4];
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sa[i] = sa_row[mt][i][kb];
+        for (int i = 0; i < 4; ++i) sa[mt][i] = sbase[(size_t)sa_row[mt][i] + w];
 #pragma unroll
-          for (int j = 0; j < NT; ++j) {
-            const f32x4 p = F::mma128(a0, a1, b0[j], b1[j]);
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mt][j][i] = fmaf(p[i], sa[i] * sw[j], acc[mt][j][i]);
-          }
+        for (int j = 0; j < NTP; ++j) {
+          f32x4 pr = {0.f, 0.f, 0.f, 0.f};
+          // a 16-byte chunk is 16 fp8 values: two 16x16x32 MFMAs (8 bytes per lane each)
+          pr = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(((const long*)&av[mt])[0], ((const long*)&b[j])[0], pr, 0, 0, 0);
+          pr = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(((const long*)&av[mt])[1], ((const long*)&b[j])[1], pr, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mt][j][i] = fmaf(pr[i], sa[mt][i] * sw[j], acc[mt][j][i]);
         }
-      }
     }
   }
 
-  // Epilogue: lane holds rows 4*grp+i of each M tile, column `row` of each N tile.
+  if constexpr (KS > 1) {
+    // red: [KS-1][MT*NTP][64] partial accumulators of waves 1..KS-1
+    if (ks > 0) {
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    if (mt >= nmt) break;
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < NTP; ++j) red[((ks - 1) * MT * NTP + mt * NTP + j) * 64 + lane] = acc[mt][j];
+    }
+    __syncthreads();
+    if (ks == 0) {
+      for (int q = 0; q < KS - 1; ++q)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int j = 0; j < NTP; ++j) acc[mt][j] += red[(q * MT * NTP + mt * NTP + j) * 64 + lane];
+    }
+    __syncthreads();
+    if (ks > 0) return;
+  }
+
+  // Fold the two K halves: lanes L = 16*h + r (h < 2, r < 8) end up holding
+  // tokens 4*h + i (i = 0..3) of each M tile for weight row r of each tile.
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < NTP; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[mt][j][i] += __shfl_xor(acc[mt][j][i], 40, 64);
+  if ((lane & 8) || lane >= 32) return;
+  const int hh = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = mt * 16 + 4 * grp + i;
+      const int r = mt * 8 + 4 * hh + i;
       if (r >= gr.m) continue;
       if (MODE == 1) {
         const size_t hrow = (size_t)(gr.slot0 + r) * a.I;
 #pragma unroll
-        for (int j = 0; j < NT / 2; ++j) {
-          const float gv = acc[mt][j][i], uv = acc[mt][j + NT / 2][i];
-          const int col = it * cols_per_item + 16 * j + row;
-          store_h<DT>(a.h, hrow + col, silu(gv) * uv);
+        for (int j = 0; j < NTP / 2; ++j) {
+          const float gv = acc[mt][j][i], uv = acc[mt][j + NTP / 2][i];
+          store_h<DT>(a.h, hrow + it * cols_per_item + 8 * (p * (NTP / 2) + j) + r8, silu(gv) * uv);
         }
       } else {
         float* yrow = gr.routed ? a.y_sorted + (size_t)(gr.slot0 + r) * a.H : a.y_shared + (size_t)r * a.H;
 #pragma unroll
-        for (int j = 0; j < NT; ++j) yrow[it * cols_per_item + 16 * j + row] = acc[mt][j][i];
+        for (int j = 0; j < NTP; ++j) yrow[it * cols_per_item + 8 * (p * NTP + j) + r8] = acc[mt][j][i];
       }
     }
   }
+}
+
+// All NT tiles of an item with MT M tiles: NT / NTP passes.
+template <int DT, int MODE, int MT, int NT, int KS>
+__device__ __forceinline__ void skinny_tile(const Args& a, const Group& gr, int g, int it, int lane, int ks,
+                                            f32x4* red) {
+  constexpr int NTP = MT == 1 ? NT : (NT / MT >= 2 ? NT / MT : 2);
+  constexpr int U0 = 8 / NTP > 0 ? 8 / NTP : 1;
+  constexpr int U = MT >= 4 && U0 > 2 ? 2 : U0;
+  for (int p = 0; p < NT / NTP; ++p) skinny_pass<DT, MODE, MT, NT, NTP, U, KS>(a, gr, g, it, p, lane, ks, red);
+}
+
+// Routed skinny groups of class CLS (MT = 1, 2, 4 M tiles of 8 tokens).
+// One wave = one work item (group, column block of kSkNT tiles); waves past
+// the class's list exit at once.
+template <int DT, int MODE, int CLS>
+__global__ __launch_bounds__(256) void ffn_skinny_kernel(Args a) {
+  constexpr int NT = kSkNT;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cols_per_item = MODE == 1 ? 4 * NT : 8 * NT;
+  const int items = (MODE == 1 ? a.I : a.H) / cols_per_item;
+  const int item = blockIdx.x * 4 + wave;
+  const int gi = item / items;
+  if (gi >= a.plan[CLS]) return;
+  const int g = a.plan[kPlanHead + CLS * a.G + gi];
+  const int it = item - gi * items;
+  const Group gr = group_of(a, g);
+  skinny_tile<DT, MODE, 1 << CLS, NT, 1>(a, gr, g, it, lane, 0, nullptr);
+}
+
+// The shared expert when T <= kSkinnyRows: its row count is known on the
+// host, so its launch is sized exactly, with narrow items (kShNT tiles) and
+// the K range split over the kShKS waves of each workgroup.
+constexpr int kShNT = 2;
+constexpr int kShKS = 8;
+
+template <int DT, int MODE, int MT>
+__global__ __launch_bounds__(64 * kShKS) void ffn_shared_skinny_kernel(Args a) {
+  constexpr int NTP = MT == 1 ? kShNT : (kShNT / MT >= 2 ? kShNT / MT : 2);
+  __shared__ f32x4 red[(kShKS - 1) * MT * NTP * 64];
+  const int lane = threadIdx.x & 63, ks = threadIdx.x >> 6;
+  const Group gr = group_of(a, a.E);
+  skinny_tile<DT, MODE, MT, kShNT, kShKS>(a, gr, a.E, blockIdx.x, lane, ks, red);
 }
 
 // ------------------------------------------------------------------ fat grouped GEMM
@@ -313,8 +429,8 @@ __global__ __launch_bounds__(256) void ffn_fat_kernel(Args a, int ntn) {
   const int wm = wave >> 1, wn = wave & 1;
   const int tile = blockIdx.x / ntn;
   const int nt = blockIdx.x - tile * ntn;
-  if (tile >= a.plan[1]) return;
-  const int32_t* fat = a.plan + 2 + a.G;
+  if (tile >= a.plan[3]) return;
+  const int32_t* fat = a.plan + kPlanHead + 3 * a.G;
   const int g = fat[2 * tile];
   const int row0 = fat[2 * tile + 1];
   const Group gr = group_of(a, g);
@@ -494,19 +610,47 @@ hipError_t run_ffn(const moe_cfg& c, Args a, hipStream_t st) {
       if (e != hipSuccess) return e;
     }
     const int N = mode == 1 ? c.I : c.H;
-    const int sk_items = N / (mode == 1 ? 8 * kSkNT : 16 * kSkNT);
-    const int sk_grid = moe::ceil_div((long long)G * sk_items, 4);
+    const int sk_items = N / (mode == 1 ? 4 * kSkNT : 8 * kSkNT);
+    // upper bounds of the three skinny lists: a group of class c has > 8 * 2^(c-1) rows
+    int sk_groups[3];
+    for (int cls = 0; cls < 3; ++cls) {
+      const int min_rows = cls == 0 ? 1 : (4 << cls) + 1;   // 1, 9, 17
+      const int bound = P / min_rows;
+      sk_groups[cls] = bound < G ? bound : G;
+    }
     const int ntn = mode == 1 ? c.I / (kBN / 2) : c.H / kBN;
     const int fat_grid = max_fat * ntn;
-    if (mode == 1) {
-      MOE_LAUNCH("ffn_gemm1_skinny", (ffn_skinny_kernel<DT, 1>), dim3(sk_grid), dim3(256), 0, st, a);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-      if (fat_grid > 0) MOE_LAUNCH("ffn_gemm1_tiled", (ffn_fat_kernel<DT, 1>), dim3(fat_grid), dim3(256), 0, st, a, ntn);
-    } else {
-      MOE_LAUNCH("ffn_gemm2_skinny", (ffn_skinny_kernel<DT, 2>), dim3(sk_grid), dim3(256), 0, st, a);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
-      if (fat_grid > 0) MOE_LAUNCH("ffn_gemm2_tiled", (ffn_fat_kernel<DT, 2>), dim3(fat_grid), dim3(256), 0, st, a, ntn);
+    static const char* const kSkName[2][3] = {
+        {"ffn_gemm1_skinny_m8", "ffn_gemm1_skinny_m16", "ffn_gemm1_skinny_m32"},
+        {"ffn_gemm2_skinny_m8", "ffn_gemm2_skinny_m16", "ffn_gemm2_skinny_m32"}};
+    const char* fatn = mode == 1 ? "ffn_gemm1_tiled" : "ffn_gemm2_tiled";
+#define MOE_SK_LAUNCH(M, CLS)                                                                   \
+    if (sk_groups[CLS] > 0) {                                                                   \
+      MOE_LAUNCH(kSkName[M - 1][CLS], (ffn_skinny_kernel<DT, M, CLS>), dim3(moe::ceil_div((long long)sk_groups[CLS] * sk_items, 4)), \
+                 dim3(256), 0, st, a);                                                          \
+      if ((e = hipGetLastError()) != hipSuccess) return e;                                     \
     }
+    if (a.has_shared && c.T <= kSkinnyRows) {
+      const int sh_items = N / (mode == 1 ? 4 * kShNT : 8 * kShNT);
+      const char* shn = mode == 1 ? "ffn_gemm1_shared_skinny" : "ffn_gemm2_shared_skinny";
+#define MOE_SH_LAUNCH(M, MT) \
+      MOE_LAUNCH(shn, (ffn_shared_skinny_kernel<DT, M, MT>), dim3(sh_items), dim3(64 * kShKS), 0, st, a)
+      if (mode == 1) {
+        if (c.T <= 8) MOE_SH_LAUNCH(1, 1); else if (c.T <= 16) MOE_SH_LAUNCH(1, 2); else MOE_SH_LAUNCH(1, 4);
+      } else {
+        if (c.T <= 8) MOE_SH_LAUNCH(2, 1); else if (c.T <= 16) MOE_SH_LAUNCH(2, 2); else MOE_SH_LAUNCH(2, 4);
+      }
+#undef MOE_SH_LAUNCH
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (mode == 1) {
+      MOE_SK_LAUNCH(1, 0) MOE_SK_LAUNCH(1, 1) MOE_SK_LAUNCH(1, 2)
+      if (fat_grid > 0) MOE_LAUNCH(fatn, (ffn_fat_kernel<DT, 1>), dim3(fat_grid), dim3(256), 0, st, a, ntn);
+    } else {
+      MOE_SK_LAUNCH(2, 0) MOE_SK_LAUNCH(2, 1) MOE_SK_LAUNCH(2, 2)
+      if (fat_grid > 0) MOE_LAUNCH(fatn, (ffn_fat_kernel<DT, 2>), dim3(fat_grid), dim3(256), 0, st, a, ntn);
+    }
+#undef MOE_SK_LAUNCH
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
@@ -520,7 +664,7 @@ size_t ffn_plan_ints(const moe_cfg& c) {
   const int P = c.T * c.k;
   const int G = c.E + (c.I_shared > 0 ? 1 : 0);
   const int max_fat = ceil_div(P, kBM) + c.E + (c.I_shared > 0 ? ceil_div(c.T, kBM) : 0);
-  return 2 + (size_t)G + 2 * (size_t)max_fat;
+  return kPlanHead + 3 * (size_t)G + 2 * (size_t)max_fat;
 }
 
 size_t ffn_h_elem_bytes(const moe_cfg& c) { return c.w_dtype == MOE_BF16 ? 2 : 4; }

@@ -19,6 +19,7 @@ struct Mark {
 
 std::mutex g_mu;
 bool g_on = false;
+std::string g_only;   // empty: all kernels
 std::vector<Mark> g_marks;
 std::vector<hipEvent_t> g_pool;
 
@@ -40,6 +41,7 @@ namespace moe {
 ProfScope::ProfScope(const char* name, hipStream_t stream) : name_(name), stream_(stream) {
   std::lock_guard<std::mutex> lk(g_mu);
   if (!g_on) return;
+  if (!g_only.empty() && g_only != name) return;
   start_ = get_event();
   if (start_ && hipEventRecord(start_, stream) != hipSuccess) {
     g_pool.push_back(start_);
@@ -63,9 +65,10 @@ ProfScope::~ProfScope() {
 
 extern "C" {
 
-int moe_profile_start(void) {
+int moe_profile_start(const char* only) {
   std::lock_guard<std::mutex> lk(g_mu);
   g_on = true;
+  g_only = only ? only : "";
   return MOE_OK;
 }
 

@@ -175,21 +175,35 @@ __global__ __launch_bounds__(256) void gate_kernel(const uint8_t* __restrict__ x
   }
 }
 
-// Sum the split-K partial logits in split order, then select.  One wave per token.
+// Sum the split-K partial logits in split order, then select.  One workgroup
+// per token: thread e sums expert e's partials (8 independent loads in
+// flight, added in split order), wave 0 runs the selection.
 __global__ __launch_bounds__(256) void route_reduce_kernel(const float* __restrict__ part, int T, int nsplit,
                                                            RouteOut o) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
+  __shared__ float lg_s[kMaxE];
+  const int t = blockIdx.x;
+  const int e = threadIdx.x;
+  if (e < o.E) {
+    const float* p = part + (size_t)t * o.E + e;
+    const size_t stride = (size_t)T * o.E;
+    float v = 0.f;
+    int s = 0;
+    for (; s + 8 <= nsplit; s += 8) {
+      float q[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) q[u] = p[(size_t)(s + u) * stride];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v += q[u];
+    }
+    for (; s < nsplit; ++s) v += p[(size_t)s * stride];
+    lg_s[e] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
   float lg[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int e = lane + 64 * c;
-    float v = 0.f;
-    if (e < o.E)
-      for (int s = 0; s < nsplit; ++s) v += part[((size_t)s * T + t) * o.E + e];
-    lg[c] = v;
-  }
+  for (int c = 0; c < 4; ++c) lg[c] = lane + 64 * c < o.E ? lg_s[lane + 64 * c] : 0.f;
   route_token(lg, t, o);
 }
 
@@ -202,8 +216,8 @@ int route_splits(const moe_cfg& c) {
   const int kf = c.act_dtype == MOE_F32 ? Frag<MOE_F32>::KF : Frag<MOE_BF16>::KF;
   const int nfrag = c.H / kf;
   if (tiles >= 256) return 1;
-  int s = ceil_div(512, tiles);
-  const int smax = nfrag / 4 > 0 ? nfrag / 4 : 1;
+  int s = ceil_div(256, tiles);
+  const int smax = nfrag / 8 > 0 ? nfrag / 8 : 1;   // at least 8 fragments of K per split
   return s < smax ? s : smax;
 }
 
@@ -233,7 +247,7 @@ hipError_t launch_route(const moe_cfg& c, const void* x, const void* wg, const f
     MOE_LAUNCH("route_gate_split", (gate_kernel<MOE_BF16, false>), grid, block, 0, st, xb, wb, c.T, c.H, s, part, o);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  MOE_LAUNCH("route_reduce_select", route_reduce_kernel, dim3(ceil_div(c.T, 4)), block, 0, st, part, c.T, s, o);
+  MOE_LAUNCH("route_reduce_select", route_reduce_kernel, dim3(c.T), block, 0, st, part, c.T, s, o);
   return hipGetLastError();
 }
 

@@ -49,6 +49,10 @@ SMALL = {
                                                    I_shared=128),
     "one_token_bf16": get_config("decode16").with_(name="one_token_bf16", T=1, H=512, E=64, k=8, I=128,
                                                   I_shared=128),
+    # decode-sized shared experts (T <= 32) of each streaming variant, one per dtype
+    "t24_bf16": get_config("decode16").with_(name="t24_bf16", T=24, H=512, E=16, k=4, I=256, I_shared=256),
+    "t12_fp8": get_config("clustered2048_fp8").with_(name="t12_fp8", T=12, H=512, E=16, k=2, I=256, I_shared=256),
+    "t20_f32": get_config("tiny_f32").with_(name="t20_f32", T=20, E=8, k=2),
 }
 
 
