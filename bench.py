@@ -22,7 +22,6 @@ Only one GPU is used; --gpus above 1 exits with a message.
 """
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -35,26 +34,6 @@ METRIC = "MoE-layer tokens/s at 1 GPU + achieved HBM GB/s (decode) / MFMA % (pre
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 SKINNY_ROWS = 32          # groups with at most this many rows take the streaming (skinny) kernels
-KERNEL_SOURCES = {        # the source file each kernel is built from (for the counter freshness check)
-    **{f"ffn_gemm{g}_skinny_m{m}": "ffn.hip" for g in (1, 2) for m in (8, 16, 32)}, "ffn_gemm1_tiled": "ffn.hip",
-    "ffn_gemm1_shared_skinny": "ffn.hip", "ffn_gemm2_shared_skinny": "ffn.hip",
-    "ffn_gemm2_tiled": "ffn.hip", "ffn_plan": "ffn.hip", "route_gate_fused": "route.hip",
-    "route_gate_split": "route.hip", "route_reduce_select": "route.hip", "dispatch_count": "dispatch.hip",
-    "dispatch_scan": "dispatch.hip", "dispatch_scatter": "dispatch.hip", "quant_fp8": "quant.hip",
-    "combine": "combine.hip",
-}
-
-
-def kernel_source_hash(kernel: str) -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "mixture_experts_layer_11_amd", "csrc")
-    for f in (KERNEL_SOURCES.get(kernel, ""), "moe_common.h"):
-        p = os.path.join(csrc, f)
-        if os.path.isfile(p):
-            h.update(open(p, "rb").read())
-    return h.hexdigest()[:16]
-
-
 def kernel_models(cfg, counts):
     """Algorithmic bytes and FLOPs of each kernel per launch, from the counts.
 
@@ -115,6 +94,7 @@ def traffic_for(kernel, workload):
         d = json.load(open(p))
     except (OSError, ValueError):
         return None
+    from mixture_experts_layer_11_amd.profiling import kernel_source_hash
     if d.get("source_hash") != kernel_source_hash(kernel):
         return None
     return d.get("bytes_per_launch")

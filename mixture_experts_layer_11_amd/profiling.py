@@ -1,0 +1,175 @@
+"""Profiling helpers: library kernel names, rocprofv3 names, counter summaries.
+
+The library's profiler (moe_profile_start/stop) names kernels by role
+("ffn_gemm1_skinny_m8", ...); rocprofv3 reports demangled template names.
+``rocprof_name`` maps one to the other for a given weight dtype, and
+``kernel_source_hash`` fingerprints the sources a kernel is built from, so a
+stored counter reading is only used while the kernel is unchanged.
+
+CLI (writes profiles/<kernel>_<workload>.md and
+profiles/traffic_<kernel>_<workload>.json from rocprofv3 CSV output):
+
+  python -m mixture_experts_layer_11_amd.profiling --workload decode16 \\
+      --kernel ffn_gemm1_skinny_m8 --stats RUN_kernel_stats.csv \\
+      --fetch FETCH_counter_collection.csv --write WRITE_counter_collection.csv \\
+      --copy-fetch COPYF.csv --copy-write COPYW.csv --copy-bytes 1073741824 \\
+      --bench-log BENCH.log --command "..." [--command "..."]
+"""
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import statistics
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+
+KERNEL_SOURCES = {
+    **{f"ffn_gemm{g}_skinny_m{m}": "ffn.hip" for g in (1, 2) for m in (8, 16, 32)},
+    "ffn_gemm1_shared_skinny": "ffn.hip", "ffn_gemm2_shared_skinny": "ffn.hip",
+    "ffn_gemm1_tiled": "ffn.hip", "ffn_gemm2_tiled": "ffn.hip", "ffn_plan": "ffn.hip",
+    "route_gate_fused": "route.hip", "route_gate_split": "route.hip", "route_reduce_select": "route.hip",
+    "dispatch_count": "dispatch.hip", "dispatch_scan": "dispatch.hip", "dispatch_scatter": "dispatch.hip",
+    "quant_fp8": "quant.hip", "combine": "combine.hip",
+}
+
+_DT = {"f32": 0, "bf16": 1, "fp8": 2}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """sha256 prefix of the kernel's source file plus the shared device header."""
+    h = hashlib.sha256()
+    csrc = os.path.join(PKG, "csrc")
+    for f in (KERNEL_SOURCES.get(kernel, ""), "moe_common.h"):
+        p = os.path.join(csrc, f)
+        if os.path.isfile(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def rocprof_name(kernel: str, w_dtype: str) -> str:
+    """Prefix of the demangled name rocprofv3 reports for a library kernel."""
+    dt = _DT[w_dtype]
+    if kernel.startswith("ffn_gemm") and "_skinny_m" in kernel:
+        mode = int(kernel[8])
+        cls = {"8": 0, "16": 1, "32": 2}[kernel.rsplit("_m", 1)[1]]
+        return f"void (anonymous namespace)::ffn_skinny_kernel<{dt}, {mode}, {cls}>"
+    if kernel.startswith("ffn_gemm") and kernel.endswith("_tiled"):
+        return f"void (anonymous namespace)::ffn_fat_kernel<{dt}, {int(kernel[8])}>"
+    if kernel.startswith("ffn_gemm") and kernel.endswith("_shared_skinny"):
+        return f"void (anonymous namespace)::ffn_shared_skinny_kernel<{dt}, {int(kernel[8])}, "
+    fixed = {"ffn_plan": "(anonymous namespace)::ffn_plan_kernel",
+             "route_reduce_select": "(anonymous namespace)::route_reduce_kernel",
+             "dispatch_count": "(anonymous namespace)::dispatch_count_kernel",
+             "dispatch_scan": "(anonymous namespace)::dispatch_scan_kernel",
+             "dispatch_scatter": "(anonymous namespace)::dispatch_scatter_kernel",
+             "route_gate_fused": "void (anonymous namespace)::gate_kernel<",
+             "route_gate_split": "void (anonymous namespace)::gate_kernel<",
+             "combine": "void (anonymous namespace)::combine_kernel<",
+             "quant_fp8": "void (anonymous namespace)::quant_fp8_kernel<"}
+    return fixed[kernel]
+
+
+def _counter_values(path, prefix, counter):
+    vals = []
+    for r in csv.DictReader(open(path)):
+        if r["Kernel_Name"].startswith(prefix) and r["Counter_Name"] == counter:
+            vals.append(float(r["Counter_Value"]))
+    return vals
+
+
+def _copy_factor(path, counter, copy_bytes):
+    vals = []
+    for r in csv.DictReader(open(path)):
+        if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no copy dispatch with {counter} in {path}")
+    return copy_bytes / (statistics.median(vals) * 1024.0), vals
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--kernel", required=True)
+    ap.add_argument("--w-dtype", default=None)
+    ap.add_argument("--stats", required=True, help="rocprofv3 --kernel-trace --stats kernel_stats.csv")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--copy-fetch")
+    ap.add_argument("--copy-write")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--bench-log", help="output of the bench run profiled with --kernel-trace")
+    ap.add_argument("--command", action="append", default=[], help="command lines that produced the inputs")
+    ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
+    args = ap.parse_args(argv)
+
+    import sys
+    sys.path.insert(0, ROOT)
+    from moe_inputs import get_config
+    cfg = get_config(args.workload)
+    wdt = args.w_dtype or cfg.w_dtype
+    prefix = rocprof_name(args.kernel, wdt)
+
+    stats = [r for r in csv.DictReader(open(args.stats))]
+    ours = [r for r in stats if r["Name"].startswith(("void (anonymous namespace)::", "(anonymous namespace)::"))]
+    dom = [r for r in ours if r["Name"].startswith(prefix)]
+    if not dom:
+        raise SystemExit(f"{prefix} not in {args.stats}")
+    avg_us = float(dom[0]["AverageNs"]) / 1e3
+
+    bench = None
+    if args.bench_log:
+        for line in open(args.bench_log):
+            if line.startswith("{"):
+                bench = json.loads(line)
+
+    traffic = None
+    lines = [f"# {args.kernel} on {args.workload}", "",
+             f"Library kernel `{args.kernel}` = rocprofv3 `{prefix}...`.", "", "## Commands", ""]
+    lines += [f"    {c}" for c in args.command]
+    lines += ["", "## Kernel trace (rocprofv3 --kernel-trace --stats), library kernels", "",
+              "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for r in sorted(ours, key=lambda r: -float(r["TotalDurationNs"])):
+        nm = r["Name"].replace("(anonymous namespace)::", "").replace("void ", "")
+        nm = nm.split("(")[0] if "(" in nm else nm
+        lines.append(f"| `{nm}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
+                     f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} |")
+    lines += ["", f"Average duration of `{args.kernel}`: **{avg_us:.2f} us** (rocprofv3)."]
+    if bench:
+        r = bench["roofline"]
+        lines += [f"Same kernel timed live by bench.py with HIP events: **{r['kernel_avg_us']} us** "
+                  f"(kernel `{r['kernel']}`); algorithmic bytes per launch {r['algorithmic_per_launch']['bytes']}; "
+                  f"achieved {r['achieved']} {r['unit']} = {r['frac']:.3f} of {r['peak']}."]
+    if args.fetch and args.write and args.copy_fetch and args.copy_write:
+        ff, fv = _copy_factor(args.copy_fetch, "FETCH_SIZE", args.copy_bytes)
+        wf, wv = _copy_factor(args.copy_write, "WRITE_SIZE", args.copy_bytes)
+        fk = _counter_values(args.fetch, prefix, "FETCH_SIZE")
+        wk = _counter_values(args.write, prefix, "WRITE_SIZE")
+        fetch_b = statistics.median(fk) * 1024.0 * ff
+        write_b = statistics.median(wk) * 1024.0 * wf
+        traffic = fetch_b + write_b
+        lines += ["", "## HBM traffic (rocprofv3 --pmc, one counter per run)", "",
+                  f"Calibration: a plain {args.copy_bytes} B device copy reads FETCH_SIZE "
+                  f"{statistics.median(fv):.1f} KiB and WRITE_SIZE {statistics.median(wv):.1f} KiB per dispatch, "
+                  f"so FETCH_SIZE is scaled by {ff:.4f} and WRITE_SIZE by {wf:.4f}.", "",
+                  f"`{args.kernel}`: FETCH_SIZE median {statistics.median(fk):.1f} KiB over {len(fk)} dispatches "
+                  f"-> {fetch_b:.4e} B read; WRITE_SIZE median {statistics.median(wk):.1f} KiB -> {write_b:.4e} B "
+                  f"written; traffic {traffic:.4e} B per launch."]
+        if bench:
+            alg = bench["roofline"]["algorithmic_per_launch"]["bytes"]
+            lines.append(f"Algorithmic bytes per launch {alg:.4e} B: traffic / algorithmic = {traffic / alg:.4f}.")
+        rec = {"kernel": args.kernel, "workload": args.workload, "source_hash": kernel_source_hash(args.kernel),
+               "bytes_per_launch": traffic, "fetch_bytes": fetch_b, "write_bytes": write_b,
+               "fetch_scale": ff, "write_scale": wf, "commands": args.command}
+        with open(os.path.join(args.out_dir, f"traffic_{args.kernel}_{args.workload}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+    with open(os.path.join(args.out_dir, f"{args.kernel}_{args.workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    main()
