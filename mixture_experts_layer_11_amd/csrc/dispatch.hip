@@ -34,31 +34,73 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
   for (int e = threadIdx.x; e < E; e += blockDim.x) seg_counts[(size_t)blockIdx.x * E + e] = hist[e];
 }
 
-__global__ __launch_bounds__(256) void dispatch_scan_kernel(const int32_t* __restrict__ seg_counts, int nseg, int E,
-                                                            int32_t* __restrict__ seg_base,
-                                                            int32_t* __restrict__ counts,
-                                                            int32_t* __restrict__ offsets) {
+// TPE threads per expert (1024 / TPE experts per pass) each own a contiguous
+// run of segments: they total it (8 loads in flight), the runs' totals are
+// scanned in LDS, then each thread writes its segments' bases.
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ seg_counts, int nseg,
+                                                             int E, int tpe, int32_t* __restrict__ seg_base,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets) {
+  __shared__ int part[1024];
   __shared__ int tot[256];
-  const int e = threadIdx.x;
+  const int e = threadIdx.x / tpe;     // expert of this thread (E * tpe <= 1024)
+  const int q = threadIdx.x % tpe;     // its run of segments
+  const int s0 = (int)((long long)nseg * q / tpe), s1 = (int)((long long)nseg * (q + 1) / tpe);
   int run = 0;
   if (e < E) {
-    for (int s = 0; s < nseg; ++s) {
-      seg_base[(size_t)s * E + e] = run;
-      run += seg_counts[(size_t)s * E + e];
+    int s = s0;
+    for (; s + 8 <= s1; s += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = seg_counts[(size_t)(s + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) run += v[u];
     }
-    counts[e] = run;
+    for (; s < s1; ++s) run += seg_counts[(size_t)s * E + e];
   }
-  tot[e] = e < E ? run : 0;
+  part[threadIdx.x] = run;
   __syncthreads();
-  // inclusive Hillis-Steele scan over 256 entries
+  if (q == 0 && e < E) {                 // per-expert exclusive scan over its runs, in run order
+    int acc = 0;
+    for (int r = 0; r < tpe; ++r) {
+      const int v = part[e * tpe + r];
+      part[e * tpe + r] = acc;
+      acc += v;
+    }
+    counts[e] = acc;
+    tot[e] = acc;
+  }
+  __syncthreads();
+  if (e < E) {
+    int b = part[threadIdx.x];
+    int s = s0;
+    for (; s + 8 <= s1; s += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = seg_counts[(size_t)(s + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        seg_base[(size_t)(s + u) * E + e] = b;
+        b += v[u];
+      }
+    }
+    for (; s < s1; ++s) {
+      seg_base[(size_t)s * E + e] = b;
+      b += seg_counts[(size_t)s * E + e];
+    }
+  }
+  // exclusive scan of the expert totals (E <= 256) by the first 256 threads
+  if (threadIdx.x < 256 && threadIdx.x >= E) tot[threadIdx.x] = 0;
+  __syncthreads();
   for (int d = 1; d < 256; d <<= 1) {
-    const int v = e >= d ? tot[e - d] : 0;
+    int v = 0;
+    if (threadIdx.x < 256 && threadIdx.x >= d) v = tot[threadIdx.x - d];
     __syncthreads();
-    tot[e] += v;
+    if (threadIdx.x < 256) tot[threadIdx.x] += v;
     __syncthreads();
   }
-  if (e < E) offsets[e] = tot[e] - run;
-  if (e == E - 1) offsets[E] = tot[e];
+  if (threadIdx.x < E) offsets[threadIdx.x] = threadIdx.x == 0 ? 0 : tot[threadIdx.x - 1];
+  if (threadIdx.x == 0) offsets[E] = tot[E - 1];
 }
 
 __global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* __restrict__ idx, int P, int E,
@@ -110,8 +152,10 @@ hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, int32_t* counts
   MOE_LAUNCH("dispatch_count", dispatch_count_kernel, dim3(nseg), dim3(kSeg), 0, st, idx, P, c.E, seg_counts);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  MOE_LAUNCH("dispatch_scan", dispatch_scan_kernel, dim3(1), dim3(256), 0, st, seg_counts, nseg, c.E, seg_base, counts,
-                     offsets);
+  int tpe = 1;                       // threads per expert in the scan
+  while (tpe * 2 * c.E <= 1024 && tpe * 2 <= nseg) tpe *= 2;
+  MOE_LAUNCH("dispatch_scan", dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, seg_counts, nseg, c.E, tpe, seg_base,
+             counts, offsets);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   MOE_LAUNCH("dispatch_scatter", dispatch_scatter_kernel, dim3(nseg), dim3(64), 0, st, idx, P, c.E, offsets, seg_base,

@@ -38,9 +38,8 @@
 namespace {
 
 constexpr int kSkinnyRows = 32;  // groups with <= this many rows take the skinny path
+constexpr int kTileRows = 256;   // rows per tile of the tiled grouped GEMM
 constexpr int kPlanHead = 4;     // plan: [0..2] skinny list sizes (<=8, <=16, <=32 rows), [3] fat tiles
-constexpr int kBM = 128;         // fat tile rows
-constexpr int kBN = 128;         // fat tile columns (GEMM1: 64 gate + 64 up)
 
 struct Args {
   int T, H, E, k, I, P;
@@ -117,7 +116,7 @@ __global__ __launch_bounds__(512) void ffn_plan_kernel(Args a) {
   // expert has a launch of its own and is in no list)
   const bool shared = g == a.E;
   const int cls = (m > 0 && m <= kSkinnyRows && !shared) ? (m <= 8 ? 0 : m <= 16 ? 1 : 2) : -1;
-  const int tiles = m > kSkinnyRows ? (m + kBM - 1) / kBM : 0;
+  const int tiles = m > kSkinnyRows ? (m + kTileRows - 1) / kTileRows : 0;
 #pragma unroll
   for (int c = 0; c < 3; ++c) sk[c][g] = cls == c ? 1 : 0;
   ft[g] = tiles;
@@ -144,7 +143,7 @@ __global__ __launch_bounds__(512) void ffn_plan_kernel(Args a) {
   int32_t* fat = plan + kPlanHead + 3 * a.G;
   for (int i = 0; i < tiles; ++i) {
     fat[2 * (t0 + i)] = g;
-    fat[2 * (t0 + i) + 1] = i * kBM;
+    fat[2 * (t0 + i) + 1] = i * kTileRows;
   }
 }
 
@@ -409,19 +408,72 @@ __global__ __launch_bounds__(64 * kShKS) void ffn_shared_skinny_kernel(Args a) {
   skinny_tile<DT, MODE, MT, kShNT, kShKS>(a, gr, a.E, blockIdx.x, lane, ks, red);
 }
 
-// ------------------------------------------------------------------ fat grouped GEMM
+// ------------------------------------------------------------------ tiled grouped GEMM
+//
+// 256 x 256 output tile per workgroup of 8 waves (4 along M x 2 along N, each
+// 64 x 128 with 16x16 MFMAs).  K advances in slices of SL bytes per row: each
+// slice of the 256 A rows and the 256 B rows goes global -> LDS directly (16
+// bytes per lane per instruction) into an NST-deep ring of LDS stages, so the
+// loads run NST - 1 slices ahead of the MFMAs and there is one barrier per
+// slice.  bf16/fp32 use 64-byte slices with 4 stages; fp8 uses 128-byte
+// slices (one scale block) with 2 stages.  LDS rows are SL bytes with 16-byte
+// chunk c of row r stored at chunk c ^ swizzle(r), which keeps the fragment
+// reads of 16 consecutive rows free of bank conflicts; the direct loads write
+// chunks in lane order, so each lane fetches the global chunk that belongs
+// at its position.  Waves whose 64 rows lie beyond the tile's valid rows skip
+// their MFMAs.
 
-// LDS tile: 128 rows x 128 bytes, 16-byte chunk c of row r stored at chunk c ^ (r & 7).
-__device__ __forceinline__ int lds_off(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+constexpr int kTM = 256;                  // tile rows (tokens)
+constexpr int kTN = 256;                  // tile columns (weight rows; GEMM1: 128 gate + 128 up)
+
+template <int DT> struct TileCfg {
+  static constexpr int SL = 128;                              // bytes of K per slice and row
+  static constexpr int NST = 2;                               // LDS stages
+  static constexpr int CPR = SL / 16;                         // 16-byte chunks per row
+  static constexpr int STAGE = (kTM + kTN) * SL;              // bytes per stage (A then B)
+  static constexpr int LPS = SL / 32;                         // direct loads per thread per slice, A and B each
+  static constexpr int ROWS_PER_INSTR = 1024 / SL;            // rows one wave instruction fills
+  __device__ static __forceinline__ int off(int r, int c) {
+    const int sw = SL == 128 ? (r & 7) : ((r >> 2) & 3);
+    return r * SL + ((c ^ sw) << 4);
+  }
+};
+
+// s_waitcnt that waits for vmcnt <= n only (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Issue the direct global -> LDS loads of slice kt into stage st (and, for
+// fp8, store the scale fetched one slice earlier and fetch the next one).
+template <int DT>
+__device__ __forceinline__ void tile_issue(uint8_t* smem, const uint8_t* const* ga, const uint8_t* const* gb, int kt,
+                                           int st, int wave, int tid, int nkt, float* lds_s, const float* gs,
+                                           float& rs) {
+  using C = TileCfg<DT>;
+  const size_t off = (size_t)kt * C::SL;
+  uint8_t* la = smem + st * C::STAGE + wave * C::LPS * 1024;
+  uint8_t* lb = smem + st * C::STAGE + kTM * C::SL + wave * C::LPS * 1024;
+#pragma unroll
+  for (int i = 0; i < C::LPS; ++i) {
+    __builtin_amdgcn_global_load_lds(ga[i] + off, la + i * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(gb[i] + off, lb + i * 1024, 16, 0, 0);
+  }
+  if constexpr (DT == MOE_FP8_E4M3) {
+    lds_s[st * (kTM + kTN) + tid] = rs;
+    if (kt + 1 < nkt) rs = gs[kt + 1];            // consumed one slice later
+  }
+}
 
 template <int DT, int MODE>
-__global__ __launch_bounds__(256) void ffn_fat_kernel(Args a, int ntn) {
+__global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
   using F = Frag<DT>;
+  using C = TileCfg<DT>;
   constexpr bool FP8 = DT == MOE_FP8_E4M3;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][kBM * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][kBN * 128];
-  __shared__ float lds_sa[2][FP8 ? kBM : 1];
-  __shared__ float lds_sb[2][FP8 ? kBN : 1];
+  constexpr int SL = C::SL, NST = C::NST, LPS = C::LPS, RPI = C::ROWS_PER_INSTR;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  float* lds_s = reinterpret_cast<float*>(smem + NST * C::STAGE);   // fp8: [NST][kTM + kTN]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -434,25 +486,13 @@ __global__ __launch_bounds__(256) void ffn_fat_kernel(Args a, int ntn) {
   const int g = fat[2 * tile];
   const int row0 = fat[2 * tile + 1];
   const Group gr = group_of(a, g);
-  const int rows = min(kBM, gr.m - row0);
+  const int rows = min(kTM, gr.m - row0);
   const int K = MODE == 1 ? a.H : a.I;
   const size_t krow = (size_t)K * F::ESZ;
-  const int nkt = (int)(krow / 128);          // 128-byte K slices
+  const int nkt = (int)(krow / SL);
   const int nkb = FP8 ? K / a.qb : 0;
 
-  // ---- global source rows for this thread's 4 A chunks and 4 B chunks
-  const int lc = tid & 7;          // 16-byte chunk within the 128-byte slice
-  const int lr = tid >> 3;         // base row 0..31; rows lr + 32*i
-  const uint8_t* ga[4];
-  const uint8_t* gb[4];
   const uint8_t* asrc = MODE == 1 ? a.a1 : a.a2;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = lr + 32 * i;
-    const int rr = r < rows ? r : rows - 1;      // clamp: padded rows recompute a valid row, never stored
-    const int src = MODE == 1 ? gemm1_src_row(a, gr, row0 + rr) : gr.slot0 + row0 + rr;
-    ga[i] = asrc + (size_t)src * krow + lc * 16;
-  }
   const uint8_t* wbase;
   const float* wsbase = nullptr;
   if (MODE == 1) {
@@ -462,116 +502,149 @@ __global__ __launch_bounds__(256) void ffn_fat_kernel(Args a, int ntn) {
     wbase = gr.routed ? a.w2 + (size_t)g * a.H * krow : a.ws2;
     if (FP8) wsbase = gr.routed ? a.w2s + (size_t)g * a.H * nkb : a.ws2s;
   }
-  auto b_wrow = [&](int n) -> int {   // weight row of LDS B row n
+  // Weight row held by LDS B row n; columns past N (a partial last column
+  // tile) are clamped to the last valid row and never stored.
+  auto b_wrow = [&](int n) -> int {
     if (MODE == 1) {
-      const int blk = n >> 4;          // 16-row block: even = gate, odd = up
-      return ((blk & 1) ? a.I : 0) + nt * (kBN / 2) + (blk >> 1) * 16 + (n & 15);
+      const int blk = n >> 4;          // 16-row blocks alternate gate, up
+      const int hc = min(nt * (kTN / 2) + (blk >> 1) * 16 + (n & 15), a.I - 1);
+      return ((blk & 1) ? a.I : 0) + hc;
     }
-    return nt * kBN + n;
+    return min(nt * kTN + n, a.H - 1);
   };
+  // This lane's direct-load sources.  Wave instruction i fills LDS rows
+  // (wave * LPS + i) * RPI + lane / CPR, physical chunk lane % CPR.
+  const uint8_t* ga[LPS];
+  const uint8_t* gb[LPS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) gb[i] = wbase + (size_t)b_wrow(lr + 32 * i) * krow + lc * 16;
-
-  // fp8 scale sources: thread tid < 128 loads A-row scale tid, 128..255 B-row scale tid-128
+  for (int i = 0; i < LPS; ++i) {
+    const int r = (wave * LPS + i) * RPI + lane / C::CPR;
+    const int pc = lane % C::CPR;
+    const int lc = (C::off(r, pc) - r * SL) >> 4;   // the swizzle is an involution: logical chunk of physical pc
+    const int rr = r < rows ? r : rows - 1;          // clamp: padded rows recompute a valid row, never stored
+    const int src = MODE == 1 ? gemm1_src_row(a, gr, row0 + rr) : gr.slot0 + row0 + rr;
+    ga[i] = asrc + (size_t)src * krow + lc * 16;
+    gb[i] = wbase + (size_t)b_wrow(r) * krow + lc * 16;
+  }
+  // fp8 scales: thread tid < kTM loads A-row scale tid, the rest B-row scale tid - kTM
   const float* gs = nullptr;
   if constexpr (FP8) {
-    if (tid < kBM) {
+    if (tid < kTM) {
       const int r = tid < rows ? tid : rows - 1;
       const int src = MODE == 1 ? gemm1_src_row(a, gr, row0 + r) : gr.slot0 + row0 + r;
       gs = (MODE == 1 ? a.a1s : a.a2s) + (size_t)src * nkb;
     } else {
-      gs = wsbase + (size_t)b_wrow(tid - kBM) * nkb;
+      gs = wsbase + (size_t)b_wrow(tid - kTM) * nkb;
     }
   }
+  float rs = 0.f;                                  // fp8: scale for the next slice to issue
+  if constexpr (FP8) rs = gs[0];
 
-  i32x4 ra[4], rb[4];
-  float rs = 0.f;
-  auto gload = [&](int kt) {
-    const size_t off = (size_t)kt * 128;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = ld16(ga[i] + off);
-      rb[i] = ld16(gb[i] + off);
-    }
-    if constexpr (FP8) rs = gs[kt];
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = lr + 32 * i;
-      *reinterpret_cast<i32x4*>(&lds_a[buf][lds_off(r, lc)]) = ra[i];
-      *reinterpret_cast<i32x4*>(&lds_b[buf][lds_off(r, lc)]) = rb[i];
-    }
-    if constexpr (FP8) {
-      if (tid < kBM) lds_sa[buf][tid] = rs;
-      else lds_sb[buf][tid - kBM] = rs;
-    }
-  };
-
-  f32x4 acc[4][4];
+  f32x4 acc[4][8];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int mval = min(4, max(0, (rows - wm * 64 + 15) >> 4));   // this wave's M tiles holding valid rows
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < NST - 1; ++p)
+    if (p < nkt) tile_issue<DT>(smem, ga, gb, p, p, wave, tid, nkt, lds_s, gs, rs);
   for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nkt) gload(kt + 1);
-    const uint8_t* la = lds_a[buf];
-    const uint8_t* lb = lds_b[buf];
+    const int st = kt % NST;
+    // wait until this thread's loads of slice kt have landed; later slices may stay in flight
+    if constexpr (FP8) {
+      __builtin_amdgcn_s_waitcnt(0);
+    } else {
+      const int ahead = min(NST - 2, nkt - 1 - kt);   // slices issued after kt
+      if (ahead >= 2) wait_vmcnt<4 * LPS>();
+      else if (ahead == 1) wait_vmcnt<2 * LPS>();
+      else wait_vmcnt<0>();
+    }
+    __syncthreads();                               // everyone's slice kt is in LDS; stage (kt-1) % NST is free
+    if (kt + NST - 1 < nkt)
+      tile_issue<DT>(smem, ga, gb, kt + NST - 1, (kt + NST - 1) % NST, wave, tid, nkt, lds_s, gs, rs);
+    const uint8_t* la = smem + st * C::STAGE;
+    const uint8_t* lb = la + kTM * SL;
     if constexpr (!FP8) {
+      // Full tiles: all fragments of the slice are read first and the MFMAs
+      // follow in the same straight-line block, so the compiler can start the
+      // first half's MFMAs while the second half's reads are in flight.  Only
+      // a group's last, partial tile takes the guarded path that skips M tiles.
+      if (mval == 4) {
+        i32x4 fa[SL / 64][4], fb[SL / 64][8];
 #pragma unroll
-      for (int fs = 0; fs < 2; ++fs) {
-        i32x4 fa[4], fb[4];
+        for (int fs = 0; fs < SL / 64; ++fs) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const i32x4*>(&la[lds_off(wm * 64 + i * 16 + row, fs * 4 + grp)]);
+          for (int j = 0; j < 8; ++j)
+            fb[fs][j] = *reinterpret_cast<const i32x4*>(&lb[C::off(wn * 128 + j * 16 + row, fs * 4 + grp)]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const i32x4*>(&lb[lds_off(wn * 64 + j * 16 + row, fs * 4 + grp)]);
+          for (int i = 0; i < 4; ++i)
+            fa[fs][i] = *reinterpret_cast<const i32x4*>(&la[C::off(wm * 64 + i * 16 + row, fs * 4 + grp)]);
+        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int fs = 0; fs < SL / 64; ++fs)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) F::mma(acc[i][j], fa[i], fb[j]);
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) F::mma(acc[i][j], fa[fs][i], fb[fs][j]);
+      } else if (mval > 0) {
+#pragma unroll
+        for (int fs = 0; fs < SL / 64; ++fs) {
+          i32x4 fb[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            fb[j] = *reinterpret_cast<const i32x4*>(&lb[C::off(wn * 128 + j * 16 + row, fs * 4 + grp)]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i < mval) {
+              const i32x4 fa = *reinterpret_cast<const i32x4*>(&la[C::off(wm * 64 + i * 16 + row, fs * 4 + grp)]);
+#pragma unroll
+              for (int j = 0; j < 8; ++j) F::mma(acc[i][j], fa, fb[j]);
+            }
+        }
       }
     } else {
-      i32x4 fa0[4], fa1[4], fb0[4], fb1[4];
+      const float* sa_l = lds_s + st * (kTM + kTN);
+      const float* sb_l = sa_l + kTM;
+      // two halves of 4 column tiles keep the B fragments within the register budget
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * 64 + i * 16 + row;
-        fa0[i] = *reinterpret_cast<const i32x4*>(&la[lds_off(r, grp)]);
-        fa1[i] = *reinterpret_cast<const i32x4*>(&la[lds_off(r, 4 + grp)]);
-      }
+      for (int jh = 0; jh < 2; ++jh) {
+        i32x4 fb0[4], fb1[4];
+        float sb[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = wn * 64 + j * 16 + row;
-        fb0[j] = *reinterpret_cast<const i32x4*>(&lb[lds_off(n, grp)]);
-        fb1[j] = *reinterpret_cast<const i32x4*>(&lb[lds_off(n, 4 + grp)]);
-      }
-      float sa[4][4], sb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sa[i][q] = lds_sa[buf][wm * 64 + i * 16 + 4 * grp + q];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sb[j] = lds_sb[buf][wn * 64 + j * 16 + row];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 p = F::mma128(fa0[i], fa1[i], fb0[j], fb1[j]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(p[q], sa[i][q] * sb[j], acc[i][j][q]);
+        for (int jj = 0; jj < 4; ++jj) {
+          const int n = wn * 128 + (4 * jh + jj) * 16 + row;
+          fb0[jj] = *reinterpret_cast<const i32x4*>(&lb[C::off(n, grp)]);
+          fb1[jj] = *reinterpret_cast<const i32x4*>(&lb[C::off(n, 4 + grp)]);
+          sb[jj] = sb_l[n];
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i < mval) {
+            const int r = wm * 64 + i * 16 + row;
+            const i32x4 fa0 = *reinterpret_cast<const i32x4*>(&la[C::off(r, grp)]);
+            const i32x4 fa1 = *reinterpret_cast<const i32x4*>(&la[C::off(r, 4 + grp)]);
+            float sa[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sa[q] = sa_l[wm * 64 + i * 16 + 4 * grp + q];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const f32x4 p = F::mma128(fa0, fa1, fb0[jj], fb1[jj]);
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                acc[i][4 * jh + jj][q] = fmaf(p[q], sa[q] * sb[jj], acc[i][4 * jh + jj][q]);
+            }
+          }
+        }
+      }
     }
-    if (kt + 1 < nkt) lstore(buf ^ 1);
-    __syncthreads();
   }
 
-  // ---- epilogue: lane holds rows wm*64 + i*16 + 4*grp + q, columns wn*64 + j*16 + row
+  // ---- epilogue: lane holds rows wm*64 + i*16 + 4*grp + q, columns wn*128 + j*16 + row
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    if (i >= mval) break;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = wm * 64 + i * 16 + 4 * grp + q;
@@ -579,19 +652,38 @@ __global__ __launch_bounds__(256) void ffn_fat_kernel(Args a, int ntn) {
       if (MODE == 1) {
         const size_t hrow = (size_t)(gr.slot0 + row0 + r) * a.I;
 #pragma unroll
-        for (int jp = 0; jp < 2; ++jp) {
+        for (int jp = 0; jp < 4; ++jp) {
           const float gv = acc[i][2 * jp][q], uv = acc[i][2 * jp + 1][q];
-          const int col = nt * (kBN / 2) + (2 * wn + jp) * 16 + row;
-          store_h<DT>(a.h, hrow + col, silu(gv) * uv);
+          const int col = nt * (kTN / 2) + (4 * wn + jp) * 16 + row;
+          if (col < a.I) store_h<DT>(a.h, hrow + col, silu(gv) * uv);
         }
       } else {
         float* yrow = gr.routed ? a.y_sorted + (size_t)(gr.slot0 + row0 + r) * a.H
                                 : a.y_shared + (size_t)(row0 + r) * a.H;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) yrow[nt * kBN + wn * 64 + j * 16 + row] = acc[i][j][q];
+        for (int j = 0; j < 8; ++j) {
+          const int col = nt * kTN + wn * 128 + j * 16 + row;
+          if (col < a.H) yrow[col] = acc[i][j][q];
+        }
       }
     }
   }
+}
+
+template <int DT, int MODE>
+hipError_t launch_fat(const char* name, int grid, int ntn, const Args& a, hipStream_t st) {
+  constexpr bool FP8 = DT == MOE_FP8_E4M3;
+  using C = TileCfg<DT>;
+  const size_t smem = (size_t)C::NST * C::STAGE + (FP8 ? C::NST * (kTM + kTN) * sizeof(float) : 0);
+  static bool attr_set = false;   // raise the dynamic-LDS limit once per process
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_fat_kernel<DT, MODE>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  MOE_LAUNCH(name, (ffn_fat_kernel<DT, MODE>), dim3(grid), dim3(512), smem, st, a, ntn);
+  return hipGetLastError();
 }
 
 template <int DT>
@@ -601,8 +693,8 @@ hipError_t run_ffn(const moe_cfg& c, Args a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int P = a.P;
-  const int max_fat = moe::ceil_div(P, kBM) + (P / (kSkinnyRows + 1) < c.E ? P / (kSkinnyRows + 1) : c.E) +
-                      (a.has_shared ? moe::ceil_div(c.T, kBM) : 0);
+  const int max_fat = moe::ceil_div(P, kTileRows) + (P / (kSkinnyRows + 1) < c.E ? P / (kSkinnyRows + 1) : c.E) +
+                      (a.has_shared ? moe::ceil_div(c.T, kTileRows) : 0);
   for (int mode = 1; mode <= 2; ++mode) {
     if (mode == 2 && DT == MOE_FP8_E4M3) {
       e = moe::launch_quant_fp8(P + (a.has_shared ? c.T : 0), c.I, a.qb, a.h, MOE_F32,
@@ -618,7 +710,7 @@ hipError_t run_ffn(const moe_cfg& c, Args a, hipStream_t st) {
       const int bound = P / min_rows;
       sk_groups[cls] = bound < G ? bound : G;
     }
-    const int ntn = mode == 1 ? c.I / (kBN / 2) : c.H / kBN;
+    const int ntn = mode == 1 ? moe::ceil_div(c.I, kTN / 2) : moe::ceil_div(c.H, kTN);
     const int fat_grid = max_fat * ntn;
     static const char* const kSkName[2][3] = {
         {"ffn_gemm1_skinny_m8", "ffn_gemm1_skinny_m16", "ffn_gemm1_skinny_m32"},
@@ -645,10 +737,10 @@ hipError_t run_ffn(const moe_cfg& c, Args a, hipStream_t st) {
     }
     if (mode == 1) {
       MOE_SK_LAUNCH(1, 0) MOE_SK_LAUNCH(1, 1) MOE_SK_LAUNCH(1, 2)
-      if (fat_grid > 0) MOE_LAUNCH(fatn, (ffn_fat_kernel<DT, 1>), dim3(fat_grid), dim3(256), 0, st, a, ntn);
+      if (fat_grid > 0 && (e = launch_fat<DT, 1>(fatn, fat_grid, ntn, a, st)) != hipSuccess) return e;
     } else {
       MOE_SK_LAUNCH(2, 0) MOE_SK_LAUNCH(2, 1) MOE_SK_LAUNCH(2, 2)
-      if (fat_grid > 0) MOE_LAUNCH(fatn, (ffn_fat_kernel<DT, 2>), dim3(fat_grid), dim3(256), 0, st, a, ntn);
+      if (fat_grid > 0 && (e = launch_fat<DT, 2>(fatn, fat_grid, ntn, a, st)) != hipSuccess) return e;
     }
 #undef MOE_SK_LAUNCH
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -663,7 +755,7 @@ namespace moe {
 size_t ffn_plan_ints(const moe_cfg& c) {
   const int P = c.T * c.k;
   const int G = c.E + (c.I_shared > 0 ? 1 : 0);
-  const int max_fat = ceil_div(P, kBM) + c.E + (c.I_shared > 0 ? ceil_div(c.T, kBM) : 0);
+  const int max_fat = ceil_div(P, kTileRows) + c.E + (c.I_shared > 0 ? ceil_div(c.T, kTileRows) : 0);
   return kPlanHead + 3 * (size_t)G + 2 * (size_t)max_fat;
 }
 

@@ -23,7 +23,6 @@ namespace {
 
 constexpr int kTokTile = 16;
 constexpr int kMaxE = 256;
-constexpr int kLdsStride = kMaxE + 4;
 
 struct RouteOut {
   const float* bias;   // [E] or nullptr
@@ -93,62 +92,85 @@ __device__ void route_token(const float (&lg)[4], int t, const RouteOut& o) {
   }
 }
 
-// Gate GEMM over fragments [f0, f1) of K for a 16-token tile.
-template <int DT, bool FUSED>
+// Gate GEMM over fragments [f0, f1) of K for a 16-token tile.  The four
+// waves split the range four ways; each accumulates all ceil(E/16) expert
+// tiles (MAXT >= that count) and the four partials are added in wave order
+// through LDS (fixed order: reproducible).
+template <int DT, bool FUSED, int MAXT>
 __global__ __launch_bounds__(256) void gate_kernel(const uint8_t* __restrict__ x, const uint8_t* __restrict__ wg,
                                                    int T, int H, int nsplit, float* __restrict__ part,
                                                    RouteOut o) {
   using F = Frag<DT>;
-  __shared__ float lds[FUSED ? kTokTile * kLdsStride : 1];
+  extern __shared__ float red[];                  // [4 waves][16 tokens][ldw]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, grp = lane >> 4;
   const int t0 = blockIdx.x * kTokTile;
   const int s = blockIdx.y;
   const int nfrag = H / F::KF;
   const int f0 = (int)((long long)nfrag * s / nsplit), f1 = (int)((long long)nfrag * (s + 1) / nsplit);
+  const int wf0 = f0 + (int)((long long)(f1 - f0) * wave / 4), wf1 = f0 + (int)((long long)(f1 - f0) * (wave + 1) / 4);
   const int E = o.E;
   const int ntiles = (E + 15) >> 4;
+  const int ldw = ntiles * 16 + 4;
   const size_t rowbytes = (size_t)H * F::ESZ;
 
   const int t = t0 + row;
-  const bool tval = t < T;
-  const uint8_t* pa = x + (size_t)(tval ? t : 0) * rowbytes + grp * 16;
-  const uint8_t* pb[4];
-  bool ev[4];
+  const uint8_t* pa = x + (size_t)(t < T ? t : T - 1) * rowbytes + grp * 16;   // rows past T: never stored
+  const uint8_t* pb[MAXT];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int e = (wave + 4 * j) * 16 + row;
-    ev[j] = e < E;
-    pb[j] = wg + (size_t)(ev[j] ? e : 0) * rowbytes + grp * 16;
+  for (int j = 0; j < MAXT; ++j) {
+    const int e = min(j * 16 + row, E - 1);     // experts past E: never selected
+    pb[j] = wg + (size_t)e * rowbytes + grp * 16;
   }
-  f32x4 acc[4];
+  f32x4 acc[MAXT];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < MAXT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll 4
-  for (int f = f0; f < f1; ++f) {
+  constexpr int U = MAXT >= 8 ? 1 : (MAXT >= 4 ? 2 : 4);   // fragments per trip: ~8 loads in flight
+  int f = wf0;
+  for (; f + U <= wf1; f += U) {
+    i32x4 av[U], bv[U][MAXT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t off = (size_t)(f + u) * 64;
+      av[u] = ld16(pa + off);
+#pragma unroll
+      for (int j = 0; j < MAXT; ++j)
+        if (j < ntiles) bv[u][j] = ld16(pb[j] + off);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < MAXT; ++j)
+        if (j < ntiles) F::mma(acc[j], av[u], bv[u][j]);
+  }
+  for (; f < wf1; ++f) {
     const size_t off = (size_t)f * 64;
-    const i32x4 a = tval ? ld16(pa + off) : zero16();
+    const i32x4 av = ld16(pa + off);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (wave + 4 * j < ntiles) {
-        const i32x4 b = ev[j] ? ld16(pb[j] + off) : zero16();
-        F::mma(acc[j], a, b);
-      }
-    }
+    for (int j = 0; j < MAXT; ++j)
+      if (j < ntiles) F::mma(acc[j], av, ld16(pb[j] + off));
   }
 
-  // acc[j][i] = logit of token t0 + 4*grp + i, expert (wave + 4j)*16 + row
-  if constexpr (FUSED) {
+  // acc[j][i] = partial logit of token t0 + 4*grp + i, expert 16*j + row
+  float* mine = red + (size_t)wave * 16 * ldw;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = (wave + 4 * j) * 16 + row;
-      if (wave + 4 * j < ntiles) {
+  for (int j = 0; j < MAXT; ++j)
+    if (j < ntiles) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds[(4 * grp + i) * kLdsStride + e] = acc[j][i];
-      }
+      for (int i = 0; i < 4; ++i) mine[(4 * grp + i) * ldw + 16 * j + row] = acc[j][i];
     }
-    __syncthreads();
+  __syncthreads();
+  // sum the four waves in order into wave 0's region
+  for (int idx = threadIdx.x; idx < 16 * ntiles * 16; idx += 256) {
+    const int r = idx / (ntiles * 16), e = idx % (ntiles * 16);
+    float v = red[r * ldw + e];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v += red[(size_t)w * 16 * ldw + r * ldw + e];
+    red[r * ldw + e] = v;
+  }
+  __syncthreads();
+  if constexpr (FUSED) {
     for (int r = wave * 4; r < wave * 4 + 4; ++r) {
       const int tt = t0 + r;
       if (tt >= T) break;
@@ -156,21 +178,15 @@ __global__ __launch_bounds__(256) void gate_kernel(const uint8_t* __restrict__ x
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int e = lane + 64 * c;
-        lg[c] = e < E ? lds[r * kLdsStride + e] : 0.f;
+        lg[c] = e < E ? red[r * ldw + e] : 0.f;
       }
       route_token(lg, tt, o);
     }
   } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = (wave + 4 * j) * 16 + row;
-      if (wave + 4 * j < ntiles && e < E) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tt = t0 + 4 * grp + i;
-          if (tt < T) part[((size_t)s * T + tt) * E + e] = acc[j][i];
-        }
-      }
+    for (int idx = threadIdx.x; idx < 16 * E; idx += 256) {
+      const int r = idx / E, e = idx % E;
+      const int tt = t0 + r;
+      if (tt < T) part[((size_t)s * T + tt) * E + e] = red[r * ldw + e];
     }
   }
 }
@@ -226,28 +242,44 @@ size_t route_ws_bytes(const moe_cfg& c) {
   return s > 1 ? (size_t)s * c.T * c.E * sizeof(float) : 0;
 }
 
+template <int DT, bool FUSED>
+static void launch_gate(const moe_cfg& c, dim3 grid, const uint8_t* xb, const uint8_t* wb, int s, float* part,
+                        const RouteOut& o, hipStream_t st) {
+  const int ntiles = ceil_div(c.E, 16);
+  const size_t smem = (size_t)4 * 16 * (ntiles * 16 + 4) * sizeof(float);
+  const char* name = FUSED ? "route_gate_fused" : "route_gate_split";
+  if (ntiles <= 2)
+    MOE_LAUNCH(name, (gate_kernel<DT, FUSED, 2>), grid, dim3(256), smem, st, xb, wb, c.T, c.H, s, part, o);
+  else if (ntiles <= 4)
+    MOE_LAUNCH(name, (gate_kernel<DT, FUSED, 4>), grid, dim3(256), smem, st, xb, wb, c.T, c.H, s, part, o);
+  else if (ntiles <= 8)
+    MOE_LAUNCH(name, (gate_kernel<DT, FUSED, 8>), grid, dim3(256), smem, st, xb, wb, c.T, c.H, s, part, o);
+  else
+    MOE_LAUNCH(name, (gate_kernel<DT, FUSED, 16>), grid, dim3(256), smem, st, xb, wb, c.T, c.H, s, part, o);
+}
+
 hipError_t launch_route(const moe_cfg& c, const void* x, const void* wg, const float* bias, int32_t* idx,
                         float* w, float* part, hipStream_t st) {
   RouteOut o{bias, idx, w, c.E, c.k, c.score, c.routed_scale};
   const int tiles = ceil_div(c.T, kTokTile);
   const int s = route_splits(c);
-  dim3 grid(tiles, s), block(256);
+  dim3 grid(tiles, s);
   const uint8_t* xb = static_cast<const uint8_t*>(x);
   const uint8_t* wb = static_cast<const uint8_t*>(wg);
   if (s == 1) {
     if (c.act_dtype == MOE_F32)
-      MOE_LAUNCH("route_gate_fused", (gate_kernel<MOE_F32, true>), grid, block, 0, st, xb, wb, c.T, c.H, 1, nullptr, o);
+      launch_gate<MOE_F32, true>(c, grid, xb, wb, 1, nullptr, o, st);
     else
-      MOE_LAUNCH("route_gate_fused", (gate_kernel<MOE_BF16, true>), grid, block, 0, st, xb, wb, c.T, c.H, 1, nullptr, o);
+      launch_gate<MOE_BF16, true>(c, grid, xb, wb, 1, nullptr, o, st);
     return hipGetLastError();
   }
   if (c.act_dtype == MOE_F32)
-    MOE_LAUNCH("route_gate_split", (gate_kernel<MOE_F32, false>), grid, block, 0, st, xb, wb, c.T, c.H, s, part, o);
+    launch_gate<MOE_F32, false>(c, grid, xb, wb, s, part, o, st);
   else
-    MOE_LAUNCH("route_gate_split", (gate_kernel<MOE_BF16, false>), grid, block, 0, st, xb, wb, c.T, c.H, s, part, o);
+    launch_gate<MOE_BF16, false>(c, grid, xb, wb, s, part, o, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  MOE_LAUNCH("route_reduce_select", route_reduce_kernel, dim3(c.T), block, 0, st, part, c.T, s, o);
+  MOE_LAUNCH("route_reduce_select", route_reduce_kernel, dim3(c.T), dim3(256), 0, st, part, c.T, s, o);
   return hipGetLastError();
 }
 
