@@ -65,7 +65,7 @@ def kernel_models(cfg, counts):
         g1, g2 = m[f"ffn_gemm1_{reg}"], m[f"ffn_gemm2_{reg}"]
         g1["bytes"] += 2 * I * H * wb + sc13 + mg * H * a1b + mg * I * hb_out + (mg * H // qb * 4 if fp8 else 0)
         g1["flops"] += 2 * mg * 2 * I * H
-        g2["bytes"] += H * I * wb + sc2 + mg * I * a2b + mg * H * 4 + (mg * I // qb * 4 if fp8 else 0)
+        g2["bytes"] += H * I * wb + sc2 + mg * I * a2b + mg * H * ab + (mg * I // qb * 4 if fp8 else 0)
         g2["flops"] += 2 * mg * H * I
     touched = sum(1 for c in counts if int(c) > 0)
     layer_bytes = (touched + (1 if cfg.I_shared else 0)) * (3 * H * I * wb + sc13 + sc2) \

@@ -131,18 +131,20 @@ int moe_quantize_fp8(int32_t rows, int32_t cols, int32_t block, const void* in, 
  * grouped GEMM; Perplexity, "GroupGEMM"), and the shared expert over all T
  * rows.  SwiGLU(a) = (SiLU(a W1^T) * (a W3^T)) W2^T.  For FP8 weights, x and
  * the SwiGLU output are block-quantised per row per quant_block first.
+ * Accumulation is fp32; outputs are rounded once to act_dtype.
  *   x           [T, H] act_dtype; offsets / sorted_pair from moe_dispatch
- *   y_sorted    [T*k, H] fp32 out: row s = expert output of pair sorted_pair[s]
- *   y_shared    [T, H] fp32 out (NULL iff I_shared == 0)
+ *   y_sorted    [T*k, H] act_dtype out: row s = expert output of pair sorted_pair[s]
+ *   y_shared    [T, H] act_dtype out (NULL iff I_shared == 0)
  * Per-expert row counts are read on the device (no host sync). */
 int moe_expert_ffn(const moe_cfg* cfg, const void* x, const int32_t* offsets,
-                   const int32_t* sorted_pair, const moe_weights* w, float* y_sorted,
-                   float* y_shared, void* ws, size_t ws_bytes, void* hip_stream);
+                   const int32_t* sorted_pair, const moe_weights* w, void* y_sorted,
+                   void* y_shared, void* ws, size_t ws_bytes, void* hip_stream);
 
 /* Combine: y[t] = y_shared[t] + sum_j topk_w[t,j] * y_sorted[pair_slot[t*k+j]],
  * accumulated in fp32 in the order shared, j = 0..k-1 (deterministic).
- *   y_shared may be NULL (treated as 0); y [T, H] act_dtype out. */
-int moe_combine(const moe_cfg* cfg, const float* y_sorted, const float* y_shared,
+ *   y_sorted [T*k, H] and y_shared [T, H] (may be NULL: treated as 0) in
+ *   act_dtype; y [T, H] act_dtype out. */
+int moe_combine(const moe_cfg* cfg, const void* y_sorted, const void* y_shared,
                 const int32_t* pair_slot, const float* topk_w, void* y, void* hip_stream);
 
 /* The whole layer: route -> dispatch -> expert FFN -> combine, on one stream.

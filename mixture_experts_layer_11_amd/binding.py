@@ -213,8 +213,8 @@ def moe_quantize_fp8(inp: torch.Tensor, block: int = 128, stream=None):
 def moe_expert_ffn(cfg: MoeCfg, x, offsets, sorted_pair, weights: Weights, ws=None, stream=None):
     lib = load_library()
     dev = x.device
-    y_sorted = _out((cfg.T * cfg.k, cfg.H), torch.float32, dev)
-    y_shared = _out((cfg.T, cfg.H), torch.float32, dev) if cfg.I_shared > 0 else None
+    y_sorted = _out((cfg.T * cfg.k, cfg.H), _act_torch(cfg), dev)
+    y_shared = _out((cfg.T, cfg.H), _act_torch(cfg), dev) if cfg.I_shared > 0 else None
     ws = ws if ws is not None else alloc_workspace(cfg, dev)
     w = weights.c_struct()
     _check(lib.moe_expert_ffn(ctypes.byref(cfg), _ptr(x), _ptr(offsets), _ptr(sorted_pair), ctypes.byref(w),

@@ -3,17 +3,29 @@
 // multi-node DeepSeek deployment", section "Expert parallelism").
 //
 // y[t] = y_shared[t] + sum_j w[t,j] * y_sorted[pair_slot[t*k + j]], fp32
-// accumulation in the fixed order shared, j = 0..k-1.  One workgroup per
-// token; each thread owns 4 consecutive hidden columns (16-byte loads).
+// accumulation in the fixed order shared, j = 0..k-1.  Inputs and output are
+// in the activation dtype.  One workgroup per token; each thread owns 4
+// consecutive hidden columns.
 
 #include "moe_common.h"
 #include "moe_launch.h"
 
 namespace {
 
+template <int DT>
+__device__ __forceinline__ f32x4 load4(const void* base, size_t idx) {
+  if constexpr (DT == MOE_BF16) {
+    const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
+    return f32x4{bf16_to_f32((uint16_t)v.x), bf16_to_f32((uint16_t)(v.x >> 16)), bf16_to_f32((uint16_t)v.y),
+                 bf16_to_f32((uint16_t)(v.y >> 16))};
+  } else {
+    return *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + idx);
+  }
+}
+
 template <int OUT_DT>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_sorted,
-                                                      const float* __restrict__ y_shared,
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y_sorted,
+                                                      const void* __restrict__ y_shared,
                                                       const int32_t* __restrict__ pair_slot,
                                                       const float* __restrict__ topk_w, int H, int k,
                                                       void* __restrict__ y) {
@@ -27,9 +39,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   __syncthreads();
   for (int c = threadIdx.x * 4; c < H; c += blockDim.x * 4) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (y_shared) acc = *reinterpret_cast<const f32x4*>(y_shared + (size_t)t * H + c);
+    if (y_shared) acc = load4<OUT_DT>(y_shared, (size_t)t * H + c);
     for (int j = 0; j < k; ++j) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(y_sorted + (size_t)slot[j] * H + c);
+      const f32x4 v = load4<OUT_DT>(y_sorted, (size_t)slot[j] * H + c);
       const float w = wt[j];
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, v[i], acc[i]);
@@ -49,7 +61,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 namespace moe {
 
-hipError_t launch_combine(const moe_cfg& c, const float* y_sorted, const float* y_shared,
+hipError_t launch_combine(const moe_cfg& c, const void* y_sorted, const void* y_shared,
                           const int32_t* pair_slot, const float* topk_w, void* y, hipStream_t st) {
   if (c.act_dtype == MOE_BF16)
     MOE_LAUNCH("combine", combine_kernel<MOE_BF16>, dim3(c.T), dim3(256), 0, st, y_sorted, y_shared, pair_slot, topk_w,

@@ -60,8 +60,8 @@ struct Args {
   uint8_t* h;                   // GEMM1 out [P+T, I]
   const uint8_t* a2;            // GEMM2 A rows: h or fp8 codes of h, [P+T, I]
   const float* a2s;             // fp8: h scales [P+T, I/qb]
-  float* y_sorted;
-  float* y_shared;
+  uint8_t* y_sorted;            // act dtype (fp32 when DT is fp32, else bf16)
+  uint8_t* y_shared;
   const int32_t* plan;          // see ffn_plan_kernel: list sizes, 3 skinny lists of G, fat (group,row0) pairs
   int G;
 };
@@ -102,6 +102,16 @@ __device__ __forceinline__ void store_h(uint8_t* h, size_t idx, float v) {
     reinterpret_cast<uint16_t*>(h)[idx] = f32_to_bf16(v);
   else
     reinterpret_cast<float*>(h)[idx] = v;
+}
+
+// Expert outputs are stored in the activation dtype: fp32 for the fp32 layer,
+// bf16 for bf16 and fp8 weights.
+template <int DT>
+__device__ __forceinline__ void store_y(uint8_t* y, size_t idx, float v) {
+  if constexpr (DT == MOE_F32)
+    reinterpret_cast<float*>(y)[idx] = v;
+  else
+    reinterpret_cast<uint16_t*>(y)[idx] = f32_to_bf16(v);
 }
 
 // ------------------------------------------------------------------ plan
@@ -357,9 +367,10 @@ __device__ __forceinline__ void skinny_pass(const Args& a, const Group& gr, int 
           store_h<DT>(a.h, hrow + it * cols_per_item + 8 * (p * (NTP / 2) + j) + r8, silu(gv) * uv);
         }
       } else {
-        float* yrow = gr.routed ? a.y_sorted + (size_t)(gr.slot0 + r) * a.H : a.y_shared + (size_t)r * a.H;
+        uint8_t* ybase = gr.routed ? a.y_sorted : a.y_shared;
+        const size_t yrow = (size_t)(gr.routed ? gr.slot0 + r : r) * a.H;
 #pragma unroll
-        for (int j = 0; j < NTP; ++j) yrow[it * cols_per_item + 8 * (p * NTP + j) + r8] = acc[mt][j][i];
+        for (int j = 0; j < NTP; ++j) store_y<DT>(ybase, yrow + it * cols_per_item + 8 * (p * NTP + j) + r8, acc[mt][j][i]);
       }
     }
   }
@@ -658,12 +669,12 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
           if (col < a.I) store_h<DT>(a.h, hrow + col, silu(gv) * uv);
         }
       } else {
-        float* yrow = gr.routed ? a.y_sorted + (size_t)(gr.slot0 + row0 + r) * a.H
-                                : a.y_shared + (size_t)(row0 + r) * a.H;
+        uint8_t* ybase = gr.routed ? a.y_sorted : a.y_shared;
+        const size_t yrow = (size_t)(gr.routed ? gr.slot0 + row0 + r : row0 + r) * a.H;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int col = nt * kTN + wn * 128 + j * 16 + row;
-          if (col < a.H) yrow[col] = acc[i][j][q];
+          if (col < a.H) store_y<DT>(ybase, yrow + col, acc[i][j][q]);
         }
       }
     }
@@ -762,8 +773,8 @@ size_t ffn_plan_ints(const moe_cfg& c) {
 size_t ffn_h_elem_bytes(const moe_cfg& c) { return c.w_dtype == MOE_BF16 ? 2 : 4; }
 
 hipError_t launch_expert_ffn(const moe_cfg& c, const void* x, const int32_t* offsets,
-                             const int32_t* sorted_pair, const moe_weights& w, float* y_sorted,
-                             float* y_shared, const FfnWs& ws, hipStream_t st) {
+                             const int32_t* sorted_pair, const moe_weights& w, void* y_sorted,
+                             void* y_shared, const FfnWs& ws, hipStream_t st) {
   Args a{};
   a.T = c.T;
   a.H = c.H;
@@ -784,8 +795,8 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const void* x, const int32_t* off
   a.ws2 = static_cast<const uint8_t*>(w.ws2);
   a.ws2s = w.ws2_scale;
   a.h = static_cast<uint8_t*>(ws.h);
-  a.y_sorted = y_sorted;
-  a.y_shared = y_shared;
+  a.y_sorted = static_cast<uint8_t*>(y_sorted);
+  a.y_shared = static_cast<uint8_t*>(y_shared);
   a.plan = ws.plan;
   a.G = c.E + (a.has_shared ? 1 : 0);
   if (c.w_dtype == MOE_FP8_E4M3) {

@@ -104,8 +104,9 @@ Layout layout(const moe_cfg& c) {
   L.f_offsets = take((E + 1) * 4);
   L.f_sorted = take(P * 4);
   L.f_slot = take(P * 4);
-  L.f_ysorted = take(P * H * 4);
-  L.f_yshared = take(Ts * H * 4);
+  const size_t ab = c.act_dtype == MOE_F32 ? 4 : 2;
+  L.f_ysorted = take(P * H * ab);
+  L.f_yshared = take(Ts * H * ab);
   L.total = off;
   return L;
 }
@@ -239,7 +240,7 @@ int moe_quantize_fp8(int32_t rows, int32_t cols, int32_t block, const void* in, 
 }
 
 int moe_expert_ffn(const moe_cfg* cfg, const void* x, const int32_t* offsets, const int32_t* sorted_pair,
-                   const moe_weights* w, float* y_sorted, float* y_shared, void* ws, size_t ws_bytes,
+                   const moe_weights* w, void* y_sorted, void* y_shared, void* ws, size_t ws_bytes,
                    void* hip_stream) {
   int s = check_cfg(cfg);
   if (s) return s;
@@ -261,7 +262,7 @@ int moe_expert_ffn(const moe_cfg* cfg, const void* x, const int32_t* offsets, co
   return e == hipSuccess ? ok() : hip_fail(e, "moe_expert_ffn");
 }
 
-int moe_combine(const moe_cfg* cfg, const float* y_sorted, const float* y_shared, const int32_t* pair_slot,
+int moe_combine(const moe_cfg* cfg, const void* y_sorted, const void* y_shared, const int32_t* pair_slot,
                 const float* topk_w, void* y, void* hip_stream) {
   int s = check_cfg(cfg);
   if (s) return s;
@@ -299,8 +300,8 @@ int moe_forward(const moe_cfg* cfg, const void* x, const void* w_gate, const flo
   int32_t* offsets = at<int32_t>(ws, L.f_offsets);
   int32_t* sorted = at<int32_t>(ws, L.f_sorted);
   int32_t* slot = at<int32_t>(ws, L.f_slot);
-  float* ys = at<float>(ws, L.f_ysorted);
-  float* ysh = cfg->I_shared > 0 ? at<float>(ws, L.f_yshared) : nullptr;
+  void* ys = at<void>(ws, L.f_ysorted);
+  void* ysh = cfg->I_shared > 0 ? at<void>(ws, L.f_yshared) : nullptr;
   hipError_t e = moe::launch_route(*cfg, x, w_gate, sel_bias, idx, wt, at<float>(ws, L.route_part), st);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/route");
   e = moe::launch_dispatch(*cfg, idx, counts, offsets, sorted, slot, at<int32_t>(ws, L.seg), st);

@@ -57,11 +57,11 @@ struct FfnWs {
 size_t ffn_plan_ints(const moe_cfg& c);
 size_t ffn_h_elem_bytes(const moe_cfg& c);
 hipError_t launch_expert_ffn(const moe_cfg& c, const void* x, const int32_t* offsets,
-                             const int32_t* sorted_pair, const moe_weights& w, float* y_sorted,
-                             float* y_shared, const FfnWs& ws, hipStream_t st);
+                             const int32_t* sorted_pair, const moe_weights& w, void* y_sorted,
+                             void* y_shared, const FfnWs& ws, hipStream_t st);
 
 // ---- combine
-hipError_t launch_combine(const moe_cfg& c, const float* y_sorted, const float* y_shared,
+hipError_t launch_combine(const moe_cfg& c, const void* y_sorted, const void* y_shared,
                           const int32_t* pair_slot, const float* topk_w, void* y, hipStream_t st);
 
 }  // namespace moe

@@ -165,14 +165,16 @@ def test_combine_small(name):
     cfg = SMALL[name]
     inp, _ = _small_inputs(cfg)
     ref = oracle.forward(inp)
-    ys32 = ref["y_sorted"].astype(np.float32)
-    ysh32 = ref["y_shared"].astype(np.float32)
+    # the stage's inputs in the activation dtype, as moe_expert_ffn stores them
+    adt = torch.float32 if cfg.act_dtype == "f32" else torch.bfloat16
+    ys_in = torch.from_numpy(ref["y_sorted"]).to(adt)
+    ysh_in = torch.from_numpy(ref["y_shared"]).to(adt)
     w32 = ref["route"]["w"].astype(np.float32)
-    expect = oracle.combine(ys32.astype(np.float64), ysh32.astype(np.float64) if cfg.I_shared else np.zeros_like(ref["y_shared"]),
+    expect = oracle.combine(oracle.to_f64(ys_in), oracle.to_f64(ysh_in) if cfg.I_shared else np.zeros_like(ref["y_shared"]),
                             ref["dispatch"]["pair_slot"], w32.astype(np.float64), cfg.k)
     mc = moe.cfg_from(cfg)
-    y = moe.moe_combine(mc, torch.from_numpy(ys32).to(DEV),
-                        torch.from_numpy(ysh32).to(DEV) if cfg.I_shared else None,
+    y = moe.moe_combine(mc, ys_in.to(DEV),
+                        ysh_in.to(DEV) if cfg.I_shared else None,
                         torch.from_numpy(ref["dispatch"]["pair_slot"].astype(np.int32)).to(DEV),
                         torch.from_numpy(w32).to(DEV))
     torch.cuda.synchronize()
