@@ -599,6 +599,18 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
           for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 8; ++j) F::mma(acc[i][j], fa[fs][i], fb[fs][j]);
+        // Instruction order for the scheduler: the first half's 12 reads, then
+        // the second half's 12 reads interleaved 1:2 with the first half's
+        // MFMAs, then the rest, so LDS latency hides behind MFMAs.
+        if constexpr (DT == MOE_BF16) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+#pragma unroll
+          for (int q = 0; q < 12; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 40, 0);
+        }
       } else if (mval > 0) {
 #pragma unroll
         for (int fs = 0; fs < SL / 64; ++fs) {
