@@ -54,11 +54,11 @@ def kernel_models(cfg, counts):
     sc2 = (H * I // qb) * 4 if fp8 else 0
     groups = [int(c) for c in counts]
     m = {f"ffn_gemm{g}_{r}": {"bytes": 0, "flops": 0} for g in (1, 2)
-         for r in ("skinny_m8", "skinny_m16", "skinny_m32", "tiled", "shared_skinny")}
+         for r in ("skinny_m8", "skinny_m16", "skinny_m32", "tiled", "shared_skinny", "shared_tiled")}
     items = [(mg, ("skinny_m8" if mg <= 8 else "skinny_m16" if mg <= 16 else "skinny_m32")
               if mg <= SKINNY_ROWS else "tiled") for mg in groups]
     if cfg.I_shared:
-        items.append((T, "shared_skinny" if T <= SKINNY_ROWS else "tiled"))
+        items.append((T, "shared_skinny" if T <= SKINNY_ROWS else "shared_tiled"))
     for mg, reg in items:
         if mg == 0:
             continue

@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["moe_api.cpp", "profile.cpp", "route.hip", "dispatch.hip", "quant.hip", "ffn.hip", "combine.hip"]
+SOURCES = ["moe_api.cpp", "profile.cpp", "streams.cpp", "route.hip", "dispatch.hip", "quant.hip", "ffn.hip", "combine.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -57,7 +57,7 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=min(6, os.cpu_count() or 1))
     ap.add_argument("--verbose", action="store_true")
-    ap.add_argument("-D", dest="defines", action="append", default=[], help="extra macro, e.g. -D MOE_SK_U=4")
+    ap.add_argument("-D", dest="defines", action="append", default=[], help="extra macro, e.g. -D NAME=VALUE")
     ap.add_argument("--out", default=LIB)
     ap.add_argument("--build-dir", default=BUILD)
     args = ap.parse_args(argv)

@@ -64,6 +64,7 @@ struct Args {
   uint8_t* y_shared;
   const int32_t* plan;          // see ffn_plan_kernel: list sizes, 3 skinny lists of G, fat (group,row0) pairs
   int G;
+  int shared_only;              // tiled launch over the shared expert's row tiles instead of the plan's fat list
 };
 
 struct Group {
@@ -126,7 +127,8 @@ __global__ __launch_bounds__(512) void ffn_plan_kernel(Args a) {
   // expert has a launch of its own and is in no list)
   const bool shared = g == a.E;
   const int cls = (m > 0 && m <= kSkinnyRows && !shared) ? (m <= 8 ? 0 : m <= 16 ? 1 : 2) : -1;
-  const int tiles = m > kSkinnyRows ? (m + kTileRows - 1) / kTileRows : 0;
+  // the shared expert is never in the lists: it has launches of its own
+  const int tiles = m > kSkinnyRows && !shared ? (m + kTileRows - 1) / kTileRows : 0;
 #pragma unroll
   for (int c = 0; c < 3; ++c) sk[c][g] = cls == c ? 1 : 0;
   ft[g] = tiles;
@@ -171,14 +173,7 @@ __global__ __launch_bounds__(512) void ffn_plan_kernel(Args a) {
 // L and L ^ 40.  Half of each MFMA is wasted, which costs nothing in this
 // bandwidth-bound regime, and every load instruction reads whole cache lines.
 
-#ifndef MOE_SK_NT
-#define MOE_SK_NT 8
-#endif
-#ifndef MOE_SK_U
-#define MOE_SK_U 1
-#endif
-constexpr int kSkNT = MOE_SK_NT;  // 8-row weight tiles per wave (even: gate/up halves in GEMM1)
-constexpr int kSkU = MOE_SK_U;    // 128-byte K windows per loop trip
+constexpr int kSkNT = 8;  // 8-row weight tiles per routed skinny item (even: gate/up halves in GEMM1)
 
 // Weights are read exactly once: nontemporal loads keep them from displacing
 // the reused activation rows in the caches.
@@ -188,7 +183,7 @@ __device__ __forceinline__ i32x4 ldw16(const uint8_t* p) {
 
 __device__ __forceinline__ int sk_chunk(int lane) { return 4 * ((lane >> 3) & 1) + (lane >> 4); }
 
-// One pass over the full K for NTP of the wave's kSkNT weight tiles (pass p),
+// One pass over the full K for NTP of the wave's NT weight tiles (pass p),
 // against MT M tiles of 8 tokens (MT * 8 >= group rows).  Rows beyond the
 // group's count are clamped to its last row: their results are never stored,
 // so the K loop carries no per-lane predicates or branches.  U windows per
@@ -264,6 +259,10 @@ __device__ __forceinline__ void skinny_pass(const Args& a, const Group& gr, int 
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) av[u][mt] = ld16(pa[mt] + off);
       }
+      // Keep every load of the trip ahead of its MFMAs: left alone, the
+      // scheduler interleaves them to shorten live ranges and waits on each
+      // load in turn, which leaves few bytes in flight per wave.
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -295,31 +294,43 @@ __device__ __forceinline__ void skinny_pass(const Args& a, const Group& gr, int 
         const int r = min(mt * 8 + ((4 * (lane >> 4) + i) & 7), gr.m - 1);
         sa_row[mt][i] = (MODE == 1 ? gemm1_src_row(a, gr, r) : gr.slot0 + r) * nwin;
       }
-    for (int w = w_begin; w < w_end; ++w) {
-      const size_t off = (size_t)w * 128;
-      i32x4 b[NTP], av[MT];
+    // U windows per trip: all loads of the trip are issued before its MFMAs.
+    constexpr int UF = MT >= 4 ? (U < 2 ? U : 2) : U;
+    int w = w_begin;
+    for (; w < w_end; w += UF) {
+      i32x4 b[UF][NTP], av[UF][MT];
+      float sw[UF][NTP], sa[UF][MT][4];
 #pragma unroll
-      for (int j = 0; j < NTP; ++j) b[j] = ldw16(pb[j] + off);
+      for (int u = 0; u < UF; ++u) {
+        const int wu = min(w + u, w_end - 1);   // a short last trip recomputes its last window, not added
+        const size_t off = (size_t)wu * 128;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) av[mt] = ld16(pa[mt] + off);
-      float sw[NTP], sa[MT][4];
+        for (int j = 0; j < NTP; ++j) b[u][j] = ldw16(pb[j] + off);
 #pragma unroll
-      for (int j = 0; j < NTP; ++j) sw[j] = wsbase[(size_t)wrow[j] * nwin + w];
+        for (int mt = 0; mt < MT; ++mt) av[u][mt] = ld16(pa[mt] + off);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int j = 0; j < NTP; ++j) sw[u][j] = wsbase[(size_t)wrow[j] * nwin + wu];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sa[mt][i] = sbase[(size_t)sa_row[mt][i] + w];
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+          for (int i = 0; i < 4; ++i) sa[u][mt][i] = sbase[(size_t)sa_row[mt][i] + wu];
+      }
+      __builtin_amdgcn_sched_barrier(0);   // all loads of the trip before its MFMAs
 #pragma unroll
-        for (int j = 0; j < NTP; ++j) {
-          f32x4 pr = {0.f, 0.f, 0.f, 0.f};
-          // a 16-byte chunk is 16 fp8 values: two 16x16x32 MFMAs (8 bytes per lane each)
-          pr = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(((const long*)&av[mt])[0], ((const long*)&b[j])[0], pr, 0, 0, 0);
-          pr = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(((const long*)&av[mt])[1], ((const long*)&b[j])[1], pr, 0, 0, 0);
+      for (int u = 0; u < UF; ++u) {
+        if (u > 0 && w + u >= w_end) break;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mt][j][i] = fmaf(pr[i], sa[mt][i] * sw[j], acc[mt][j][i]);
-        }
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int j = 0; j < NTP; ++j) {
+            f32x4 pr = {0.f, 0.f, 0.f, 0.f};
+            // a 16-byte chunk is 16 fp8 values: two 16x16x32 MFMAs (8 bytes per lane each)
+            pr = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(((const long*)&av[u][mt])[0], ((const long*)&b[u][j])[0], pr, 0, 0, 0);
+            pr = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(((const long*)&av[u][mt])[1], ((const long*)&b[u][j])[1], pr, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mt][j][i] = fmaf(pr[i], sa[u][mt][i] * sw[u][j], acc[mt][j][i]);
+          }
+      }
     }
   }
 
@@ -387,21 +398,35 @@ __device__ __forceinline__ void skinny_tile(const Args& a, const Group& gr, int 
 }
 
 // Routed skinny groups of class CLS (MT = 1, 2, 4 M tiles of 8 tokens).
-// One wave = one work item (group, column block of kSkNT tiles); waves past
-// the class's list exit at once.
+// One wave = one work item (group, column block of kSkNT weight tiles) in a
+// single pass over K; waves past the class's list exit at once.  Every class
+// uses the same wide items: each activation fragment then serves 8 weight
+// tiles, which keeps the activation re-reads (one per item) a small share of
+// the load instructions even at 32 rows.
 template <int DT, int MODE, int CLS>
 __global__ __launch_bounds__(256) void ffn_skinny_kernel(Args a) {
+  constexpr int MT = 1 << CLS;
   constexpr int NT = kSkNT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cols_per_item = MODE == 1 ? 4 * NT : 8 * NT;
   const int items = (MODE == 1 ? a.I : a.H) / cols_per_item;
-  const int item = blockIdx.x * 4 + wave;
+  // XCD-aware order: workgroups go to the 8 XCDs round-robin (blockIdx % 8),
+  // so XCD x takes the contiguous range x * per_xcd ... of the class's real
+  // work.  The items of a group then run on one or two XCDs and its
+  // activation rows, re-read by every item, stay in that XCD's L2 instead of
+  // being fetched into all eight.  The grid is a multiple of 8 and at least
+  // 8 * per_xcd workgroups.
+  const int real_wg = (a.plan[CLS] * items + 3) >> 2;
+  const int per_xcd = (real_wg + 7) >> 3;
+  const int local = blockIdx.x >> 3;
+  if (local >= per_xcd) return;
+  const int item = ((blockIdx.x & 7) * per_xcd + local) * 4 + wave;
   const int gi = item / items;
   if (gi >= a.plan[CLS]) return;
   const int g = a.plan[kPlanHead + CLS * a.G + gi];
   const int it = item - gi * items;
   const Group gr = group_of(a, g);
-  skinny_tile<DT, MODE, 1 << CLS, NT, 1>(a, gr, g, it, lane, 0, nullptr);
+  skinny_pass<DT, MODE, MT, NT, NT, 1, 1>(a, gr, g, it, 0, lane, 0, nullptr);
 }
 
 // The shared expert when T <= kSkinnyRows: its row count is known on the
@@ -492,10 +517,16 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
   const int wm = wave >> 1, wn = wave & 1;
   const int tile = blockIdx.x / ntn;
   const int nt = blockIdx.x - tile * ntn;
-  if (tile >= a.plan[3]) return;
-  const int32_t* fat = a.plan + kPlanHead + 3 * a.G;
-  const int g = fat[2 * tile];
-  const int row0 = fat[2 * tile + 1];
+  int g, row0;
+  if (a.shared_only) {              // the grid covers exactly ceil(T / kTM) row tiles of the shared expert
+    g = a.E;
+    row0 = tile * kTM;
+  } else {
+    if (tile >= a.plan[3]) return;
+    const int32_t* fat = a.plan + kPlanHead + 3 * a.G;
+    g = fat[2 * tile];
+    row0 = fat[2 * tile + 1];
+  }
   const Group gr = group_of(a, g);
   const int rows = min(kTM, gr.m - row0);
   const int K = MODE == 1 ? a.H : a.I;
@@ -709,43 +740,21 @@ hipError_t launch_fat(const char* name, int grid, int ntn, const Args& a, hipStr
   return hipGetLastError();
 }
 
+// The shared expert: its own launches, on the stream it is given.
 template <int DT>
-hipError_t run_ffn(const moe_cfg& c, Args a, hipStream_t st) {
-  const int G = a.G;
-  MOE_LAUNCH("ffn_plan", ffn_plan_kernel, dim3(1), dim3(512), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+hipError_t run_shared(const moe_cfg& c, Args a, hipStream_t st) {
+  a.shared_only = 1;
   const int P = a.P;
-  const int max_fat = moe::ceil_div(P, kTileRows) + (P / (kSkinnyRows + 1) < c.E ? P / (kSkinnyRows + 1) : c.E) +
-                      (a.has_shared ? moe::ceil_div(c.T, kTileRows) : 0);
+  hipError_t e;
   for (int mode = 1; mode <= 2; ++mode) {
-    if (mode == 2 && DT == MOE_FP8_E4M3) {
-      e = moe::launch_quant_fp8(P + (a.has_shared ? c.T : 0), c.I, a.qb, a.h, MOE_F32,
-                                const_cast<uint8_t*>(a.a2), const_cast<float*>(a.a2s), st);
+    if (mode == 2 && DT == MOE_FP8_E4M3) {   // its rows [P, P + T) of h
+      e = moe::launch_quant_fp8(c.T, c.I, a.qb, a.h + (size_t)P * c.I * 4, MOE_F32,
+                                const_cast<uint8_t*>(a.a2) + (size_t)P * c.I,
+                                const_cast<float*>(a.a2s) + (size_t)P * (c.I / a.qb), st);
       if (e != hipSuccess) return e;
     }
     const int N = mode == 1 ? c.I : c.H;
-    const int sk_items = N / (mode == 1 ? 4 * kSkNT : 8 * kSkNT);
-    // upper bounds of the three skinny lists: a group of class c has > 8 * 2^(c-1) rows
-    int sk_groups[3];
-    for (int cls = 0; cls < 3; ++cls) {
-      const int min_rows = cls == 0 ? 1 : (4 << cls) + 1;   // 1, 9, 17
-      const int bound = P / min_rows;
-      sk_groups[cls] = bound < G ? bound : G;
-    }
-    const int ntn = mode == 1 ? moe::ceil_div(c.I, kTN / 2) : moe::ceil_div(c.H, kTN);
-    const int fat_grid = max_fat * ntn;
-    static const char* const kSkName[2][3] = {
-        {"ffn_gemm1_skinny_m8", "ffn_gemm1_skinny_m16", "ffn_gemm1_skinny_m32"},
-        {"ffn_gemm2_skinny_m8", "ffn_gemm2_skinny_m16", "ffn_gemm2_skinny_m32"}};
-    const char* fatn = mode == 1 ? "ffn_gemm1_tiled" : "ffn_gemm2_tiled";
-#define MOE_SK_LAUNCH(M, CLS)                                                                   \
-    if (sk_groups[CLS] > 0) {                                                                   \
-      MOE_LAUNCH(kSkName[M - 1][CLS], (ffn_skinny_kernel<DT, M, CLS>), dim3(moe::ceil_div((long long)sk_groups[CLS] * sk_items, 4)), \
-                 dim3(256), 0, st, a);                                                          \
-      if ((e = hipGetLastError()) != hipSuccess) return e;                                     \
-    }
-    if (a.has_shared && c.T <= kSkinnyRows) {
+    if (c.T <= kSkinnyRows) {
       const int sh_items = N / (mode == 1 ? 4 * kShNT : 8 * kShNT);
       const char* shn = mode == 1 ? "ffn_gemm1_shared_skinny" : "ffn_gemm2_shared_skinny";
 #define MOE_SH_LAUNCH(M, MT) \
@@ -757,6 +766,57 @@ hipError_t run_ffn(const moe_cfg& c, Args a, hipStream_t st) {
       }
 #undef MOE_SH_LAUNCH
       if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+      const int ntn = mode == 1 ? moe::ceil_div(c.I, kTN / 2) : moe::ceil_div(c.H, kTN);
+      const int grid = moe::ceil_div(c.T, kTM) * ntn;
+      e = mode == 1 ? launch_fat<DT, 1>("ffn_gemm1_shared_tiled", grid, ntn, a, st)
+                    : launch_fat<DT, 2>("ffn_gemm2_shared_tiled", grid, ntn, a, st);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+// The routed experts, on the stream it is given: plan, then per projection
+// the three skinny classes and the tiled groups.
+template <int DT>
+hipError_t run_routed(const moe_cfg& c, Args a, hipStream_t st) {
+  a.shared_only = 0;
+  const int G = a.G;
+  MOE_LAUNCH("ffn_plan", ffn_plan_kernel, dim3(1), dim3(512), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int P = a.P;
+  // Upper bound of the fat tiles: a token picks k distinct experts, so a
+  // routed group has at most T rows and none is fat when T <= kSkinnyRows.
+  // Otherwise at most ceil(P / kTileRows) full tiles plus one partial tile per
+  // fat group, and at most min(E, P / (kSkinnyRows + 1)) fat groups.
+  const int fat_groups = c.T > kSkinnyRows ? (P / (kSkinnyRows + 1) < c.E ? P / (kSkinnyRows + 1) : c.E) : 0;
+  const int max_fat = fat_groups > 0 ? moe::ceil_div(P, kTileRows) + fat_groups : 0;
+  for (int mode = 1; mode <= 2; ++mode) {
+    if (mode == 2 && DT == MOE_FP8_E4M3) {
+      e = moe::launch_quant_fp8(P, c.I, a.qb, a.h, MOE_F32, const_cast<uint8_t*>(a.a2), const_cast<float*>(a.a2s), st);
+      if (e != hipSuccess) return e;
+    }
+    const int N = mode == 1 ? c.I : c.H;
+    // upper bounds of the three skinny lists: a group of class c has > 8 * 2^(c-1) rows
+    int sk_groups[3];
+    for (int cls = 0; cls < 3; ++cls) {
+      const int min_rows = cls == 0 ? 1 : (4 << cls) + 1;   // 1, 9, 17
+      const int bound = P / min_rows;
+      sk_groups[cls] = bound < c.E ? bound : c.E;
+    }
+    const int ntn = mode == 1 ? moe::ceil_div(c.I, kTN / 2) : moe::ceil_div(c.H, kTN);
+    const int fat_grid = max_fat * ntn;
+    static const char* const kSkName[2][3] = {
+        {"ffn_gemm1_skinny_m8", "ffn_gemm1_skinny_m16", "ffn_gemm1_skinny_m32"},
+        {"ffn_gemm2_skinny_m8", "ffn_gemm2_skinny_m16", "ffn_gemm2_skinny_m32"}};
+    const char* fatn = mode == 1 ? "ffn_gemm1_tiled" : "ffn_gemm2_tiled";
+#define MOE_SK_LAUNCH(M, CLS)                                                                   \
+    if (sk_groups[CLS] > 0) {                                                                   \
+      MOE_LAUNCH(kSkName[M - 1][CLS], (ffn_skinny_kernel<DT, M, CLS>), dim3((moe::ceil_div((long long)sk_groups[CLS] * (N / ((M == 1 ? 4 : 8) * kSkNT)), 4) + 7) & ~7LL), \
+                 dim3(256), 0, st, a);                                                          \
+      if ((e = hipGetLastError()) != hipSuccess) return e;                                     \
     }
     if (mode == 1) {
       MOE_SK_LAUNCH(1, 0) MOE_SK_LAUNCH(1, 1) MOE_SK_LAUNCH(1, 2)
@@ -769,6 +829,35 @@ hipError_t run_ffn(const moe_cfg& c, Args a, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+// A tiled shared expert (T > kSkinnyRows) runs on a side stream forked from
+// st (an event records st's position, the side stream waits on it) and
+// joined back at the end (st waits on an event recorded after the shared
+// launches), so it overlaps the routed experts: at a few hundred tokens its
+// GEMMs have too few tiles to fill the device on their own.  It is enqueued
+// first so that its large workgroups find free CUs before the routed kernels
+// fill the device.  Both halves write disjoint rows of h and separate
+// outputs.  A skinny shared expert stays on st: it streams weights like the
+// routed skinny kernels, and running it beside them only adds contention.
+template <int DT>
+hipError_t run_ffn(const moe_cfg& c, const Args& a, hipStream_t st) {
+  if (!a.has_shared) return run_routed<DT>(c, a, st);
+  if (c.T <= kSkinnyRows) {
+    hipError_t e = run_shared<DT>(c, a, st);
+    return e != hipSuccess ? e : run_routed<DT>(c, a, st);
+  }
+  moe::SideStream side;
+  hipError_t e = moe::side_stream(&side);
+  if (e != hipSuccess) return e;
+  if ((e = hipEventRecord(side.fork, st)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(side.stream, side.fork, 0)) != hipSuccess) return e;
+  hipError_t es = run_shared<DT>(c, a, side.stream);
+  hipError_t er = es == hipSuccess ? run_routed<DT>(c, a, st) : hipSuccess;
+  // join even after a failed launch, so that work queued later on st never
+  // runs ahead of work already queued on the side stream
+  if ((e = hipEventRecord(side.join, side.stream)) == hipSuccess) e = hipStreamWaitEvent(st, side.join, 0);
+  return es != hipSuccess ? es : er != hipSuccess ? er : e;
 }
 
 }  // namespace

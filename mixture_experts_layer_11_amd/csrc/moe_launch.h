@@ -60,6 +60,14 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const void* x, const int32_t* off
                              const int32_t* sorted_pair, const moe_weights& w, void* y_sorted,
                              void* y_shared, const FfnWs& ws, hipStream_t st);
 
+// ---- side stream (streams.cpp): forked from and joined back to the caller's stream
+struct SideStream {
+  hipStream_t stream;
+  hipEvent_t fork;
+  hipEvent_t join;
+};
+hipError_t side_stream(SideStream* out);
+
 // ---- combine
 hipError_t launch_combine(const moe_cfg& c, const void* y_sorted, const void* y_shared,
                           const int32_t* pair_slot, const float* topk_w, void* y, hipStream_t st);

@@ -1,0 +1,35 @@
+// Side stream for work that overlaps the caller's stream.
+//
+// One non-blocking stream (default priority) and two timing-free events per
+// host thread and device, created on first use and kept until the process
+// ends.  Each call forks from the caller's stream with `fork` and joins back
+// with `join`, so the caller's stream keeps the library's ordering contract:
+// everything a call enqueues runs after earlier work on that stream and before
+// later work on it.  Per-thread resources keep calls from different host
+// threads from sharing the events.
+
+#include <vector>
+
+#include "moe_launch.h"
+
+namespace moe {
+
+hipError_t side_stream(SideStream* out) {
+  thread_local std::vector<SideStream> per_device;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if ((int)per_device.size() <= dev) per_device.resize(dev + 1);
+  SideStream& s = per_device[dev];
+  if (!s.stream) {
+    SideStream n{};
+    if ((e = hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming)) != hipSuccess) return e;
+    s = n;
+  }
+  *out = s;
+  return hipSuccess;
+}
+
+}  // namespace moe

@@ -29,6 +29,7 @@ ROOT = os.path.dirname(PKG)
 KERNEL_SOURCES = {
     **{f"ffn_gemm{g}_skinny_m{m}": "ffn.hip" for g in (1, 2) for m in (8, 16, 32)},
     "ffn_gemm1_shared_skinny": "ffn.hip", "ffn_gemm2_shared_skinny": "ffn.hip",
+    "ffn_gemm1_shared_tiled": "ffn.hip", "ffn_gemm2_shared_tiled": "ffn.hip",
     "ffn_gemm1_tiled": "ffn.hip", "ffn_gemm2_tiled": "ffn.hip", "ffn_plan": "ffn.hip",
     "route_gate_fused": "route.hip", "route_gate_split": "route.hip", "route_reduce_select": "route.hip",
     "dispatch_count": "dispatch.hip", "dispatch_scan": "dispatch.hip", "dispatch_scatter": "dispatch.hip",

@@ -214,6 +214,30 @@ def test_forward_is_deterministic():
             assert torch.equal(a, b)
 
 
+def test_forward_on_user_stream_is_ordered():
+    """The call forks the shared expert (T > 32) onto a side stream and joins
+    it back: work queued after it on the caller's stream sees the whole
+    output, without a device-wide synchronisation in between."""
+    cfg = SMALL["small_bf16"]
+    inp, gin = _small_inputs(cfg)
+    ref = oracle.forward(inp)
+    mc = moe.cfg_from(cfg)
+    ws = moe.alloc_workspace(mc)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        copies = []
+        for _ in range(2):
+            out = moe.moe_forward(mc, gin.x, gin.wg, gin.bias, moe.Weights.from_inputs(gin), ws=ws,
+                                  return_routing=True)
+            copies.append([t.clone() for t in out])      # queued on s right after the call
+    s.synchronize()
+    for y, idx, w, _ in copies:
+        _, mism = compare_routing(idx, w, ref["route"], cfg.k)
+        keep = np.setdiff1d(np.arange(cfg.T), mism)
+        assert_outputs_close(to_np(y)[keep], ref["y"][keep], tol_key(cfg), "y")
+
+
 def test_zero_input_gives_zero_output():
     cfg = SMALL["small_bf16"]
     _, gin = _small_inputs(cfg)
