@@ -11,7 +11,9 @@ resident in HBM.  Prints ONE JSON line:
              bytes (or FLOPs) per launch, from the step's real per-expert
              counts, divided by the kernel's mean launch time measured with
              HIP events on its own stream during the timed steps; the peak is
-             MI355X's published HBM3E bandwidth (8 TB/s) or dense MFMA rate.
+             MI355X's published HBM3E bandwidth (8 TB/s) when the kernel's
+             FLOPs per byte lie below the ridge point, else its dense MFMA
+             rate for the weight dtype.
              `traffic` is the measured HBM bytes per launch from rocprofv3
              counters (profiles/traffic_<kernel>_<workload>.json) when those
              were taken on the current kernel source, else null.
@@ -199,15 +201,19 @@ def main(argv=None):
     wdt = "fp8" if cfg.w_dtype == "fp8" else cfg.act_dtype
     if dom in models:
         mm = models[dom]
-        if "skinny" in dom:
+        # the kernel's own roofline: HBM-bound below the ridge point
+        # (peak FLOP/s / peak bytes/s), MFMA-bound above it
+        peak = MFMA_PEAK_TFLOPS[wdt]
+        ridge = peak * 1e12 / (HBM_PEAK_GBPS * 1e9)
+        tflops = mm["flops"] / (avg_ms * 1e-3) / 1e12
+        if mm["flops"] < ridge * mm["bytes"]:
             achieved = mm["bytes"] / (avg_ms * 1e-3) / 1e9
             roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBPS, 4)}
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "mfma_frac": round(tflops / peak, 4)}   # the MFMA rate beside it, for reference
         else:
-            achieved = mm["flops"] / (avg_ms * 1e-3) / 1e12
-            peak = MFMA_PEAK_TFLOPS[wdt]
-            roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(achieved / peak, 4)}
+            roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(tflops / peak, 4)}
         roof["traffic"] = traffic_for(dom, cfg.name)
     else:
         roof = {"bound": "hbm", "achieved": None, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": None,

@@ -13,7 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["moe_api.cpp", "profile.cpp", "streams.cpp", "route.hip", "dispatch.hip", "quant.hip", "ffn.hip", "combine.hip"]
+SOURCES = ["moe_api.cpp", "profile.cpp", "streams.cpp", "route.hip", "dispatch.hip", "quant.hip", "ffn.hip",
+           "ffn_skinny.hip", "ffn_tiled.hip", "combine.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

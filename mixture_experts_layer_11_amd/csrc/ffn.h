@@ -1,0 +1,110 @@
+// Expert FFN internals shared by the planner and launcher (ffn.hip), the
+// streaming "skinny" kernels (ffn_skinny.hip) and the tiled kernels
+// (ffn_tiled.hip): the kernel argument block, group bookkeeping, output
+// stores, the regime and tile constants and the per-file launchers.
+#pragma once
+
+#include "moe_common.h"
+#include "moe_launch.h"
+
+namespace moe {
+namespace ffn {
+
+constexpr int kSkinnyRows = 32;  // groups with <= this many rows take the skinny path
+constexpr int kTileRows = 256;   // rows per tile of the tiled grouped GEMM
+constexpr int kPlanHead = 4;     // plan: [0..2] skinny list sizes (<=8, <=16, <=32 rows), [3] fat tiles
+
+struct Args {
+  int T, H, E, k, I, P;
+  int has_shared;
+  int qb;                       // fp8 block (128)
+  const uint8_t* a1;            // GEMM1 A rows: x or fp8 codes of x, [T, H]
+  const float* a1s;             // fp8: x scales [T, H/qb]
+  const int32_t* offsets;
+  const int32_t* sorted_pair;
+  const uint8_t* w13;
+  const float* w13s;
+  const uint8_t* ws13;
+  const float* ws13s;
+  const uint8_t* w2;
+  const float* w2s;
+  const uint8_t* ws2;
+  const float* ws2s;
+  uint8_t* h;                   // GEMM1 out [P+T, I]
+  const uint8_t* a2;            // GEMM2 A rows: h or fp8 codes of h, [P+T, I]
+  const float* a2s;             // fp8: h scales [P+T, I/qb]
+  uint8_t* y_sorted;            // act dtype (fp32 when DT is fp32, else bf16)
+  uint8_t* y_shared;
+  const int32_t* plan;          // see ffn_plan_kernel: list sizes, 3 skinny lists of G, fat (group,row0) pairs
+  int G;
+};
+
+struct Group {
+  int m;         // rows
+  int slot0;     // first row in the [P+T] row space of h (routed: offsets[g]; shared: P)
+  bool routed;
+};
+
+__device__ __forceinline__ Group group_of(const Args& a, int g) {
+  Group r;
+  if (g < a.E) {
+    r.slot0 = a.offsets[g];
+    r.m = a.offsets[g + 1] - r.slot0;
+    r.routed = true;
+  } else {
+    r.slot0 = a.P;
+    r.m = a.T;
+    r.routed = false;
+  }
+  return r;
+}
+
+// Token (row of x) feeding row r of group g in GEMM1.
+__device__ __forceinline__ int gemm1_src_row(const Args& a, const Group& gr, int r) {
+  return gr.routed ? a.sorted_pair[gr.slot0 + r] / a.k : r;
+}
+
+template <int DT> struct HOut;  // element type of h
+template <> struct HOut<MOE_F32> { static constexpr int ESZ = 4; };
+template <> struct HOut<MOE_BF16> { static constexpr int ESZ = 2; };
+template <> struct HOut<MOE_FP8_E4M3> { static constexpr int ESZ = 4; };  // fp32, quantised afterwards
+
+template <int DT>
+__device__ __forceinline__ void store_h(uint8_t* h, size_t idx, float v) {
+  if constexpr (DT == MOE_BF16)
+    reinterpret_cast<uint16_t*>(h)[idx] = f32_to_bf16(v);
+  else
+    reinterpret_cast<float*>(h)[idx] = v;
+}
+
+// Expert outputs are stored in the activation dtype: fp32 for the fp32 layer,
+// bf16 for bf16 and fp8 weights.
+template <int DT>
+__device__ __forceinline__ void store_y(uint8_t* y, size_t idx, float v) {
+  if constexpr (DT == MOE_F32)
+    reinterpret_cast<float*>(y)[idx] = v;
+  else
+    reinterpret_cast<uint16_t*>(y)[idx] = f32_to_bf16(v);
+}
+
+constexpr int kSkNT = 8;   // 8-row weight tiles per routed skinny item (even: gate/up halves in GEMM1)
+constexpr int kShNT = 2;   // 8-row weight tiles per item of the skinny shared expert
+constexpr int kShKS = 8;   // waves splitting K in the skinny shared expert's workgroups
+constexpr int kTM = 256;   // tiled GEMM: tile rows (tokens)
+constexpr int kTN = 256;   // tiled GEMM: tile columns (weight rows; GEMM1: 128 gate + 128 up)
+
+// Launchers (explicitly instantiated for MOE_F32, MOE_BF16, MOE_FP8_E4M3).
+// mode 1 = gate/up GEMM with SwiGLU, mode 2 = down GEMM.
+// Routed skinny class cls (0: 1..8 rows, 1: 9..16, 2: 17..32) over `grid` workgroups.
+template <int DT>
+hipError_t launch_skinny(int mode, int cls, unsigned grid, const Args& a, hipStream_t st);
+// The shared expert when T <= kSkinnyRows.
+template <int DT>
+hipError_t launch_shared_skinny(int mode, int T, const Args& a, hipStream_t st);
+// Tiled grouped GEMM: the plan's fat tiles (shared = false) or the shared
+// expert's ceil(T / kTM) row tiles (shared = true); ntn column tiles each.
+template <int DT>
+hipError_t launch_tiled(int mode, bool shared, unsigned grid, int ntn, const Args& a, hipStream_t st);
+
+}  // namespace ffn
+}  // namespace moe

@@ -1,0 +1,349 @@
+// Skinny grouped GEMM: expert groups of 1..32 rows (decode), streamed.
+//
+// Perplexity's "Lower latency and higher throughput with multi-node DeepSeek
+// deployment" (section "GroupGEMM") finds the grouped GEMM bandwidth-bound
+// while the rows per expert are few; here each weight byte is read from HBM
+// exactly once, straight into MFMA registers, against the group's rows.
+
+#include "ffn.h"
+
+namespace {
+
+using namespace moe::ffn;
+
+//
+// Streaming layout.  A weight row is read in 128-byte windows (one cache
+// line).  One wave load instruction covers 8 weight rows x one window: lane l
+// reads row (l % 8), 16-byte chunk c(l) = 4 * ((l >> 3) & 1) + (l >> 4).  Fed
+// as the B operand of a 16x16 MFMA, column n (lane l % 16) thus holds weight
+// row n % 8, and columns n and n + 8 hold the two complementary 64-byte halves
+// of the window.  The A operand mirrors this: M row m holds token m % 8 with
+// the same chunk rule.  The diagonal 8x8 blocks of the 16x16 result are then
+// the two K halves of the same (token, row) dot products and the off-diagonal
+// blocks are discarded: out[t][r] = C[t][r] + C[t+8][r+8], which sits in lanes
+// L and L ^ 40.  Half of each MFMA is wasted, which costs nothing in this
+// bandwidth-bound regime, and every load instruction reads whole cache lines.
+
+
+// Weights are read exactly once: nontemporal loads keep them from displacing
+// the reused activation rows in the caches.
+__device__ __forceinline__ i32x4 ldw16(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
+}
+
+__device__ __forceinline__ int sk_chunk(int lane) { return 4 * ((lane >> 3) & 1) + (lane >> 4); }
+
+// One pass over the full K for NTP of the wave's NT weight tiles (pass p),
+// against MT M tiles of 8 tokens (MT * 8 >= group rows).  Rows beyond the
+// group's count are clamped to its last row: their results are never stored,
+// so the K loop carries no per-lane predicates or branches.  U windows per
+// loop trip give NTP * U = 8 independent weight loads per lane.
+//
+// Split K (KS > 1): the KS waves of a workgroup share the item, wave `ks`
+// takes windows [ks*nwin/KS, (ks+1)*nwin/KS); partial accumulators meet in
+// LDS and wave 0 adds them in slice order (fixed order: reproducible) before
+// the epilogue.
+template <int DT, int MODE, int MT, int NT, int NTP, int U, int KS>
+__device__ __forceinline__ void skinny_pass(const Args& a, const Group& gr, int g, int it, int p, int lane,
+                                            int ks, f32x4* red) {
+  using F = Frag<DT>;
+  constexpr bool FP8 = DT == MOE_FP8_E4M3;
+  const int r8 = lane & 7;
+  const int ch16 = sk_chunk(lane) * 16;
+  const int cols_per_item = MODE == 1 ? 4 * NT : 8 * NT;   // h columns (GEMM1) or y columns (GEMM2)
+  const int K = MODE == 1 ? a.H : a.I;
+  const size_t krow = (size_t)K * F::ESZ;
+  const int nwin = (int)(krow / 128);
+  const int w_begin = KS > 1 ? (int)((long long)nwin * ks / KS) : 0;
+  const int w_end = KS > 1 ? (int)((long long)nwin * (ks + 1) / KS) : nwin;
+
+  const uint8_t* abase = MODE == 1 ? a.a1 : a.a2;
+  int arow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int r = min(mt * 8 + r8, gr.m - 1);
+    arow[mt] = MODE == 1 ? gemm1_src_row(a, gr, r) : gr.slot0 + r;
+  }
+  const uint8_t* wbase;
+  const float* wsbase = nullptr;
+  if (MODE == 1) {
+    wbase = gr.routed ? a.w13 + (size_t)g * 2 * a.I * krow : a.ws13;
+    if (FP8) wsbase = gr.routed ? a.w13s + (size_t)g * 2 * a.I * nwin : a.ws13s;
+  } else {
+    wbase = gr.routed ? a.w2 + (size_t)g * a.H * krow : a.ws2;
+    if (FP8) wsbase = gr.routed ? a.w2s + (size_t)g * a.H * nwin : a.ws2s;
+  }
+  // tile j of this pass -> tile index in the item (GEMM1: first half gate, second half up)
+  int wrow[NTP];
+#pragma unroll
+  for (int j = 0; j < NTP; ++j) {
+    if (MODE == 1) {
+      const int jg = j < NTP / 2 ? p * (NTP / 2) + j : p * (NTP / 2) + j - NTP / 2;   // gate-tile index
+      wrow[j] = (j < NTP / 2 ? 0 : a.I) + it * cols_per_item + 8 * jg + r8;
+    } else {
+      wrow[j] = it * cols_per_item + 8 * (p * NTP + j) + r8;
+    }
+  }
+  const uint8_t* pb[NTP];
+#pragma unroll
+  for (int j = 0; j < NTP; ++j) pb[j] = wbase + (size_t)wrow[j] * krow + ch16;
+  const uint8_t* pa[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) pa[mt] = abase + (size_t)arow[mt] * krow + ch16;
+
+  f32x4 acc[MT][NTP];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < NTP; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if constexpr (!FP8) {
+    int w = w_begin;
+    for (; w + U <= w_end; w += U) {
+      i32x4 b[U][NTP], av[U][MT];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const size_t off = (size_t)(w + u) * 128;
+#pragma unroll
+        for (int j = 0; j < NTP; ++j) b[u][j] = ldw16(pb[j] + off);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) av[u][mt] = ld16(pa[mt] + off);
+      }
+      // Keep every load of the trip ahead of its MFMAs: left alone, the
+      // scheduler interleaves them to shorten live ranges and waits on each
+      // load in turn, which leaves few bytes in flight per wave.
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int j = 0; j < NTP; ++j) F::mma(acc[mt][j], av[u][mt], b[u][j]);
+    }
+    for (; w < w_end; ++w) {
+      const size_t off = (size_t)w * 128;
+      i32x4 b[NTP];
+#pragma unroll
+      for (int j = 0; j < NTP; ++j) b[j] = ldw16(pb[j] + off);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const i32x4 av = ld16(pa[mt] + off);
+#pragma unroll
+        for (int j = 0; j < NTP; ++j) F::mma(acc[mt][j], av, b[j]);
+      }
+    }
+  } else {
+    // One 128-byte window is one fp8 scale block.  Scales of the C rows this
+    // lane holds (token (4*(lane>>4)+i) % 8 of each M tile) and of its column's row.
+    const float* sbase = MODE == 1 ? a.a1s : a.a2s;
+    int sa_row[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = min(mt * 8 + ((4 * (lane >> 4) + i) & 7), gr.m - 1);
+        sa_row[mt][i] = (MODE == 1 ? gemm1_src_row(a, gr, r) : gr.slot0 + r) * nwin;
+      }
+    // U windows per trip: all loads of the trip are issued before its MFMAs.
+    constexpr int UF = MT >= 4 ? (U < 2 ? U : 2) : U;
+    int w = w_begin;
+    for (; w < w_end; w += UF) {
+      i32x4 b[UF][NTP], av[UF][MT];
+      float sw[UF][NTP], sa[UF][MT][4];
+#pragma unroll
+      for (int u = 0; u < UF; ++u) {
+        const int wu = min(w + u, w_end - 1);   // a short last trip recomputes its last window, not added
+        const size_t off = (size_t)wu * 128;
+#pragma unroll
+        for (int j = 0; j < NTP; ++j) b[u][j] = ldw16(pb[j] + off);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) av[u][mt] = ld16(pa[mt] + off);
+#pragma unroll
+        for (int j = 0; j < NTP; ++j) sw[u][j] = wsbase[(size_t)wrow[j] * nwin + wu];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sa[u][mt][i] = sbase[(size_t)sa_row[mt][i] + wu];
+      }
+      __builtin_amdgcn_sched_barrier(0);   // all loads of the trip before its MFMAs
+#pragma unroll
+      for (int u = 0; u < UF; ++u) {
+        if (u > 0 && w + u >= w_end) break;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int j = 0; j < NTP; ++j) {
+            f32x4 pr = {0.f, 0.f, 0.f, 0.f};
+            // a 16-byte chunk is 16 fp8 values: two 16x16x32 MFMAs (8 bytes per lane each)
+            pr = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(((const long*)&av[u][mt])[0], ((const long*)&b[u][j])[0], pr, 0, 0, 0);
+            pr = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(((const long*)&av[u][mt])[1], ((const long*)&b[u][j])[1], pr, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mt][j][i] = fmaf(pr[i], sa[u][mt][i] * sw[u][j], acc[mt][j][i]);
+          }
+      }
+    }
+  }
+
+  if constexpr (KS > 1) {
+    // red: [KS-1][MT*NTP][64] partial accumulators of waves 1..KS-1
+    if (ks > 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < NTP; ++j) red[((ks - 1) * MT * NTP + mt * NTP + j) * 64 + lane] = acc[mt][j];
+    }
+    __syncthreads();
+    if (ks == 0) {
+      for (int q = 0; q < KS - 1; ++q)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int j = 0; j < NTP; ++j) acc[mt][j] += red[(q * MT * NTP + mt * NTP + j) * 64 + lane];
+    }
+    __syncthreads();
+    if (ks > 0) return;
+  }
+
+  // Fold the two K halves: lanes L = 16*h + r (h < 2, r < 8) end up holding
+  // tokens 4*h + i (i = 0..3) of each M tile for weight row r of each tile.
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < NTP; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[mt][j][i] += __shfl_xor(acc[mt][j][i], 40, 64);
+  if ((lane & 8) || lane >= 32) return;
+  const int hh = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = mt * 8 + 4 * hh + i;
+      if (r >= gr.m) continue;
+      if (MODE == 1) {
+        const size_t hrow = (size_t)(gr.slot0 + r) * a.I;
+#pragma unroll
+        for (int j = 0; j < NTP / 2; ++j) {
+          const float gv = acc[mt][j][i], uv = acc[mt][j + NTP / 2][i];
+          store_h<DT>(a.h, hrow + it * cols_per_item + 8 * (p * (NTP / 2) + j) + r8, silu(gv) * uv);
+        }
+      } else {
+        uint8_t* ybase = gr.routed ? a.y_sorted : a.y_shared;
+        const size_t yrow = (size_t)(gr.routed ? gr.slot0 + r : r) * a.H;
+#pragma unroll
+        for (int j = 0; j < NTP; ++j) store_y<DT>(ybase, yrow + it * cols_per_item + 8 * (p * NTP + j) + r8, acc[mt][j][i]);
+      }
+    }
+  }
+}
+
+// All NT tiles of an item with MT M tiles: NT / NTP passes.
+template <int DT, int MODE, int MT, int NT, int KS>
+__device__ __forceinline__ void skinny_tile(const Args& a, const Group& gr, int g, int it, int lane, int ks,
+                                            f32x4* red) {
+  constexpr int NTP = MT == 1 ? NT : (NT / MT >= 2 ? NT / MT : 2);
+  constexpr int U0 = 8 / NTP > 0 ? 8 / NTP : 1;
+  constexpr int U = MT >= 4 && U0 > 2 ? 2 : U0;
+  for (int p = 0; p < NT / NTP; ++p) skinny_pass<DT, MODE, MT, NT, NTP, U, KS>(a, gr, g, it, p, lane, ks, red);
+}
+
+// Routed skinny groups of class CLS (MT = 1, 2, 4 M tiles of 8 tokens).
+// One wave = one work item (group, column block of kSkNT weight tiles) in a
+// single pass over K; waves past the class's list exit at once.  Every class
+// uses the same wide items: each activation fragment then serves 8 weight
+// tiles, which keeps the activation re-reads (one per item) a small share of
+// the load instructions even at 32 rows.
+template <int DT, int MODE, int CLS>
+__global__ __launch_bounds__(256) void ffn_skinny_kernel(Args a) {
+  constexpr int MT = 1 << CLS;
+  constexpr int NT = kSkNT;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cols_per_item = MODE == 1 ? 4 * NT : 8 * NT;
+  const int items = (MODE == 1 ? a.I : a.H) / cols_per_item;
+  // XCD-aware order: workgroups go to the 8 XCDs round-robin (blockIdx % 8),
+  // so XCD x takes the contiguous range x * per_xcd ... of the class's real
+  // work.  The items of a group then run on one or two XCDs and its
+  // activation rows, re-read by every item, stay in that XCD's L2 instead of
+  // being fetched into all eight.  The grid is a multiple of 8 and at least
+  // 8 * per_xcd workgroups.
+  const int real_wg = (a.plan[CLS] * items + 3) >> 2;
+  const int per_xcd = (real_wg + 7) >> 3;
+  const int local = blockIdx.x >> 3;
+  if (local >= per_xcd) return;
+  const int item = ((blockIdx.x & 7) * per_xcd + local) * 4 + wave;
+  const int gi = item / items;
+  if (gi >= a.plan[CLS]) return;
+  const int g = a.plan[kPlanHead + CLS * a.G + gi];
+  const int it = item - gi * items;
+  const Group gr = group_of(a, g);
+  skinny_pass<DT, MODE, MT, NT, NT, 1, 1>(a, gr, g, it, 0, lane, 0, nullptr);
+}
+
+// The shared expert when T <= kSkinnyRows: its row count is known on the
+// host, so its launch is sized exactly, with narrow items (kShNT tiles) and
+// the K range split over the kShKS waves of each workgroup.
+
+template <int DT, int MODE, int MT>
+__global__ __launch_bounds__(64 * kShKS) void ffn_shared_skinny_kernel(Args a) {
+  constexpr int NTP = MT == 1 ? kShNT : (kShNT / MT >= 2 ? kShNT / MT : 2);
+  __shared__ f32x4 red[(kShKS - 1) * MT * NTP * 64];
+  const int lane = threadIdx.x & 63, ks = threadIdx.x >> 6;
+  const Group gr = group_of(a, a.E);
+  skinny_tile<DT, MODE, MT, kShNT, kShKS>(a, gr, a.E, blockIdx.x, lane, ks, red);
+}
+
+template <int DT>
+hipError_t launch_skinny_t(int mode, int cls, unsigned grid, const Args& a, hipStream_t st) {
+  static const char* const kName[2][3] = {
+      {"ffn_gemm1_skinny_m8", "ffn_gemm1_skinny_m16", "ffn_gemm1_skinny_m32"},
+      {"ffn_gemm2_skinny_m8", "ffn_gemm2_skinny_m16", "ffn_gemm2_skinny_m32"}};
+  const char* name = kName[mode - 1][cls];
+#define MOE_SK(M, CLS) MOE_LAUNCH(name, (ffn_skinny_kernel<DT, M, CLS>), dim3(grid), dim3(256), 0, st, a)
+  if (mode == 1) {
+    if (cls == 0) MOE_SK(1, 0); else if (cls == 1) MOE_SK(1, 1); else MOE_SK(1, 2);
+  } else {
+    if (cls == 0) MOE_SK(2, 0); else if (cls == 1) MOE_SK(2, 1); else MOE_SK(2, 2);
+  }
+#undef MOE_SK
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_shared_skinny_t(int mode, int T, const Args& a, hipStream_t st) {
+  const int N = mode == 1 ? a.I : a.H;
+  const dim3 grid(N / (mode == 1 ? 4 * kShNT : 8 * kShNT));
+  const char* name = mode == 1 ? "ffn_gemm1_shared_skinny" : "ffn_gemm2_shared_skinny";
+#define MOE_SH(M, MT) MOE_LAUNCH(name, (ffn_shared_skinny_kernel<DT, M, MT>), grid, dim3(64 * kShKS), 0, st, a)
+  if (mode == 1) {
+    if (T <= 8) MOE_SH(1, 1); else if (T <= 16) MOE_SH(1, 2); else MOE_SH(1, 4);
+  } else {
+    if (T <= 8) MOE_SH(2, 1); else if (T <= 16) MOE_SH(2, 2); else MOE_SH(2, 4);
+  }
+#undef MOE_SH
+  return hipGetLastError();
+}
+
+}  // namespace
+
+namespace moe {
+namespace ffn {
+
+template <int DT>
+hipError_t launch_skinny(int mode, int cls, unsigned grid, const Args& a, hipStream_t st) {
+  return launch_skinny_t<DT>(mode, cls, grid, a, st);
+}
+template <int DT>
+hipError_t launch_shared_skinny(int mode, int T, const Args& a, hipStream_t st) {
+  return launch_shared_skinny_t<DT>(mode, T, a, st);
+}
+
+#define MOE_INST(DT)                                                                                \
+  template hipError_t launch_skinny<DT>(int, int, unsigned, const Args&, hipStream_t);              \
+  template hipError_t launch_shared_skinny<DT>(int, int, const Args&, hipStream_t);
+MOE_INST(MOE_F32)
+MOE_INST(MOE_BF16)
+MOE_INST(MOE_FP8_E4M3)
+#undef MOE_INST
+
+}  // namespace ffn
+}  // namespace moe

@@ -65,6 +65,7 @@ struct SideStream {
   hipStream_t stream;
   hipEvent_t fork;
   hipEvent_t join;
+  int cus;          // compute units of the device
 };
 hipError_t side_stream(SideStream* out);
 

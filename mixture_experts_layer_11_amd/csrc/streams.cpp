@@ -2,7 +2,7 @@
 //
 // One non-blocking stream (default priority) and two timing-free events per
 // host thread and device, created on first use and kept until the process
-// ends.  Each call forks from the caller's stream with `fork` and joins back
+// ends, with the device's CU count.  Each call forks from the caller's stream with `fork` and joins back
 // with `join`, so the caller's stream keeps the library's ordering contract:
 // everything a call enqueues runs after earlier work on that stream and before
 // later work on it.  Per-thread resources keep calls from different host
@@ -26,6 +26,7 @@ hipError_t side_stream(SideStream* out) {
     if ((e = hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking)) != hipSuccess) return e;
     if ((e = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming)) != hipSuccess) return e;
     if ((e = hipEventCreateWithFlags(&n.join, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&n.cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
     s = n;
   }
   *out = s;

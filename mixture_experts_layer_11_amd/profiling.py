@@ -27,10 +27,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 
 KERNEL_SOURCES = {
-    **{f"ffn_gemm{g}_skinny_m{m}": "ffn.hip" for g in (1, 2) for m in (8, 16, 32)},
-    "ffn_gemm1_shared_skinny": "ffn.hip", "ffn_gemm2_shared_skinny": "ffn.hip",
-    "ffn_gemm1_shared_tiled": "ffn.hip", "ffn_gemm2_shared_tiled": "ffn.hip",
-    "ffn_gemm1_tiled": "ffn.hip", "ffn_gemm2_tiled": "ffn.hip", "ffn_plan": "ffn.hip",
+    **{f"ffn_gemm{g}_skinny_m{m}": "ffn_skinny.hip" for g in (1, 2) for m in (8, 16, 32)},
+    "ffn_gemm1_shared_skinny": "ffn_skinny.hip", "ffn_gemm2_shared_skinny": "ffn_skinny.hip",
+    "ffn_gemm1_tiled": "ffn_tiled.hip", "ffn_gemm2_tiled": "ffn_tiled.hip",
+    "ffn_gemm1_shared_tiled": "ffn_tiled.hip", "ffn_gemm2_shared_tiled": "ffn_tiled.hip", "ffn_plan": "ffn.hip",
     "route_gate_fused": "route.hip", "route_gate_split": "route.hip", "route_reduce_select": "route.hip",
     "dispatch_count": "dispatch.hip", "dispatch_scan": "dispatch.hip", "dispatch_scatter": "dispatch.hip",
     "quant_fp8": "quant.hip", "combine": "combine.hip",
@@ -40,10 +40,11 @@ _DT = {"f32": 0, "bf16": 1, "fp8": 2}
 
 
 def kernel_source_hash(kernel: str) -> str:
-    """sha256 prefix of the kernel's source file plus the shared device header."""
+    """sha256 prefix of the kernel's source file plus the device headers it includes."""
     h = hashlib.sha256()
     csrc = os.path.join(PKG, "csrc")
-    for f in (KERNEL_SOURCES.get(kernel, ""), "moe_common.h"):
+    src = KERNEL_SOURCES.get(kernel, "")
+    for f in (src, "ffn.h" if src.startswith("ffn") else "", "moe_common.h"):
         p = os.path.join(csrc, f)
         if os.path.isfile(p):
             h.update(open(p, "rb").read())
@@ -58,7 +59,8 @@ def rocprof_name(kernel: str, w_dtype: str) -> str:
         cls = {"8": 0, "16": 1, "32": 2}[kernel.rsplit("_m", 1)[1]]
         return f"void (anonymous namespace)::ffn_skinny_kernel<{dt}, {mode}, {cls}>"
     if kernel.startswith("ffn_gemm") and kernel.endswith("_tiled"):
-        return f"void (anonymous namespace)::ffn_fat_kernel<{dt}, {int(kernel[8])}>"
+        shared = "true" if "_shared_" in kernel else "false"
+        return f"void (anonymous namespace)::ffn_fat_kernel<{dt}, {int(kernel[8])}, {shared}>"
     if kernel.startswith("ffn_gemm") and kernel.endswith("_shared_skinny"):
         return f"void (anonymous namespace)::ffn_shared_skinny_kernel<{dt}, {int(kernel[8])}, "
     fixed = {"ffn_plan": "(anonymous namespace)::ffn_plan_kernel",
