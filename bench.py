@@ -55,12 +55,25 @@ def kernel_models(cfg, counts):
     sc13 = (2 * I * H // qb) * 4 if fp8 else 0
     sc2 = (H * I // qb) * 4 if fp8 else 0
     groups = [int(c) for c in counts]
-    m = {f"ffn_gemm{g}_{r}": {"bytes": 0, "flops": 0} for g in (1, 2)
-         for r in ("skinny_m8", "skinny_m16", "skinny_m32", "tiled", "shared_skinny", "shared_tiled")}
-    items = [(mg, ("skinny_m8" if mg <= 8 else "skinny_m16" if mg <= 16 else "skinny_m32")
-              if mg <= SKINNY_ROWS else "tiled") for mg in groups]
+    regions = ("skinny_m8", "skinny_m16", "skinny_m32", "tiled", "tiled128", "shared_skinny", "shared_tiled",
+               "shared_tiled128")
+    m = {f"ffn_gemm{g}_{r}": {"bytes": 0, "flops": 0} for g in (1, 2) for r in regions}
+    # (rows, region): a group of > 32 rows takes 256-row tiles; with fp8
+    # weights only its floor(m / 256) full tiles do, and its other m mod 256
+    # rows take the 128-row kernel.  Each kernel that serves a group streams
+    # that group's weights once.
+    def tiled(mg, pre):
+        if not fp8:
+            return [(mg, pre + "tiled")]
+        return [(mg // 256 * 256, pre + "tiled"), (mg % 256, pre + "tiled128")]
+    items = []
+    for mg in [int(c) for c in counts]:
+        if mg <= SKINNY_ROWS:
+            items.append((mg, "skinny_m8" if mg <= 8 else "skinny_m16" if mg <= 16 else "skinny_m32"))
+        else:
+            items += tiled(mg, "")
     if cfg.I_shared:
-        items.append((T, "shared_skinny" if T <= SKINNY_ROWS else "shared_tiled"))
+        items += [(T, "shared_skinny")] if T <= SKINNY_ROWS else tiled(T, "shared_")
     for mg, reg in items:
         if mg == 0:
             continue

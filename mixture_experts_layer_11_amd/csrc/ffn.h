@@ -11,8 +11,10 @@ namespace moe {
 namespace ffn {
 
 constexpr int kSkinnyRows = 32;  // groups with <= this many rows take the skinny path
-constexpr int kTileRows = 256;   // rows per tile of the tiled grouped GEMM
-constexpr int kPlanHead = 4;     // plan: [0..2] skinny list sizes (<=8, <=16, <=32 rows), [3] fat tiles
+constexpr int kTileRows = 256;   // rows per full tile of the tiled grouped GEMM
+constexpr int kMidRows = 128;    // rows per tile for the rest of a group (m mod 256 rows), fp8 weights
+constexpr int kPlanHead = 5;     // plan: [0..2] skinny list sizes (<=8, <=16, <=32 rows), [3] 256-row tiles,
+                                 // [4] 128-row tiles
 
 struct Args {
   int T, H, E, k, I, P;
@@ -37,6 +39,8 @@ struct Args {
   uint8_t* y_shared;
   const int32_t* plan;          // see ffn_plan_kernel: list sizes, 3 skinny lists of G, fat (group,row0) pairs
   int G;
+  int fat_cap;                  // capacity of the plan's 256-row tile list (the 128-row list follows it)
+  int mid_rest;                 // 1: a group's last m mod 256 rows take 128-row tiles; 0: one more 256-row tile
 };
 
 struct Group {
@@ -101,10 +105,12 @@ hipError_t launch_skinny(int mode, int cls, unsigned grid, const Args& a, hipStr
 // The shared expert when T <= kSkinnyRows.
 template <int DT>
 hipError_t launch_shared_skinny(int mode, int T, const Args& a, hipStream_t st);
-// Tiled grouped GEMM: the plan's fat tiles (shared = false) or the shared
-// expert's ceil(T / kTM) row tiles (shared = true); ntn column tiles each.
+// Tiled grouped GEMM with tm-row tiles (256 or 128): the plan's list of that
+// size (shared = false) or the shared expert's tiles of that size (shared =
+// true: floor(T / 256) full tiles, or ceil((T mod 256) / 128) tiles for the
+// rest); ntn column tiles each.
 template <int DT>
-hipError_t launch_tiled(int mode, bool shared, unsigned grid, int ntn, const Args& a, hipStream_t st);
+hipError_t launch_tiled(int mode, bool shared, int tm, unsigned grid, int ntn, const Args& a, hipStream_t st);
 
 }  // namespace ffn
 }  // namespace moe

@@ -44,28 +44,35 @@ using namespace moe::ffn;
 __global__ __launch_bounds__(512) void ffn_plan_kernel(Args a) {
   __shared__ int sk[3][512];
   __shared__ int ft[512];
+  __shared__ int mt[512];
   const int g = threadIdx.x;
   int m = 0;
   if (g < a.G) m = g < a.E ? a.offsets[g + 1] - a.offsets[g] : a.T;
-  // skinny class: 0 for 1..8 rows, 1 for 9..16, 2 for 17..32 (a skinny shared
-  // expert has a launch of its own and is in no list)
+  // skinny class: 0 for 1..8 rows, 1 for 9..16, 2 for 17..32; larger groups
+  // take floor(m / 256) full tiles, and their last m mod 256 rows one more
+  // 256-row tile or (mid_rest) ceil((m mod 256) / 128) 128-row tiles.  The
+  // shared expert is in no list: it has launches of its own.
   const bool shared = g == a.E;
   const int cls = (m > 0 && m <= kSkinnyRows && !shared) ? (m <= 8 ? 0 : m <= 16 ? 1 : 2) : -1;
-  // the shared expert is never in the lists: it has launches of its own
-  const int tiles = m > kSkinnyRows && !shared ? (m + kTileRows - 1) / kTileRows : 0;
+  const bool tiled = m > kSkinnyRows && !shared;
+  const int tiles = tiled ? (a.mid_rest ? m / kTileRows : (m + kTileRows - 1) / kTileRows) : 0;
+  const int mids = tiled && a.mid_rest ? (m % kTileRows + kMidRows - 1) / kMidRows : 0;
 #pragma unroll
   for (int c = 0; c < 3; ++c) sk[c][g] = cls == c ? 1 : 0;
   ft[g] = tiles;
+  mt[g] = mids;
   __syncthreads();
   for (int d = 1; d < 512; d <<= 1) {
     int v[3];
 #pragma unroll
     for (int c = 0; c < 3; ++c) v[c] = g >= d ? sk[c][g - d] : 0;
     const int v2 = g >= d ? ft[g - d] : 0;
+    const int v3 = g >= d ? mt[g - d] : 0;
     __syncthreads();
 #pragma unroll
     for (int c = 0; c < 3; ++c) sk[c][g] += v[c];
     ft[g] += v2;
+    mt[g] += v3;
     __syncthreads();
   }
   int32_t* plan = const_cast<int32_t*>(a.plan);
@@ -73,13 +80,20 @@ __global__ __launch_bounds__(512) void ffn_plan_kernel(Args a) {
 #pragma unroll
     for (int c = 0; c < 3; ++c) plan[c] = sk[c][511];
     plan[3] = ft[511];
+    plan[4] = mt[511];
   }
   if (cls >= 0) plan[kPlanHead + cls * a.G + sk[cls][g] - 1] = g;
-  const int t0 = ft[g] - tiles;
   int32_t* fat = plan + kPlanHead + 3 * a.G;
+  const int t0 = ft[g] - tiles;
   for (int i = 0; i < tiles; ++i) {
     fat[2 * (t0 + i)] = g;
     fat[2 * (t0 + i) + 1] = i * kTileRows;
+  }
+  int32_t* mid = fat + 2 * a.fat_cap;
+  const int m0 = mt[g] - mids;
+  for (int i = 0; i < mids; ++i) {
+    mid[2 * (m0 + i)] = g;
+    mid[2 * (m0 + i) + 1] = tiles * kTileRows + i * kMidRows;
   }
 }
 
@@ -99,7 +113,11 @@ hipError_t run_shared(const moe_cfg& c, const Args& a, hipStream_t st) {
       e = launch_shared_skinny<DT>(mode, c.T, a, st);
     } else {
       const int ntn = mode == 1 ? moe::ceil_div(c.I, kTN / 2) : moe::ceil_div(c.H, kTN);
-      e = launch_tiled<DT>(mode, true, (unsigned)(moe::ceil_div(c.T, kTM) * ntn), ntn, a, st);
+      const int full = a.mid_rest ? c.T / kTileRows : moe::ceil_div(c.T, kTileRows);
+      const int rest = a.mid_rest ? moe::ceil_div(c.T % kTileRows, kMidRows) : 0;
+      e = hipSuccess;
+      if (full > 0) e = launch_tiled<DT>(mode, true, kTileRows, (unsigned)(full * ntn), ntn, a, st);
+      if (e == hipSuccess && rest > 0) e = launch_tiled<DT>(mode, true, kMidRows, (unsigned)(rest * ntn), ntn, a, st);
     }
     if (e != hipSuccess) return e;
   }
@@ -115,12 +133,13 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int P = a.P;
-  // Upper bound of the fat tiles: a token picks k distinct experts, so a
-  // routed group has at most T rows and none is fat when T <= kSkinnyRows.
-  // Otherwise at most ceil(P / kTileRows) full tiles plus one partial tile per
-  // fat group, and at most min(E, P / (kSkinnyRows + 1)) fat groups.
-  const int fat_groups = c.T > kSkinnyRows ? (P / (kSkinnyRows + 1) < c.E ? P / (kSkinnyRows + 1) : c.E) : 0;
-  const int max_fat = fat_groups > 0 ? moe::ceil_div(P, kTileRows) + fat_groups : 0;
+  // Upper bounds of the tile lists: a token picks k distinct experts, so a
+  // routed group has at most T rows and none is tiled when T <= kSkinnyRows.
+  // Otherwise at most P / 256 full tiles, and at most two 128-row tiles per
+  // tiled group, of which there are at most min(E, P / (kSkinnyRows + 1)).
+  const int tiled_groups = c.T > kSkinnyRows ? (P / (kSkinnyRows + 1) < c.E ? P / (kSkinnyRows + 1) : c.E) : 0;
+  const int max_fat = tiled_groups > 0 ? P / kTileRows + (a.mid_rest ? 0 : tiled_groups) : 0;
+  const int max_mid = a.mid_rest ? 2 * tiled_groups : 0;
   for (int mode = 1; mode <= 2; ++mode) {
     if (mode == 2 && DT == MOE_FP8_E4M3) {
       e = moe::launch_quant_fp8(P, c.I, a.qb, a.h, MOE_F32, const_cast<uint8_t*>(a.a2), const_cast<float*>(a.a2s), st);
@@ -137,7 +156,9 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st) {
       if ((e = launch_skinny<DT>(mode, cls, grid, a, st)) != hipSuccess) return e;
     }
     const int ntn = mode == 1 ? moe::ceil_div(c.I, kTN / 2) : moe::ceil_div(c.H, kTN);
-    if (max_fat > 0 && (e = launch_tiled<DT>(mode, false, (unsigned)(max_fat * ntn), ntn, a, st)) != hipSuccess)
+    if (max_fat > 0 && (e = launch_tiled<DT>(mode, false, kTileRows, (unsigned)(max_fat * ntn), ntn, a, st)) != hipSuccess)
+      return e;
+    if (max_mid > 0 && (e = launch_tiled<DT>(mode, false, kMidRows, (unsigned)(max_mid * ntn), ntn, a, st)) != hipSuccess)
       return e;
   }
   return hipSuccess;
@@ -160,7 +181,9 @@ hipError_t run_ffn(const moe_cfg& c, const Args& a, hipStream_t st) {
   moe::SideStream side;
   hipError_t e = moe::side_stream(&side);
   if (e != hipSuccess) return e;
-  const long long shared_tiles1 = (long long)moe::ceil_div(c.T, kTM) * moe::ceil_div(c.I, kTN / 2);
+  const long long shared_tiles1 =
+      (long long)(a.mid_rest ? c.T / kTileRows + moe::ceil_div(c.T % kTileRows, kMidRows) : moe::ceil_div(c.T, kTileRows)) *
+      moe::ceil_div(c.I, kTN / 2);
   if (c.T <= kSkinnyRows || shared_tiles1 >= side.cus) {
     e = run_shared<DT>(c, a, st);
     return e != hipSuccess ? e : run_routed<DT>(c, a, st);
@@ -179,11 +202,14 @@ hipError_t run_ffn(const moe_cfg& c, const Args& a, hipStream_t st) {
 
 namespace moe {
 
+// Capacity of the 256-row tile list: at most P / 256 full tiles, plus one
+// partial tile per routed group unless those rows take 128-row tiles.
+int ffn_fat_cap(const moe_cfg& c) { return c.T * c.k / kTileRows + (c.w_dtype == MOE_FP8_E4M3 ? 0 : c.E); }
+
 size_t ffn_plan_ints(const moe_cfg& c) {
-  const int P = c.T * c.k;
   const int G = c.E + (c.I_shared > 0 ? 1 : 0);
-  const int max_fat = ceil_div(P, kTileRows) + c.E + (c.I_shared > 0 ? ceil_div(c.T, kTileRows) : 0);
-  return kPlanHead + 3 * (size_t)G + 2 * (size_t)max_fat;
+  // 128-row tiles: at most two per routed group
+  return kPlanHead + 3 * (size_t)G + 2 * (size_t)ffn_fat_cap(c) + 2 * (size_t)(2 * c.E);
 }
 
 size_t ffn_h_elem_bytes(const moe_cfg& c) { return c.w_dtype == MOE_BF16 ? 2 : 4; }
@@ -215,6 +241,8 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const void* x, const int32_t* off
   a.y_shared = static_cast<uint8_t*>(y_shared);
   a.plan = ws.plan;
   a.G = c.E + (a.has_shared ? 1 : 0);
+  a.fat_cap = ffn_fat_cap(c);
+  a.mid_rest = c.w_dtype == MOE_FP8_E4M3;   // HBM-bound medium groups: deeper pipeline on 128-row tiles
   if (c.w_dtype == MOE_FP8_E4M3) {
     hipError_t e = launch_quant_fp8(c.T, c.H, c.quant_block, x, MOE_BF16, ws.xq, ws.xs, st);
     if (e != hipSuccess) return e;

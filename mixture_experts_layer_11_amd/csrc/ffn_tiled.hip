@@ -11,32 +11,44 @@ namespace {
 
 using namespace moe::ffn;
 
-//
-// 256 x 256 output tile per workgroup of 8 waves (4 along M x 2 along N, each
-// 64 x 128 with 16x16 MFMAs).  K advances in slices of SL bytes per row: each
-// slice of the 256 A rows and the 256 B rows goes global -> LDS directly (16
-// bytes per lane per instruction) into an NST-deep ring of LDS stages, so the
-// loads run NST - 1 slices ahead of the MFMAs and there is one barrier per
-// slice.  bf16/fp32 use 64-byte slices with 4 stages; fp8 uses 128-byte
-// slices (one scale block) with 2 stages.  LDS rows are SL bytes with 16-byte
-// chunk c of row r stored at chunk c ^ swizzle(r), which keeps the fragment
-// reads of 16 consecutive rows free of bank conflicts; the direct loads write
-// chunks in lane order, so each lane fetches the global chunk that belongs
-// at its position.  Waves whose 64 rows lie beyond the tile's valid rows skip
-// their MFMAs.
+// Output tiles of TM x kTN per workgroup of 8 waves, with 16x16 MFMAs:
+//   TM = 256: 4 waves along M x 2 along N, 64 x 128 each, 2 LDS stages
+//             (groups of 256 rows and more: the prefill regime);
+//   TM = 128: 2 waves along M x 4 along N, 64 x 64 each, 3 LDS stages
+//             (fp8 weights: the last 1..255 rows of a group, and groups of
+//             33..255 rows).
+// K advances in 128-byte slices: each slice of the TM A rows and the kTN B
+// rows goes global -> LDS directly (16 bytes per lane per instruction) into
+// a ring of NST stages, so the loads run NST - 1 slices ahead of the MFMAs
+// and there is one barrier per slice.  With 128-row tiles a stage is 48 KB,
+// so three fit and two weight slices (64 KB) per CU stay in flight: the
+// medium groups are bound by HBM, and the bytes in flight per CU set the
+// bandwidth.  LDS rows are 128 bytes with 16-byte chunk c of row r stored at
+// chunk c ^ (r & 7), which keeps the fragment reads of 16 consecutive rows
+// free of bank conflicts; the direct loads write chunks in lane order, so
+// each lane fetches the global chunk that belongs at its position.  fp8
+// scales of the slice (one per A row and per B row) go global -> LDS the same
+// way, 4 bytes per lane, so every thread issues the same number of loads per
+// slice and the wait counts are uniform.  Waves whose 64 rows lie beyond the
+// tile's valid rows skip their MFMAs.
 
-
-template <int DT> struct TileCfg {
+template <int DT, int TM> struct TileCfg {
   static constexpr int SL = 128;                              // bytes of K per slice and row
-  static constexpr int NST = 2;                               // LDS stages
+  static constexpr int NST = TM == 256 ? 2 : 3;               // LDS stages
   static constexpr int CPR = SL / 16;                         // 16-byte chunks per row
-  static constexpr int STAGE = (kTM + kTN) * SL;              // bytes per stage (A then B)
-  static constexpr int LPS = SL / 32;                         // direct loads per thread per slice, A and B each
-  static constexpr int ROWS_PER_INSTR = 1024 / SL;            // rows one wave instruction fills
-  __device__ static __forceinline__ int off(int r, int c) {
-    const int sw = SL == 128 ? (r & 7) : ((r >> 2) & 3);
-    return r * SL + ((c ^ sw) << 4);
-  }
+  static constexpr int RPI = 1024 / SL;                       // rows one wave instruction fills
+  static constexpr int WAVES_M = TM / 64;                     // waves along M (64 rows each)
+  static constexpr int WAVES_N = 8 / WAVES_M;                 // waves along N
+  static constexpr int WN = kTN / WAVES_N;                    // columns per wave
+  static constexpr int NTW = WN / 16;                         // 16-column MFMA tiles per wave
+  static constexpr int LPA = TM * SL / 1024 / 8;              // A loads per thread per slice
+  static constexpr int LPB = kTN * SL / 1024 / 8;             // B loads per thread per slice
+  static constexpr int NSC = 512;                             // fp8 scale slots per stage: 8 waves x 64
+  static constexpr int STAGE = (TM + kTN) * SL;               // tile bytes per stage (A then B)
+  static constexpr int PER_SLICE = LPA + LPB + (DT == MOE_FP8_E4M3 ? 1 : 0);   // loads per thread per slice
+  static constexpr size_t LDS_BYTES = (size_t)NST * STAGE + (DT == MOE_FP8_E4M3 ? (size_t)NST * NSC * 4 : 0);
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  __device__ static __forceinline__ int off(int r, int c) { return r * SL + ((c ^ (r & 7)) << 4); }
 };
 
 // s_waitcnt that waits for vmcnt <= n only (expcnt and lgkmcnt left at their maxima).
@@ -45,54 +57,61 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Issue the direct global -> LDS loads of slice kt into stage st (and, for
-// fp8, store the scale fetched one slice earlier and fetch the next one).
-template <int DT>
-__device__ __forceinline__ void tile_issue(uint8_t* smem, const uint8_t* const* ga, const uint8_t* const* gb, int kt,
-                                           int st, int wave, int tid, int nkt, float* lds_s, const float* gs,
-                                           float& rs) {
-  using C = TileCfg<DT>;
+// Workgroup barrier without the memory fence of __syncthreads(), whose
+// release would wait for every outstanding load, including the direct-to-LDS
+// loads of later slices that are meant to stay in flight.  The caller first
+// waits (vmcnt) for its own loads of the slice about to be read, so after the
+// barrier every wave's part of that slice is in LDS; the memory clobber keeps
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+// Issue the direct global -> LDS loads of slice kt into stage st.
+template <int DT, int TM>
+__device__ __forceinline__ void tile_issue(uint8_t* smem, const uint8_t* const* ga, const uint8_t* const* gb,
+                                           const float* gs, int kt, int st, int wave) {
+  using C = TileCfg<DT, TM>;
   const size_t off = (size_t)kt * C::SL;
-  uint8_t* la = smem + st * C::STAGE + wave * C::LPS * 1024;
-  uint8_t* lb = smem + st * C::STAGE + kTM * C::SL + wave * C::LPS * 1024;
+  uint8_t* la = smem + st * C::STAGE + wave * C::LPA * 1024;
+  uint8_t* lb = smem + st * C::STAGE + TM * C::SL + wave * C::LPB * 1024;
 #pragma unroll
-  for (int i = 0; i < C::LPS; ++i) {
-    __builtin_amdgcn_global_load_lds(ga[i] + off, la + i * 1024, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(gb[i] + off, lb + i * 1024, 16, 0, 0);
-  }
+  for (int i = 0; i < C::LPA; ++i) __builtin_amdgcn_global_load_lds(ga[i] + off, la + i * 1024, 16, 0, 0);
+#pragma unroll
+  for (int i = 0; i < C::LPB; ++i) __builtin_amdgcn_global_load_lds(gb[i] + off, lb + i * 1024, 16, 0, 0);
   if constexpr (DT == MOE_FP8_E4M3) {
-    lds_s[st * (kTM + kTN) + tid] = rs;
-    if (kt + 1 < nkt) rs = gs[kt + 1];            // consumed one slice later
+    float* ls = reinterpret_cast<float*>(smem + C::NST * C::STAGE) + st * C::NSC + wave * 64;
+    __builtin_amdgcn_global_load_lds(gs + kt, ls, 4, 0, 0);
   }
 }
 
-template <int DT, int MODE, bool SHARED>
+template <int DT, int MODE, bool SHARED, int TM>
 __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
   using F = Frag<DT>;
-  using C = TileCfg<DT>;
+  using C = TileCfg<DT, TM>;
   constexpr bool FP8 = DT == MOE_FP8_E4M3;
-  constexpr int SL = C::SL, NST = C::NST, LPS = C::LPS, RPI = C::ROWS_PER_INSTR;
+  constexpr int SL = C::SL, NST = C::NST, RPI = C::RPI, NTW = C::NTW, WN = C::WN;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  float* lds_s = reinterpret_cast<float*>(smem + NST * C::STAGE);   // fp8: [NST][kTM + kTN]
+  const float* lds_s = reinterpret_cast<const float*>(smem + NST * C::STAGE);   // fp8: [NST][NSC]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int row = lane & 15, grp = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int tile = blockIdx.x / ntn;
   const int nt = blockIdx.x - tile * ntn;
   int g, row0;
-  if constexpr (SHARED) {          // the grid covers exactly ceil(T / kTM) row tiles of the shared expert
+  if constexpr (SHARED) {
+    // the grid covers exactly the shared expert's tiles of this size: the
+    // floor(T / 256) full tiles, or the 128-row tiles of the rest
     g = a.E;
-    row0 = tile * kTM;
+    row0 = TM == 256 ? tile * 256 : (a.T / 256) * 256 + tile * 128;   // 128-row tiles only with mid_rest
   } else {
-    if (tile >= a.plan[3]) return;
-    const int32_t* fat = a.plan + kPlanHead + 3 * a.G;
-    g = fat[2 * tile];
-    row0 = fat[2 * tile + 1];
+    if (tile >= a.plan[TM == 256 ? 3 : 4]) return;
+    const int32_t* list = a.plan + kPlanHead + 3 * a.G + (TM == 256 ? 0 : 2 * a.fat_cap);
+    g = list[2 * tile];
+    row0 = list[2 * tile + 1];
   }
   const Group gr = group_of(a, g);
-  const int rows = min(kTM, gr.m - row0);
+  const int rows = min(TM, gr.m - row0);
   const int K = MODE == 1 ? a.H : a.I;
   const size_t krow = (size_t)K * F::ESZ;
   const int nkt = (int)(krow / SL);
@@ -118,72 +137,68 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
     }
     return min(nt * kTN + n, a.H - 1);
   };
+  // Source row of A row r (clamped: padded rows recompute a valid row, never stored).
+  auto a_src = [&](int r) -> int {
+    const int rr = r < rows ? r : rows - 1;
+    return MODE == 1 ? gemm1_src_row(a, gr, row0 + rr) : gr.slot0 + row0 + rr;
+  };
   // This lane's direct-load sources.  Wave instruction i fills LDS rows
-  // (wave * LPS + i) * RPI + lane / CPR, physical chunk lane % CPR.
-  const uint8_t* ga[LPS];
-  const uint8_t* gb[LPS];
+  // (wave * LP + i) * RPI + lane / CPR, physical chunk lane % CPR.
+  const uint8_t* ga[C::LPA];
+  const uint8_t* gb[C::LPB];
 #pragma unroll
-  for (int i = 0; i < LPS; ++i) {
-    const int r = (wave * LPS + i) * RPI + lane / C::CPR;
-    const int pc = lane % C::CPR;
-    const int lc = (C::off(r, pc) - r * SL) >> 4;   // the swizzle is an involution: logical chunk of physical pc
-    const int rr = r < rows ? r : rows - 1;          // clamp: padded rows recompute a valid row, never stored
-    const int src = MODE == 1 ? gemm1_src_row(a, gr, row0 + rr) : gr.slot0 + row0 + rr;
-    ga[i] = asrc + (size_t)src * krow + lc * 16;
+  for (int i = 0; i < C::LPA; ++i) {
+    const int r = (wave * C::LPA + i) * RPI + lane / C::CPR;
+    const int lc = (C::off(r, lane % C::CPR) - r * SL) >> 4;   // the swizzle is an involution
+    ga[i] = asrc + (size_t)a_src(r) * krow + lc * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < C::LPB; ++i) {
+    const int r = (wave * C::LPB + i) * RPI + lane / C::CPR;
+    const int lc = (C::off(r, lane % C::CPR) - r * SL) >> 4;
     gb[i] = wbase + (size_t)b_wrow(r) * krow + lc * 16;
   }
-  // fp8 scales: thread tid < kTM loads A-row scale tid, the rest B-row scale tid - kTM
+  // fp8 scales: scale slot s = 64 * wave + lane of each stage holds the
+  // slice's scale of A row s (s < TM), of B row s - TM (s < TM + kTN), or a
+  // copy of B row 0's (the remaining slots, never read).
   const float* gs = nullptr;
   if constexpr (FP8) {
-    if (tid < kTM) {
-      const int r = tid < rows ? tid : rows - 1;
-      const int src = MODE == 1 ? gemm1_src_row(a, gr, row0 + r) : gr.slot0 + row0 + r;
-      gs = (MODE == 1 ? a.a1s : a.a2s) + (size_t)src * nkb;
-    } else {
-      gs = wsbase + (size_t)b_wrow(tid - kTM) * nkb;
-    }
+    const int sidx = 64 * wave + lane;
+    if (sidx < TM) gs = (MODE == 1 ? a.a1s : a.a2s) + (size_t)a_src(sidx) * nkb;
+    else gs = wsbase + (size_t)b_wrow(sidx < TM + kTN ? sidx - TM : 0) * nkb;
   }
-  float rs = 0.f;                                  // fp8: scale for the next slice to issue
-  if constexpr (FP8) rs = gs[0];
 
-  f32x4 acc[4][8];
+  f32x4 acc[4][NTW];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int mval = min(4, max(0, (rows - wm * 64 + 15) >> 4));   // this wave's M tiles holding valid rows
 
 #pragma unroll
   for (int p = 0; p < NST - 1; ++p)
-    if (p < nkt) tile_issue<DT>(smem, ga, gb, p, p, wave, tid, nkt, lds_s, gs, rs);
+    if (p < nkt) tile_issue<DT, TM>(smem, ga, gb, gs, p, p, wave);
   for (int kt = 0; kt < nkt; ++kt) {
     const int st = kt % NST;
     // wait until this thread's loads of slice kt have landed; later slices may stay in flight
-    if constexpr (FP8) {
-      __builtin_amdgcn_s_waitcnt(0);
-    } else {
-      const int ahead = min(NST - 2, nkt - 1 - kt);   // slices issued after kt
-      if (ahead >= 2) wait_vmcnt<4 * LPS>();
-      else if (ahead == 1) wait_vmcnt<2 * LPS>();
-      else wait_vmcnt<0>();
-    }
-    __syncthreads();                               // everyone's slice kt is in LDS; stage (kt-1) % NST is free
-    if (kt + NST - 1 < nkt)
-      tile_issue<DT>(smem, ga, gb, kt + NST - 1, (kt + NST - 1) % NST, wave, tid, nkt, lds_s, gs, rs);
+    if (NST > 2 && kt + 1 < nkt) wait_vmcnt<C::PER_SLICE>();
+    else wait_vmcnt<0>();
+    barrier_no_fence();                            // everyone's slice kt is in LDS; stage (kt-1) % NST is free
+    if (kt + NST - 1 < nkt) tile_issue<DT, TM>(smem, ga, gb, gs, kt + NST - 1, (kt + NST - 1) % NST, wave);
     const uint8_t* la = smem + st * C::STAGE;
-    const uint8_t* lb = la + kTM * SL;
+    const uint8_t* lb = la + TM * SL;
     if constexpr (!FP8) {
       // Full tiles: all fragments of the slice are read first and the MFMAs
       // follow in the same straight-line block, so the compiler can start the
       // first half's MFMAs while the second half's reads are in flight.  Only
       // a group's last, partial tile takes the guarded path that skips M tiles.
       if (mval == 4) {
-        i32x4 fa[SL / 64][4], fb[SL / 64][8];
+        i32x4 fa[SL / 64][4], fb[SL / 64][NTW];
 #pragma unroll
         for (int fs = 0; fs < SL / 64; ++fs) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            fb[fs][j] = *reinterpret_cast<const i32x4*>(&lb[C::off(wn * 128 + j * 16 + row, fs * 4 + grp)]);
+          for (int j = 0; j < NTW; ++j)
+            fb[fs][j] = *reinterpret_cast<const i32x4*>(&lb[C::off(wn * WN + j * 16 + row, fs * 4 + grp)]);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             fa[fs][i] = *reinterpret_cast<const i32x4*>(&la[C::off(wm * 64 + i * 16 + row, fs * 4 + grp)]);
@@ -193,46 +208,47 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) F::mma(acc[i][j], fa[fs][i], fb[fs][j]);
-        // Instruction order for the scheduler: the first half's 12 reads, then
-        // the second half's 12 reads interleaved 1:2 with the first half's
+            for (int j = 0; j < NTW; ++j) F::mma(acc[i][j], fa[fs][i], fb[fs][j]);
+        // Instruction order for the scheduler: the first half's reads, then
+        // the second half's reads interleaved 1:2 with the first half's
         // MFMAs, then the rest, so LDS latency hides behind MFMAs.
         if constexpr (DT == MOE_BF16) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+          constexpr int R = 4 + NTW;                 // fragment reads per half
+          __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
 #pragma unroll
-          for (int q = 0; q < 12; ++q) {
+          for (int q = 0; q < R; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
           }
-          __builtin_amdgcn_sched_group_barrier(0x008, 40, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 8 * NTW - 2 * R, 0);
         }
       } else if (mval > 0) {
 #pragma unroll
         for (int fs = 0; fs < SL / 64; ++fs) {
-          i32x4 fb[8];
+          i32x4 fb[NTW];
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            fb[j] = *reinterpret_cast<const i32x4*>(&lb[C::off(wn * 128 + j * 16 + row, fs * 4 + grp)]);
+          for (int j = 0; j < NTW; ++j)
+            fb[j] = *reinterpret_cast<const i32x4*>(&lb[C::off(wn * WN + j * 16 + row, fs * 4 + grp)]);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (i < mval) {
               const i32x4 fa = *reinterpret_cast<const i32x4*>(&la[C::off(wm * 64 + i * 16 + row, fs * 4 + grp)]);
 #pragma unroll
-              for (int j = 0; j < 8; ++j) F::mma(acc[i][j], fa, fb[j]);
+              for (int j = 0; j < NTW; ++j) F::mma(acc[i][j], fa, fb[j]);
             }
         }
       }
     } else {
-      const float* sa_l = lds_s + st * (kTM + kTN);
-      const float* sb_l = sa_l + kTM;
-      // two halves of 4 column tiles keep the B fragments within the register budget
+      const float* sa_l = lds_s + st * C::NSC;
+      const float* sb_l = sa_l + TM;
+      // groups of 4 column tiles keep the B fragments within the register budget
 #pragma unroll
-      for (int jh = 0; jh < 2; ++jh) {
+      for (int jh = 0; jh < NTW / 4; ++jh) {
         i32x4 fb0[4], fb1[4];
         float sb[4];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const int n = wn * 128 + (4 * jh + jj) * 16 + row;
+          const int n = wn * WN + (4 * jh + jj) * 16 + row;
           fb0[jj] = *reinterpret_cast<const i32x4*>(&lb[C::off(n, grp)]);
           fb1[jj] = *reinterpret_cast<const i32x4*>(&lb[C::off(n, 4 + grp)]);
           sb[jj] = sb_l[n];
@@ -259,7 +275,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
     }
   }
 
-  // ---- epilogue: lane holds rows wm*64 + i*16 + 4*grp + q, columns wn*128 + j*16 + row
+  // ---- epilogue: lane holds rows wm*64 + i*16 + 4*grp + q, columns wn*WN + j*16 + row
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (i >= mval) break;
@@ -270,17 +286,17 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
       if (MODE == 1) {
         const size_t hrow = (size_t)(gr.slot0 + row0 + r) * a.I;
 #pragma unroll
-        for (int jp = 0; jp < 4; ++jp) {
+        for (int jp = 0; jp < NTW / 2; ++jp) {
           const float gv = acc[i][2 * jp][q], uv = acc[i][2 * jp + 1][q];
-          const int col = nt * (kTN / 2) + (4 * wn + jp) * 16 + row;
+          const int col = nt * (kTN / 2) + (wn * (NTW / 2) + jp) * 16 + row;
           if (col < a.I) store_h<DT>(a.h, hrow + col, silu(gv) * uv);
         }
       } else {
         uint8_t* ybase = gr.routed ? a.y_sorted : a.y_shared;
         const size_t yrow = (size_t)(gr.routed ? gr.slot0 + row0 + r : row0 + r) * a.H;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int col = nt * kTN + wn * 128 + j * 16 + row;
+        for (int j = 0; j < NTW; ++j) {
+          const int col = nt * kTN + wn * WN + j * 16 + row;
           if (col < a.H) store_y<DT>(ybase, yrow + col, acc[i][j][q]);
         }
       }
@@ -288,19 +304,17 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
   }
 }
 
-template <int DT, int MODE, bool SHARED>
+template <int DT, int MODE, bool SHARED, int TM>
 hipError_t launch_fat(const char* name, unsigned grid, int ntn, const Args& a, hipStream_t st) {
-  constexpr bool FP8 = DT == MOE_FP8_E4M3;
-  using C = TileCfg<DT>;
-  const size_t smem = (size_t)C::NST * C::STAGE + (FP8 ? C::NST * (kTM + kTN) * sizeof(float) : 0);
+  using C = TileCfg<DT, TM>;
   static bool attr_set = false;   // raise the dynamic-LDS limit once per process
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_fat_kernel<DT, MODE, SHARED>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_fat_kernel<DT, MODE, SHARED, TM>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  MOE_LAUNCH(name, (ffn_fat_kernel<DT, MODE, SHARED>), dim3(grid), dim3(512), smem, st, a, ntn);
+  MOE_LAUNCH(name, (ffn_fat_kernel<DT, MODE, SHARED, TM>), dim3(grid), dim3(512), C::LDS_BYTES, st, a, ntn);
   return hipGetLastError();
 }
 
@@ -310,17 +324,27 @@ namespace moe {
 namespace ffn {
 
 template <int DT>
-hipError_t launch_tiled(int mode, bool shared, unsigned grid, int ntn, const Args& a, hipStream_t st) {
-  if (mode == 1)
-    return shared ? launch_fat<DT, 1, true>("ffn_gemm1_shared_tiled", grid, ntn, a, st)
-                  : launch_fat<DT, 1, false>("ffn_gemm1_tiled", grid, ntn, a, st);
-  return shared ? launch_fat<DT, 2, true>("ffn_gemm2_shared_tiled", grid, ntn, a, st)
-                : launch_fat<DT, 2, false>("ffn_gemm2_tiled", grid, ntn, a, st);
+hipError_t launch_tiled(int mode, bool shared, int tm, unsigned grid, int ntn, const Args& a, hipStream_t st) {
+  static const char* const kName[2][2][2] = {                  // [mode - 1][shared][tm == 128]
+      {{"ffn_gemm1_tiled", "ffn_gemm1_tiled128"}, {"ffn_gemm1_shared_tiled", "ffn_gemm1_shared_tiled128"}},
+      {{"ffn_gemm2_tiled", "ffn_gemm2_tiled128"}, {"ffn_gemm2_shared_tiled", "ffn_gemm2_shared_tiled128"}}};
+  const char* name = kName[mode - 1][shared ? 1 : 0][tm == 128 ? 1 : 0];
+#define MOE_TL(M, S, TMV) launch_fat<DT, M, S, TMV>(name, grid, ntn, a, st)
+  if (tm == 256) {
+    if (mode == 1) return shared ? MOE_TL(1, true, 256) : MOE_TL(1, false, 256);
+    return shared ? MOE_TL(2, true, 256) : MOE_TL(2, false, 256);
+  }
+  if constexpr (DT == MOE_FP8_E4M3) {   // 128-row tiles serve fp8 weights only
+    if (mode == 1) return shared ? MOE_TL(1, true, 128) : MOE_TL(1, false, 128);
+    return shared ? MOE_TL(2, true, 128) : MOE_TL(2, false, 128);
+  }
+  return hipErrorInvalidValue;
+#undef MOE_TL
 }
 
-template hipError_t launch_tiled<MOE_F32>(int, bool, unsigned, int, const Args&, hipStream_t);
-template hipError_t launch_tiled<MOE_BF16>(int, bool, unsigned, int, const Args&, hipStream_t);
-template hipError_t launch_tiled<MOE_FP8_E4M3>(int, bool, unsigned, int, const Args&, hipStream_t);
+template hipError_t launch_tiled<MOE_F32>(int, bool, int, unsigned, int, const Args&, hipStream_t);
+template hipError_t launch_tiled<MOE_BF16>(int, bool, int, unsigned, int, const Args&, hipStream_t);
+template hipError_t launch_tiled<MOE_FP8_E4M3>(int, bool, int, unsigned, int, const Args&, hipStream_t);
 
 }  // namespace ffn
 }  // namespace moe

@@ -29,8 +29,8 @@ ROOT = os.path.dirname(PKG)
 KERNEL_SOURCES = {
     **{f"ffn_gemm{g}_skinny_m{m}": "ffn_skinny.hip" for g in (1, 2) for m in (8, 16, 32)},
     "ffn_gemm1_shared_skinny": "ffn_skinny.hip", "ffn_gemm2_shared_skinny": "ffn_skinny.hip",
-    "ffn_gemm1_tiled": "ffn_tiled.hip", "ffn_gemm2_tiled": "ffn_tiled.hip",
-    "ffn_gemm1_shared_tiled": "ffn_tiled.hip", "ffn_gemm2_shared_tiled": "ffn_tiled.hip", "ffn_plan": "ffn.hip",
+    **{f"ffn_gemm{g}_{s}tiled{t}": "ffn_tiled.hip" for g in (1, 2) for s in ("", "shared_") for t in ("", "128")},
+    "ffn_plan": "ffn.hip",
     "route_gate_fused": "route.hip", "route_gate_split": "route.hip", "route_reduce_select": "route.hip",
     "dispatch_count": "dispatch.hip", "dispatch_scan": "dispatch.hip", "dispatch_scatter": "dispatch.hip",
     "quant_fp8": "quant.hip", "combine": "combine.hip",
@@ -58,9 +58,10 @@ def rocprof_name(kernel: str, w_dtype: str) -> str:
         mode = int(kernel[8])
         cls = {"8": 0, "16": 1, "32": 2}[kernel.rsplit("_m", 1)[1]]
         return f"void (anonymous namespace)::ffn_skinny_kernel<{dt}, {mode}, {cls}>"
-    if kernel.startswith("ffn_gemm") and kernel.endswith("_tiled"):
+    if kernel.startswith("ffn_gemm") and "_tiled" in kernel:
         shared = "true" if "_shared_" in kernel else "false"
-        return f"void (anonymous namespace)::ffn_fat_kernel<{dt}, {int(kernel[8])}, {shared}>"
+        tm = 128 if kernel.endswith("128") else 256
+        return f"void (anonymous namespace)::ffn_fat_kernel<{dt}, {int(kernel[8])}, {shared}, {tm}>"
     if kernel.startswith("ffn_gemm") and kernel.endswith("_shared_skinny"):
         return f"void (anonymous namespace)::ffn_shared_skinny_kernel<{dt}, {int(kernel[8])}, "
     fixed = {"ffn_plan": "(anonymous namespace)::ffn_plan_kernel",
