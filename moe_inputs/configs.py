@@ -37,6 +37,8 @@ class MoEConfig:
     routing: str      # "random", "zipf" or "clusters": how the gate data is drawn
     seed: int = 0
     quant_block: int = 128   # fp8 block width along K (1 x quant_block scales)
+    n_group: int = 1         # group-limited routing: E / n_group consecutive experts per group
+    topk_group: int = 1      # groups kept eligible per token
     zipf_s: float = 1.1
     n_clusters: int = 16
     cluster_boost: float = 2.0

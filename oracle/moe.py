@@ -54,16 +54,27 @@ def to_f64(t) -> np.ndarray:
 
 # --------------------------------------------------------------------------- router
 
-def route(x, wg, bias, k: int, score: str, routed_scale: float = 1.0):
+def route(x, wg, bias, k: int, score: str, routed_scale: float = 1.0, n_group: int = 1, topk_group: int = 1):
     """Gate GEMM -> expert scoring -> selection bias -> top-k -> weights.
 
     [VLLM] "Mega-Gate" names the four steps; [PPLX] "Expert parallelism"
     requires k different experts per token and a weighted sum.
 
+    Group-limited routing ([PPLX] "MoE router": the router is shared by all
+    MoE models, Mixtral routing being the DeepSeek routing whose group holds
+    all experts).  With n_group > 1 the E experts form n_group groups of
+    E / n_group consecutive experts; a group's score is the sum of its two
+    largest selection keys; the topk_group groups of highest score (ties to
+    the lower group) stay eligible and the top-k runs over their experts
+    only.  The pages give no group scores, so the two-largest-keys sum is the
+    DeepSeek-V3 reading; n_group = 1 (or topk_group = n_group) is plain top-k.
+
     Returns a dict with ``logits`` [T,E], ``scores`` [T,E], ``keys`` [T,E],
     ``idx`` int64 [T,k] (descending key, ties to the lower expert),
-    ``w`` [T,k] and ``gap`` [T]: the smallest difference between adjacent keys
-    among the first min(k+1, E) sorted keys (a small gap marks a near tie).
+    ``w`` [T,k], ``gap`` [T]: the smallest difference between adjacent keys
+    among the first min(k+1, E) sorted eligible keys (a small gap marks a near
+    tie), and ``group_gap`` [T]: the score difference between the last chosen
+    and the first unchosen group (inf without a group stage).
     """
     x = np.asarray(x, dtype=np.float64)
     wg = np.asarray(wg, dtype=np.float64)
@@ -80,15 +91,32 @@ def route(x, wg, bias, k: int, score: str, routed_scale: float = 1.0):
     else:
         raise ValueError(f"unknown scoring {score!r}")
     keys = scores + (0.0 if bias is None else np.asarray(bias, dtype=np.float64)[None, :])
+    elig = keys
+    group_gap = np.full(T, np.inf)
+    if n_group > 1:
+        gs = E // n_group
+        if gs * n_group != E or gs < 2 or not 1 <= topk_group <= n_group or k > topk_group * gs:
+            raise ValueError("need E = n_group * g with g >= 2, 1 <= topk_group <= n_group, k <= topk_group * g")
+        top2 = np.sort(keys.reshape(T, n_group, gs), axis=2)[:, :, -2:]
+        gscore = top2[:, :, 0] + top2[:, :, 1]
+        gorder = np.argsort(-gscore, axis=1, kind="stable")       # equal scores: lower group first
+        chosen = np.zeros((T, n_group), dtype=bool)
+        np.put_along_axis(chosen, gorder[:, :topk_group], True, axis=1)
+        elig = np.where(np.repeat(chosen, gs, axis=1), keys, -np.inf)
+        if topk_group < n_group:
+            gsorted = np.take_along_axis(gscore, gorder, axis=1)
+            group_gap = gsorted[:, topk_group - 1] - gsorted[:, topk_group]
     # A stable sort of the negated keys lists equal keys by ascending index.
-    order = np.argsort(-keys, axis=1, kind="stable")
+    order = np.argsort(-elig, axis=1, kind="stable")
     idx = order[:, :k]
     nk = min(k + 1, E)
-    ks = np.take_along_axis(keys, order[:, :nk], axis=1)
-    gap = (ks[:, :-1] - ks[:, 1:]).min(axis=1) if nk > 1 else np.full(T, np.inf)
+    ks = np.take_along_axis(elig, order[:, :nk], axis=1)
+    with np.errstate(invalid="ignore"):
+        gap = (ks[:, :-1] - ks[:, 1:]).min(axis=1) if nk > 1 else np.full(T, np.inf)
+    gap = np.where(np.isnan(gap), np.inf, gap)
     sel = np.take_along_axis(scores, idx, axis=1)
     w = sel / sel.sum(axis=1, keepdims=True) * routed_scale
-    return dict(logits=logits, scores=scores, keys=keys, idx=idx, w=w, gap=gap)
+    return dict(logits=logits, scores=scores, keys=keys, idx=idx, w=w, gap=gap, group_gap=group_gap)
 
 
 # --------------------------------------------------------------------------- dispatch
@@ -232,7 +260,8 @@ def forward(inp, weights: Optional[OracleWeights] = None):
     cfg = inp.cfg
     weights = weights or OracleWeights.from_inputs(inp)
     x = to_f64(inp.x)
-    r = route(x, to_f64(inp.wg), to_f64(inp.bias), cfg.k, cfg.score)
+    r = route(x, to_f64(inp.wg), to_f64(inp.bias), cfg.k, cfg.score,
+              n_group=cfg.n_group, topk_group=cfg.topk_group)
     d = dispatch(r["idx"], cfg.E)
     xa = prepare_activations(x, weights.fp8, weights.block)
     y_sorted, y_shared = expert_ffn(xa, d["offsets"], d["sorted_pair"], cfg.k, weights)
@@ -253,7 +282,8 @@ def forward_tokens(inp, tokens, weights: Optional[OracleWeights] = None):
     weights = weights or OracleWeights.from_inputs(inp)
     tokens = np.asarray(tokens, dtype=np.int64)
     x = to_f64(inp.x[tokens.tolist()]) if len(tokens) else np.zeros((0, cfg.H))
-    r = route(x, to_f64(inp.wg), to_f64(inp.bias), cfg.k, cfg.score)
+    r = route(x, to_f64(inp.wg), to_f64(inp.bias), cfg.k, cfg.score,
+              n_group=cfg.n_group, topk_group=cfg.topk_group)
     xa = prepare_activations(x, weights.fp8, weights.block)
     y = np.zeros_like(xa)
     for e in np.unique(r["idx"]):

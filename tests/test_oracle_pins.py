@@ -342,3 +342,92 @@ def test_fp8_weights_dequantise_per_row_block():
     np.testing.assert_array_equal(dequantize_weight(inp.w2[1].numpy(), inp.w2_scale[1].numpy()),
                                   (inp.w2[1].view(torch.float8_e4m3fn).to(torch.float64)
                                    * inp.w2_scale[1].to(torch.float64).repeat_interleave(128, 1)).numpy())
+
+
+# --------------------------------------------------------------------------- group-limited routing
+
+def _sigmoid(v):
+    return 1.0 / (1.0 + math.exp(-v))
+
+
+def test_group_limited_worked_cases(golden_dir):
+    """Hand-worked cases (tests/golden/group_limited_E8_G4.json): the group
+    score is a two-largest-keys sum of the biased keys, ties go to the lower
+    group, the weights use the unbiased scores."""
+    g = _load(golden_dir, "group_limited_E8_G4.json")
+    for case in g["cases"]:
+        logits = np.array(case["logits"])[None, :]
+        bias = np.array(case["bias"], dtype=np.float64)
+        r = oracle.route(logits, np.eye(8), bias, case["k"], "sigmoid",
+                         n_group=case["n_group"], topk_group=case["topk_group"])
+        assert r["idx"][0].tolist() == case["idx"], case["name"]
+        plain = oracle.route(logits, np.eye(8), bias, case["k"], "sigmoid")
+        assert plain["idx"][0].tolist() == case["plain_idx"], case["name"]
+        s = [_sigmoid(case["logits"][e]) for e in case["idx"]]
+        np.testing.assert_allclose(r["w"][0], np.array(s) / sum(s), rtol=1e-12)
+
+
+def _brute_force_group_route(keys, n_group, topk_group, k):
+    """Every topk_group-subset of groups; the one with the largest total of
+    group scores (two largest keys each), the lexicographically smallest on
+    ties; then the k largest eligible keys, smaller index first on ties."""
+    E = len(keys)
+    gs = E // n_group
+    gscore = []
+    for gi in range(n_group):
+        best = second = -math.inf
+        for e in range(gi * gs, (gi + 1) * gs):
+            if keys[e] > best:
+                best, second = keys[e], best
+            elif keys[e] > second:
+                second = keys[e]
+        gscore.append(best + second)
+    best_set, best_total = None, -math.inf
+    for subset in itertools.combinations(range(n_group), topk_group):
+        total = sum(gscore[gi] for gi in subset)
+        if total > best_total:
+            best_set, best_total = subset, total
+    elig = [e for e in range(E) if e // gs in best_set]
+    return sorted(elig, key=lambda e: (-keys[e], e))[:k]
+
+
+@pytest.mark.parametrize("E,n_group,topk_group,k", [(8, 4, 2, 3), (12, 3, 1, 2), (16, 4, 3, 5), (16, 8, 2, 4)])
+def test_group_limited_matches_brute_force(E, n_group, topk_group, k):
+    rng = np.random.default_rng(E * 100 + n_group * 10 + topk_group)
+    T, H = 40, 6
+    x = rng.standard_normal((T, H))
+    wg = rng.standard_normal((E, H))
+    bias = rng.uniform(-0.2, 0.2, E)
+    r = oracle.route(x, wg, bias, k, "sigmoid", n_group=n_group, topk_group=topk_group)
+    keys = 1.0 / (1.0 + np.exp(-(x @ wg.T))) + bias
+    for t in range(T):
+        assert r["idx"][t].tolist() == _brute_force_group_route(keys[t].tolist(), n_group, topk_group, k)
+
+
+def test_group_limited_all_groups_is_plain_topk():
+    """topk_group = n_group keeps every expert eligible (the Mixtral case):
+    the group stage runs and must change nothing."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((50, 10))
+    wg = rng.standard_normal((32, 10))
+    bias = rng.uniform(-0.1, 0.1, 32)
+    for score in ("sigmoid", "softmax"):
+        plain = oracle.route(x, wg, bias, 6, score)
+        for n_group in (2, 4, 8, 16):
+            r = oracle.route(x, wg, bias, 6, score, n_group=n_group, topk_group=n_group)
+            np.testing.assert_array_equal(r["idx"], plain["idx"])
+            np.testing.assert_array_equal(r["w"], plain["w"])
+
+
+def test_group_limited_invariants():
+    rng = np.random.default_rng(11)
+    E, n_group, topk_group, k = 64, 8, 3, 8
+    x = rng.standard_normal((100, 12))
+    wg = rng.standard_normal((E, 12))
+    r = oracle.route(x, wg, None, k, "sigmoid", n_group=n_group, topk_group=topk_group)
+    gs = E // n_group
+    for t in range(100):
+        groups = set(int(e) // gs for e in r["idx"][t])
+        assert len(groups) <= topk_group
+        assert len(set(r["idx"][t].tolist())) == k
+    assert np.all(r["group_gap"] >= 0)
