@@ -65,8 +65,17 @@ typedef struct {
                           MOE_FP8_E4M3 (act BF16) */
   int32_t quant_block; /* FP8 block width along K: 128; ignored otherwise */
   float routed_scale;  /* multiplies the renormalised combine weights (1.0) */
-  int32_t n_group;     /* group-limited routing: only n_group = topk_group = 1 */
-  int32_t topk_group;
+  int32_t n_group;     /* group-limited routing (Perplexity, "Lower latency and higher throughput with
+                          multi-node DeepSeek deployment", section "MoE router": Mixtral routing is the
+                          DeepSeek routing whose group holds all experts).  The E experts form n_group
+                          groups of E / n_group consecutive experts; a group's score is the sum of its
+                          two largest selection keys (score + bias; the pages give no group score, this
+                          is the DeepSeek-V3 reading); the top-k runs over the experts of the topk_group
+                          best groups (ties to the lower group).  n_group = 1 or topk_group = n_group:
+                          plain top-k.  Needs E % n_group == 0, E / n_group >= 2, n_group <= 64
+                          (UNSUPPORTED above), 1 <= topk_group <= n_group and
+                          k <= topk_group * E / n_group (INVALID_ARG otherwise). */
+  int32_t topk_group;  /* groups kept eligible per token */
 } moe_cfg;
 
 /* Expert weights.  Routed: w13 [E, 2I, H] (rows [0,I) = gate projection W1,

@@ -115,7 +115,8 @@ def make_cfg(T, H, E, k, I, I_shared, score="sigmoid", act_dtype="bf16", w_dtype
 def cfg_from(c) -> MoeCfg:
     """MoeCfg from any object with the layer's fields (T, H, E, k, I, I_shared, score, act_dtype, w_dtype)."""
     return make_cfg(c.T, c.H, c.E, c.k, c.I, c.I_shared, c.score, c.act_dtype, c.w_dtype,
-                    getattr(c, "quant_block", 128))
+                    getattr(c, "quant_block", 128), n_group=getattr(c, "n_group", 1),
+                    topk_group=getattr(c, "topk_group", 1))
 
 
 def workspace_size(cfg: MoeCfg) -> int:

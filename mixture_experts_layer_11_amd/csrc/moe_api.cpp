@@ -56,8 +56,16 @@ int check_cfg(const moe_cfg* c) {
   if (c->k > 32) return fail(MOE_ERR_UNSUPPORTED, "k = %d > 32", c->k);
   if (c->I_shared != 0 && c->I_shared != c->I)
     return fail(MOE_ERR_UNSUPPORTED, "shared-expert width %d differs from I = %d", c->I_shared, c->I);
-  if (c->n_group != 1 || c->topk_group != 1)
-    return fail(MOE_ERR_UNSUPPORTED, "group-limited routing (n_group %d, topk_group %d)", c->n_group, c->topk_group);
+  if (c->n_group < 1 || c->topk_group < 1 || c->topk_group > c->n_group)
+    return fail(MOE_ERR_INVALID_ARG, "need 1 <= topk_group (%d) <= n_group (%d)", c->topk_group, c->n_group);
+  if (c->n_group > 1) {
+    if (c->E % c->n_group) return fail(MOE_ERR_INVALID_ARG, "E = %d not a multiple of n_group = %d", c->E, c->n_group);
+    const int gs = c->E / c->n_group;
+    if (gs < 2) return fail(MOE_ERR_INVALID_ARG, "groups of one expert have no two-key score");
+    if (c->k > c->topk_group * gs)
+      return fail(MOE_ERR_INVALID_ARG, "k = %d above the %d experts of %d groups", c->k, c->topk_group * gs, c->topk_group);
+    if (c->n_group > 64) return fail(MOE_ERR_UNSUPPORTED, "n_group = %d > 64", c->n_group);
+  }
   const bool f32 = c->act_dtype == MOE_F32 && c->w_dtype == MOE_F32;
   const bool bf16 = c->act_dtype == MOE_BF16 && c->w_dtype == MOE_BF16;
   const bool fp8 = c->act_dtype == MOE_BF16 && c->w_dtype == MOE_FP8_E4M3;

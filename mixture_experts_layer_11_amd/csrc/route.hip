@@ -30,6 +30,7 @@ struct RouteOut {
   float* w;            // [T, k]
   int E, k, score;
   float rscale;
+  int n_group, topk_group;   // group-limited routing; n_group = 1: plain top-k
 };
 
 // Scores, keys, top-k and weights for one token whose logits sit in the
@@ -60,11 +61,47 @@ __device__ void route_token(const float (&lg)[4], int t, const RouteOut& o) {
     for (int c = 0; c < 4; ++c) sc[c] = 1.0f / (1.0f + expf(-lg[c]));
   }
   uint64_t key[4];
+  float kv[4];                                    // selection keys score + bias (-inf past E)
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int e = lane + 64 * c;
     const float b = (o.bias && valid[c]) ? o.bias[e] : 0.f;
-    key[c] = valid[c] ? (((uint64_t)f32_order_key(sc[c] + b) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e)) : 0ull;
+    kv[c] = valid[c] ? sc[c] + b : -INFINITY;
+    key[c] = valid[c] ? (((uint64_t)f32_order_key(kv[c]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e)) : 0ull;
+  }
+  if (o.n_group > 1 && o.topk_group < o.n_group) {
+    // Group-limited routing: lane g < n_group scores group g (experts
+    // g*gs .. g*gs+gs-1) by the sum of its two largest keys, gathered with
+    // shuffles; topk_group rounds of a wave arg-max pick the groups (ties to
+    // the lower group); experts of other groups drop out of the top-k.
+    const int gs = o.E / o.n_group;
+    const int gl = lane < o.n_group ? lane : o.n_group - 1;
+    float b1 = -INFINITY, b2 = -INFINITY;
+    for (int i = 0; i < gs; ++i) {
+      const int e = gl * gs + i;
+      const int src = e & 63, slot = e >> 6;
+      const float v0 = __shfl(kv[0], src, 64), v1 = __shfl(kv[1], src, 64);
+      const float v2 = __shfl(kv[2], src, 64), v3 = __shfl(kv[3], src, 64);
+      const float v = slot == 0 ? v0 : slot == 1 ? v1 : slot == 2 ? v2 : v3;
+      if (v > b1) {
+        b2 = b1;
+        b1 = v;
+      } else if (v > b2) {
+        b2 = v;
+      }
+    }
+    uint64_t gkey = lane < o.n_group
+                        ? (((uint64_t)f32_order_key(b1 + b2) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)lane))
+                        : 0ull;
+    uint64_t chosen = 0;                          // bit g: group g stays eligible
+    for (int j = 0; j < o.topk_group; ++j) {
+      const uint64_t best = wave_max_u64(gkey);
+      chosen |= 1ull << (0xFFFFFFFFu - (uint32_t)best);
+      if (gkey == best) gkey = 0ull;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (valid[c] && !((chosen >> ((lane + 64 * c) / gs)) & 1ull)) key[c] = 0ull;
   }
   float wsum = 0.f, my_s = 0.f;
   int my_e = 0;
@@ -260,7 +297,7 @@ static void launch_gate(const moe_cfg& c, dim3 grid, const uint8_t* xb, const ui
 
 hipError_t launch_route(const moe_cfg& c, const void* x, const void* wg, const float* bias, int32_t* idx,
                         float* w, float* part, hipStream_t st) {
-  RouteOut o{bias, idx, w, c.E, c.k, c.score, c.routed_scale};
+  RouteOut o{bias, idx, w, c.E, c.k, c.score, c.routed_scale, c.n_group, c.topk_group};
   const int tiles = ceil_div(c.T, kTokTile);
   const int s = route_splits(c);
   dim3 grid(tiles, s);

@@ -73,8 +73,10 @@ def route(x, wg, bias, k: int, score: str, routed_scale: float = 1.0, n_group: i
     ``idx`` int64 [T,k] (descending key, ties to the lower expert),
     ``w`` [T,k], ``gap`` [T]: the smallest difference between adjacent keys
     among the first min(k+1, E) sorted eligible keys (a small gap marks a near
-    tie), and ``group_gap`` [T]: the score difference between the last chosen
-    and the first unchosen group (inf without a group stage).
+    tie), ``group_gap`` [T]: the score difference between the last chosen
+    and the first unchosen group (inf without a group stage), ``elig`` [T,E]:
+    the keys with the experts of unchosen groups at -inf, and
+    ``group_scores`` [T, n_group] (None without a group stage).
     """
     x = np.asarray(x, dtype=np.float64)
     wg = np.asarray(wg, dtype=np.float64)
@@ -93,6 +95,7 @@ def route(x, wg, bias, k: int, score: str, routed_scale: float = 1.0, n_group: i
     keys = scores + (0.0 if bias is None else np.asarray(bias, dtype=np.float64)[None, :])
     elig = keys
     group_gap = np.full(T, np.inf)
+    gscore = None
     if n_group > 1:
         gs = E // n_group
         if gs * n_group != E or gs < 2 or not 1 <= topk_group <= n_group or k > topk_group * gs:
@@ -116,7 +119,8 @@ def route(x, wg, bias, k: int, score: str, routed_scale: float = 1.0, n_group: i
     gap = np.where(np.isnan(gap), np.inf, gap)
     sel = np.take_along_axis(scores, idx, axis=1)
     w = sel / sel.sum(axis=1, keepdims=True) * routed_scale
-    return dict(logits=logits, scores=scores, keys=keys, idx=idx, w=w, gap=gap, group_gap=group_gap)
+    return dict(logits=logits, scores=scores, keys=keys, elig=elig, idx=idx, w=w, gap=gap,
+                group_gap=group_gap, group_scores=gscore, n_group=n_group, topk_group=topk_group)
 
 
 # --------------------------------------------------------------------------- dispatch

@@ -56,20 +56,33 @@ def assert_outputs_close(gpu, ref, key, what="output"):
 
 def compare_routing(gpu_idx, gpu_w, oracle_route, k):
     """Returns (n_near_tie, mismatched_tokens).  Asserts exact indices on
-    non-near-tie tokens and weights within WEIGHT_RTOL where indices agree."""
+    non-near-tie tokens and weights within WEIGHT_RTOL where indices agree.
+    A token is a near tie when two of its first k+1 eligible keys, or (with
+    group-limited routing) the last chosen and the first unchosen group
+    scores, lie within NEAR_TIE; there the GPU's choice must be a valid one."""
     gi = to_np(gpu_idx).astype(np.int64)
     gw = to_np(gpu_w).astype(np.float64)
     oi = oracle_route["idx"]
-    near = oracle_route["gap"] < NEAR_TIE
+    near_g = oracle_route["group_gap"] < NEAR_TIE
+    near = (oracle_route["gap"] < NEAR_TIE) | near_g
     same = (gi == oi).all(axis=1)
     bad = np.nonzero(~same & ~near)[0]
     assert len(bad) == 0, f"{len(bad)} tokens route differently without a near tie, first {bad[:8]}"
-    # near-tie tokens: the GPU choice must be a valid top-k within the tie gap
-    keys = oracle_route["keys"]
+    elig = oracle_route["elig"]
     for t in np.nonzero(near & ~same)[0]:
-        chosen = keys[t, gi[t]]
-        kth = np.sort(keys[t])[::-1][k - 1]
         assert len(set(gi[t].tolist())) == k
+        if near_g[t]:
+            # groups: each chosen expert's group scores within NEAR_TIE of the
+            # last chosen group; at most topk_group groups
+            gsc = oracle_route["group_scores"][t]
+            ng, tg = oracle_route["n_group"], oracle_route["topk_group"]
+            gs = len(elig[t]) // ng
+            last = np.sort(gsc)[::-1][tg - 1]
+            groups = set((gi[t] // gs).tolist())
+            assert len(groups) <= tg and all(gsc[g] >= last - NEAR_TIE for g in groups), f"token {t}: invalid groups"
+            continue
+        chosen = elig[t, gi[t]]
+        kth = np.sort(elig[t])[::-1][k - 1]
         assert chosen.min() >= kth - NEAR_TIE, f"token {t}: invalid near-tie choice"
         assert np.all(np.diff(chosen) <= NEAR_TIE)
     if same.any():

@@ -88,7 +88,8 @@ def _route_check(cfg, x, wg, bias):
     mc = moe.cfg_from(cfg)
     idx, w = moe.moe_route(mc, x.to(DEV), wg.to(DEV), bias.to(DEV))
     torch.cuda.synchronize()
-    r = oracle.route(oracle.to_f64(x), oracle.to_f64(wg), oracle.to_f64(bias), cfg.k, cfg.score)
+    r = oracle.route(oracle.to_f64(x), oracle.to_f64(wg), oracle.to_f64(bias), cfg.k, cfg.score,
+                     n_group=cfg.n_group, topk_group=cfg.topk_group)
     near, mism = compare_routing(idx, w, r, cfg.k)
     _log(f"[route {cfg.name}] T={cfg.T} near-ties={near} differing near-tie tokens={len(mism)}")
     return idx, w, r
@@ -106,6 +107,47 @@ def test_route_full_size(name):
     cfg = get_config(name)
     x, wg, bias = make_router_inputs(cfg, DEV)
     _route_check(cfg, x.cpu(), wg.cpu(), bias.cpu())
+
+
+# Group-limited routing: DeepSeek-V3-like groups (256 experts in 8 groups,
+# 4 kept) on the split-K router, a prefill-sized call on the fused router,
+# softmax scoring in fp32, and the all-groups case.
+GROUPED = {
+    "groups_e256_g8_t4": get_config("decode16").with_(name="groups_e256_g8_t4", T=64, H=1024, n_group=8,
+                                                     topk_group=4),
+    "groups_e32_g4_t2_fused": get_config("prefill8192_ep8").with_(name="groups_e32_g4_t2_fused", n_group=4,
+                                                                  topk_group=2),
+    "groups_e16_g4_t2_f32": get_config("tiny_f32").with_(name="groups_e16_g4_t2_f32", T=37, n_group=4,
+                                                          topk_group=2, k=3),
+    "groups_all_e64": get_config("decode16").with_(name="groups_all_e64", T=40, H=512, E=64, n_group=8,
+                                                   topk_group=8),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GROUPED))
+def test_route_group_limited(name):
+    cfg = GROUPED[name]
+    x, wg, bias = make_router_inputs(cfg, "cpu")
+    idx, _, r = _route_check(cfg, x, wg, bias)
+    gs = cfg.E // cfg.n_group
+    groups = to_np(idx).astype(np.int64) // gs
+    assert max(len(set(row.tolist())) for row in groups) <= cfg.topk_group
+    if cfg.topk_group < cfg.n_group:
+        plain = oracle.route(oracle.to_f64(x), oracle.to_f64(wg), oracle.to_f64(bias), cfg.k, cfg.score)
+        assert (plain["idx"] != r["idx"]).any(), "the group stage changed nothing: a weak test case"
+
+
+def test_forward_group_limited():
+    cfg = get_config("decode16").with_(name="forward_groups", T=48, H=512, E=32, k=4, I=256, I_shared=256,
+                                       n_group=8, topk_group=2)
+    inp, gin = _small_inputs(cfg)
+    ref = oracle.forward(inp)
+    y, idx, w, counts = moe.moe_forward(moe.cfg_from(cfg), gin.x, gin.wg, gin.bias, moe.Weights.from_inputs(gin),
+                                        return_routing=True)
+    torch.cuda.synchronize()
+    _, mism = compare_routing(idx, w, ref["route"], cfg.k)
+    keep = np.setdiff1d(np.arange(cfg.T), mism)
+    assert_outputs_close(to_np(y)[keep], ref["y"][keep], tol_key(cfg), "y")
 
 
 # ------------------------------------------------------------------ dispatch
