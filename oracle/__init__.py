@@ -17,6 +17,7 @@ from .moe import (  # noqa: F401
     forward_tokens,
     prepare_activations,
     route,
+    routing_stats,
     swiglu_ffn,
     to_f64,
 )

@@ -242,6 +242,46 @@ def expert_ffn(xa, offsets, sorted_pair, k: int, weights: OracleWeights):
     return y_sorted, y_shared
 
 
+# --------------------------------------------------------------------------- routing statistics
+
+def routing_stats(idx, E: int, n_ranks: int):
+    """Per-expert load, load skew and the expert affinity matrix of one batch.
+
+    The GRACE-MoE summary in the pages (section "Expert Grouping") builds an
+    expert affinity matrix A from activation patterns and drives replication
+    by the load skew rho = W_max / W_mean of the group loads (section "Expert
+    Replication").  Readings: A[i][j] is the number of tokens routed to both
+    experts i and j (A = M^T M for the T x E routing incidence matrix M, so
+    the diagonal holds the per-expert loads); the groups are n_ranks equal
+    ranges of consecutive experts (expert-parallel ranks).  Written as plain
+    loops over tokens and expert pairs.
+
+    Returns counts [E], rank_load [n_ranks], rho_rank, rho_expert (the skew
+    with one group per expert) and affinity [E, E] (int64).
+    """
+    idx = np.asarray(idx, dtype=np.int64)
+    T, k = idx.shape
+    if E % n_ranks:
+        raise ValueError("need E divisible by n_ranks")
+    counts = np.zeros(E, dtype=np.int64)
+    affinity = np.zeros((E, E), dtype=np.int64)
+    for t in range(T):
+        for a in range(k):
+            counts[idx[t, a]] += 1
+            for b in range(k):
+                affinity[idx[t, a], idx[t, b]] += 1
+    per = E // n_ranks
+    rank_load = np.zeros(n_ranks, dtype=np.int64)
+    for r in range(n_ranks):
+        for e in range(r * per, (r + 1) * per):
+            rank_load[r] += counts[e]
+    P = T * k
+    rho_rank = rank_load.max() / (P / n_ranks) if P else 0.0
+    rho_expert = counts.max() / (P / E) if P else 0.0
+    return dict(counts=counts, rank_load=rank_load, rho_rank=float(rho_rank), rho_expert=float(rho_expert),
+                affinity=affinity)
+
+
 # --------------------------------------------------------------------------- combine
 
 def combine(y_sorted, y_shared, pair_slot, w, k: int):

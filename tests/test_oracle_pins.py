@@ -431,3 +431,42 @@ def test_group_limited_invariants():
         assert len(groups) <= topk_group
         assert len(set(r["idx"][t].tolist())) == k
     assert np.all(r["group_gap"] >= 0)
+
+
+# --------------------------------------------------------------------------- routing statistics
+
+def test_routing_stats_worked_case(golden_dir):
+    g = _load(golden_dir, "routing_stats_T3_E4_k2.json")
+    r = oracle.routing_stats(np.array(g["idx"]), g["E"], g["n_ranks"])
+    assert r["counts"].tolist() == g["counts"]
+    assert r["affinity"].tolist() == g["affinity"]
+    assert r["rank_load"].tolist() == g["rank_load"]
+    assert r["rho_rank"] == pytest.approx(g["rho_rank"], rel=1e-15)
+    assert r["rho_expert"] == pytest.approx(g["rho_expert"], rel=1e-15)
+
+
+def test_routing_stats_closed_form_and_invariants():
+    """A = M^T M for the T x E routing incidence matrix M (a matrix product
+    against the oracle's loops); symmetric, diagonal = loads, row sums =
+    k * loads, total = T k^2; skews at least 1."""
+    rng = np.random.default_rng(5)
+    T, E, k, D = 300, 32, 6, 4
+    idx = np.argsort(rng.random((T, E)), axis=1)[:, :k]
+    r = oracle.routing_stats(idx, E, D)
+    M = np.zeros((T, E), dtype=np.int64)
+    M[np.arange(T)[:, None], idx] = 1
+    A = r["affinity"]
+    np.testing.assert_array_equal(A, M.T @ M)
+    np.testing.assert_array_equal(A, A.T)
+    np.testing.assert_array_equal(np.diag(A), r["counts"])
+    np.testing.assert_array_equal(A.sum(axis=1), k * r["counts"])
+    assert A.sum() == T * k * k
+    np.testing.assert_array_equal(r["rank_load"], r["counts"].reshape(D, -1).sum(axis=1))
+    assert r["rho_rank"] >= 1 and r["rho_expert"] >= r["rho_rank"] - 1e-12
+
+
+def test_routing_stats_balanced_routing_has_unit_skew():
+    T, E, k = 64, 16, 4
+    idx = (np.arange(T)[:, None] * k + np.arange(k)[None, :]) % E     # every expert k*T/E times
+    r = oracle.routing_stats(idx, E, 4)
+    assert r["rho_rank"] == 1.0 and r["rho_expert"] == 1.0
