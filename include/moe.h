@@ -163,6 +163,24 @@ int moe_forward(const moe_cfg* cfg, const void* x, const void* w_gate, const flo
                 const moe_weights* w, void* y, int32_t* topk_idx_out, float* topk_w_out,
                 int32_t* counts_out, void* ws, size_t ws_bytes, void* hip_stream);
 
+/* Routing statistics of one batch (the GRACE-MoE summary in the pages:
+ * section "Expert Grouping" builds an expert affinity matrix from activation
+ * patterns, section "Expert Replication" the load skew rho = W_max / W_mean
+ * of the group loads).  Groups are n_ranks ranges of E / n_ranks consecutive
+ * experts (expert-parallel ranks).
+ *   topk_idx   [T, k] int32 (from moe_route); entries outside [0, E) are skipped
+ *   counts     [E] int32 out: pairs routed to each expert (NULL to skip)
+ *   rank_load  [n_ranks] int32 out: pairs routed to each rank's experts (NULL to skip)
+ *   skew       [2] fp32 out: {max rank load, max expert load} divided by the
+ *              mean load T*k/n_ranks, T*k/E; 0 when T*k = 0 (NULL to skip)
+ *   affinity   [E, E] int32 out: tokens routed to both i and j; the diagonal
+ *              holds counts (NULL to skip)
+ * Needs 1 <= n_ranks, E % n_ranks == 0 (INVALID_ARG).  Integer results are
+ * exact and order-independent; T = 0 enqueues nothing and leaves the outputs
+ * untouched.  No workspace. */
+int moe_routing_stats(const moe_cfg* cfg, const int32_t* topk_idx, int32_t n_ranks, int32_t* counts,
+                      int32_t* rank_load, float* skew, int32_t* affinity, void* hip_stream);
+
 /* ---- Per-kernel timing (measurement tools; not part of the layer).
  * Between moe_profile_start(only) and moe_profile_stop(), every kernel the
  * library launches (or, when `only` is not NULL, every kernel of that name)

@@ -27,6 +27,7 @@ from .binding import (  # noqa: F401
     moe_profile_stop,
     moe_quantize_fp8,
     moe_route,
+    moe_routing_stats,
     status_str,
     workspace_size,
 )

@@ -21,8 +21,8 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = range(2)
 
 EXPORTS = ("moe_status_str", "moe_last_error", "moe_workspace_size", "moe_route", "moe_dispatch",
-           "moe_quantize_fp8", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_profile_start",
-           "moe_profile_stop")
+           "moe_quantize_fp8", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_routing_stats",
+           "moe_profile_start", "moe_profile_stop")
 
 
 class MoELibraryMissing(RuntimeError):
@@ -77,6 +77,7 @@ def load_library(path: str = LIB_PATH):
     lib.moe_expert_ffn.argtypes = [cfgp, P, P, P, wp, P, P, P, SZ, P]
     lib.moe_combine.argtypes = [cfgp, P, P, P, P, P, P]
     lib.moe_forward.argtypes = [cfgp, P, P, P, wp, P, P, P, P, P, SZ, P]
+    lib.moe_routing_stats.argtypes = [cfgp, P, I32, P, P, P, P, P]
     lib.moe_profile_start.argtypes = [ctypes.c_char_p]
     lib.moe_profile_stop.argtypes = [P, I32, ctypes.POINTER(I32)]
     for name in EXPORTS[2:]:
@@ -185,6 +186,21 @@ def moe_route(cfg: MoeCfg, x, w_gate, sel_bias=None, ws=None, topk_idx=None, top
     _check(lib.moe_route(ctypes.byref(cfg), _ptr(x), _ptr(w_gate), _ptr(sel_bias), _ptr(topk_idx), _ptr(topk_w),
                          _ptr(ws), ws.numel(), _stream(stream)))
     return topk_idx, topk_w
+
+
+def moe_routing_stats(cfg: MoeCfg, topk_idx, n_ranks: int = 1, affinity: bool = True, stream=None):
+    """Per-expert load, per-rank load, skews and (optionally) the expert
+    affinity matrix of one routing.  Returns (counts [E], rank_load
+    [n_ranks], skew [2] fp32, affinity [E, E] or None)."""
+    lib = load_library()
+    dev = topk_idx.device
+    counts = _out((cfg.E,), torch.int32, dev)
+    rank_load = _out((n_ranks,), torch.int32, dev)
+    skew = _out((2,), torch.float32, dev)
+    aff = _out((cfg.E, cfg.E), torch.int32, dev) if affinity else None
+    _check(lib.moe_routing_stats(ctypes.byref(cfg), _ptr(topk_idx), int(n_ranks), _ptr(counts), _ptr(rank_load),
+                                 _ptr(skew), _ptr(aff), _stream(stream)))
+    return counts, rank_load, skew, aff
 
 
 def moe_dispatch(cfg: MoeCfg, topk_idx, ws=None, stream=None):

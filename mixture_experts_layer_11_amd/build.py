@@ -14,7 +14,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["moe_api.cpp", "profile.cpp", "streams.cpp", "route.hip", "dispatch.hip", "quant.hip", "ffn.hip",
-           "ffn_skinny.hip", "ffn_tiled.hip", "combine.hip"]
+           "ffn_skinny.hip", "ffn_tiled.hip", "combine.hip",
+           "stats.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

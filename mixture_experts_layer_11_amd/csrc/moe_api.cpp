@@ -232,6 +232,19 @@ int moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, int32_t* counts, i
   return e == hipSuccess ? ok() : hip_fail(e, "moe_dispatch");
 }
 
+int moe_routing_stats(const moe_cfg* cfg, const int32_t* topk_idx, int32_t n_ranks, int32_t* counts,
+                      int32_t* rank_load, float* skew, int32_t* affinity, void* hip_stream) {
+  int s = check_cfg(cfg);
+  if (s) return s;
+  if (n_ranks < 1 || cfg->E % n_ranks)
+    return fail(MOE_ERR_INVALID_ARG, "n_ranks = %d does not divide E = %d", n_ranks, cfg->E);
+  if (cfg->T == 0) return ok();
+  NEED_PTR(topk_idx);
+  hipError_t e = moe::launch_routing_stats(*cfg, topk_idx, n_ranks, counts, rank_load, skew, affinity,
+                                           static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "moe_routing_stats");
+}
+
 int moe_quantize_fp8(int32_t rows, int32_t cols, int32_t block, const void* in, int32_t in_dtype, uint8_t* codes,
                      float* scales, void* hip_stream) {
   if (rows < 0 || cols < 0) return fail(MOE_ERR_INVALID_ARG, "negative shape");

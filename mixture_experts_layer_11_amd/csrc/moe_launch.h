@@ -69,6 +69,10 @@ struct SideStream {
 };
 hipError_t side_stream(SideStream* out);
 
+// ---- routing statistics
+hipError_t launch_routing_stats(const moe_cfg& c, const int32_t* idx, int n_ranks, int32_t* counts,
+                                int32_t* rank_load, float* skew, int32_t* affinity, hipStream_t st);
+
 // ---- combine
 hipError_t launch_combine(const moe_cfg& c, const void* y_sorted, const void* y_shared,
                           const int32_t* pair_slot, const float* topk_w, void* y, hipStream_t st);

@@ -150,6 +150,40 @@ def test_forward_group_limited():
     assert_outputs_close(to_np(y)[keep], ref["y"][keep], tol_key(cfg), "y")
 
 
+# ------------------------------------------------------------------ routing statistics
+
+@pytest.mark.parametrize("name,n_ranks", [("decode16", 8), ("decode256", 8), ("prefill8192_ep8", 4),
+                                          ("clustered2048_fp8", 16), ("tiny_f32", 1)])
+def test_routing_stats_exact(name, n_ranks):
+    """Loads, skews and the affinity matrix of the oracle's own routing of
+    each workload (the input is the oracle's top-k, so GPU routing near ties
+    do not enter): integers bit-exact, skews to fp32 rounding."""
+    cfg = get_config(name)
+    x, wg, bias = make_router_inputs(cfg, "cpu")
+    r = oracle.route(oracle.to_f64(x), oracle.to_f64(wg), oracle.to_f64(bias), cfg.k, cfg.score)
+    ref = oracle.routing_stats(r["idx"], cfg.E, n_ranks)
+    idx = torch.from_numpy(r["idx"].astype(np.int32)).to(DEV)
+    counts, rank_load, skew, aff = moe.moe_routing_stats(moe.cfg_from(cfg), idx, n_ranks)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(counts), ref["counts"])
+    np.testing.assert_array_equal(to_np(rank_load), ref["rank_load"])
+    np.testing.assert_array_equal(to_np(aff), ref["affinity"])
+    np.testing.assert_allclose(to_np(skew), [ref["rho_rank"], ref["rho_expert"]], rtol=2e-7)
+    _log(f"[stats {name}] rho over {n_ranks} ranks {ref['rho_rank']:.3f}, over experts {ref['rho_expert']:.3f}")
+
+
+def test_routing_stats_skips_out_of_range_and_optional_outputs():
+    cfg = get_config("tiny_f32").with_(T=5, k=2, E=16)
+    idx = torch.tensor([[0, 1], [2, 3], [-1, 4], [16, 5], [6, 7]], dtype=torch.int32, device=DEV)
+    counts, rank_load, skew, aff = moe.moe_routing_stats(moe.cfg_from(cfg), idx, 2, affinity=False)
+    torch.cuda.synchronize()
+    assert aff is None
+    expect = np.zeros(16, dtype=np.int64)
+    expect[:8] = 1                       # -1 and 16 are skipped
+    np.testing.assert_array_equal(to_np(counts), expect)
+    np.testing.assert_array_equal(to_np(rank_load), [8, 0])
+
+
 # ------------------------------------------------------------------ dispatch
 
 def _distinct_topk(rng, T, E, k):
