@@ -238,6 +238,37 @@ def main(argv=None):
     layer_gbps = layer["bytes"] / (ms_per_step * 1e-3) / 1e9
     layer_tflops = layer["flops"] / (ms_per_step * 1e-3) / 1e12
 
+    # beside the timed steps: the same step captured once as a HIP graph
+    # (moe_graph_capture) and replayed K times, which removes the host launch
+    # cost of the ~15-20 kernels per step
+    graph = moe.MoEGraph(mc, inp.x, inp.wg, inp.bias, w, y, ws)
+    for _ in range(args.warmup):
+        graph.launch()
+    torch.cuda.synchronize()
+    g0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.launch()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - g0) * 1e3 / args.steps
+    graph.close()
+    graph_line = {"ms_per_step": round(graph_ms, 4), "tokens_per_s": round(cfg.T / (graph_ms * 1e-3), 1),
+                  "eager_minus_graph_us": round((ms_per_step - graph_ms) * 1e3, 2)}
+
+    # beside the layer, outside the timed steps: routing statistics of this
+    # batch (loads over 8 expert-parallel ranks when E allows, skews, affinity)
+    n_ranks = 8 if cfg.E % 8 == 0 else 1
+    moe.moe_routing_stats(mc, idx, n_ranks)
+    torch.cuda.synchronize()
+    moe.moe_profile_start()
+    for _ in range(5):
+        _, _, skew, _ = moe.moe_routing_stats(mc, idx, n_ranks)
+    torch.cuda.synchronize()
+    sp = moe.moe_profile_stop()
+    stat_us = {n: round(v[1] / max(v[0], 1) * 1e3, 2) for n, v in sorted(sp.items())}
+    skew_h = skew.cpu().tolist()
+    routing_stats = {"n_ranks": n_ranks, "rho_rank": round(skew_h[0], 4), "rho_expert": round(skew_h[1], 4),
+                     "us_per_call": round(sum(stat_us.values()), 2), "kernels_us": stat_us}
+
     cpu = None
     if not (args.no_cpu_baseline or args.quick):
         n = min(args.cpu_tokens, cfg.T)
@@ -268,6 +299,8 @@ def main(argv=None):
                   "hbm_frac": round(layer_gbps / HBM_PEAK_GBPS, 4), "TFLOPs": round(layer_tflops, 2),
                   "gpu_event_ms_per_step": round(gpu_ms / args.steps, 4)},
         "kernels": {n: kernel_line(n, v, models) for n, v in sorted(breakdown.items())},
+        "graph": graph_line,
+        "routing_stats": routing_stats,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -163,6 +163,29 @@ int moe_forward(const moe_cfg* cfg, const void* x, const void* w_gate, const flo
                 const moe_weights* w, void* y, int32_t* topk_idx_out, float* topk_w_out,
                 int32_t* counts_out, void* ws, size_t ws_bytes, void* hip_stream);
 
+/* Graph of one whole-layer call (Perplexity, "Lower latency and higher
+ * throughput with multi-node DeepSeek deployment", section "Quantization",
+ * MoE-router paragraph: one graph is captured per batch size, so the
+ * kernels read the per-expert token counts on the device).
+ * moe_graph_capture first runs moe_forward once on hip_stream (validating
+ * the arguments exactly as moe_forward does, writing its outputs, and
+ * creating the per-device state made on first use), then captures the same
+ * call on a private stream and instantiates it.  The graph keeps the
+ * pointers it was captured with: each moe_graph_launch runs the whole layer
+ * on the current contents of x, w_gate, sel_bias and the weights, into the
+ * same y / routing outputs / workspace, on hip_stream (ordered like any
+ * other work on it).  Routings may differ between launches; T, the shapes
+ * and the buffers may not.  Launches of one graph must not overlap (they
+ * share the workspace).  Capture allocates the graph (host and device
+ * resources); launch allocates nothing.  *out is NULL on failure; T = 0 is
+ * INVALID_ARG.  Do not capture while moe_profile_start() is on. */
+typedef struct moe_graph moe_graph;
+int moe_graph_capture(const moe_cfg* cfg, const void* x, const void* w_gate, const float* sel_bias,
+                      const moe_weights* w, void* y, int32_t* topk_idx_out, float* topk_w_out,
+                      int32_t* counts_out, void* ws, size_t ws_bytes, void* hip_stream, moe_graph** out);
+int moe_graph_launch(const moe_graph* g, void* hip_stream);
+int moe_graph_destroy(moe_graph* g);   /* NULL is a no-op */
+
 /* Routing statistics of one batch (the GRACE-MoE summary in the pages:
  * section "Expert Grouping" builds an expert affinity matrix from activation
  * patterns, section "Expert Replication" the load skew rho = W_max / W_mean

@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     EXPORTS,
     MoeCfg,
     MoEError,
+    MoEGraph,
     MoELibraryMissing,
     Weights,
     alloc_workspace,

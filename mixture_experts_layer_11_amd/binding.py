@@ -21,8 +21,8 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = range(2)
 
 EXPORTS = ("moe_status_str", "moe_last_error", "moe_workspace_size", "moe_route", "moe_dispatch",
-           "moe_quantize_fp8", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_routing_stats",
-           "moe_profile_start", "moe_profile_stop")
+           "moe_quantize_fp8", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_graph_capture",
+           "moe_graph_launch", "moe_graph_destroy", "moe_routing_stats", "moe_profile_start", "moe_profile_stop")
 
 
 class MoELibraryMissing(RuntimeError):
@@ -78,6 +78,9 @@ def load_library(path: str = LIB_PATH):
     lib.moe_combine.argtypes = [cfgp, P, P, P, P, P, P]
     lib.moe_forward.argtypes = [cfgp, P, P, P, wp, P, P, P, P, P, SZ, P]
     lib.moe_routing_stats.argtypes = [cfgp, P, I32, P, P, P, P, P]
+    lib.moe_graph_capture.argtypes = [cfgp, P, P, P, wp, P, P, P, P, P, SZ, P, ctypes.POINTER(P)]
+    lib.moe_graph_launch.argtypes = [P, P]
+    lib.moe_graph_destroy.argtypes = [P]
     lib.moe_profile_start.argtypes = [ctypes.c_char_p]
     lib.moe_profile_stop.argtypes = [P, I32, ctypes.POINTER(I32)]
     for name in EXPORTS[2:]:
@@ -262,6 +265,37 @@ def moe_forward(cfg: MoeCfg, x, w_gate, sel_bias, weights: Weights, ws=None, y=N
     _check(lib.moe_forward(ctypes.byref(cfg), _ptr(x), _ptr(w_gate), _ptr(sel_bias), ctypes.byref(w), _ptr(y),
                            _ptr(idx), _ptr(wt), _ptr(counts), _ptr(ws), ws.numel(), _stream(stream)))
     return (y, idx, wt, counts) if return_routing else y
+
+
+class MoEGraph:
+    """One captured whole-layer call (moe_graph_capture): every launch runs
+    the layer on the current contents of the tensors it was captured with,
+    into the same outputs.  The tensors stay referenced while it lives."""
+
+    def __init__(self, cfg: MoeCfg, x, w_gate, sel_bias, weights: Weights, y, ws, topk_idx=None, topk_w=None,
+                 counts=None, stream=None):
+        lib = load_library()
+        self._keep = (cfg, x, w_gate, sel_bias, weights, y, ws, topk_idx, topk_w, counts)
+        self._w = weights.c_struct()
+        h = ctypes.c_void_p()
+        _check(lib.moe_graph_capture(ctypes.byref(cfg), _ptr(x), _ptr(w_gate), _ptr(sel_bias), ctypes.byref(self._w),
+                                     _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(ws), ws.numel(),
+                                     _stream(stream), ctypes.byref(h)))
+        self._h = h
+
+    def launch(self, stream=None):
+        _check(load_library().moe_graph_launch(self._h, _stream(stream)))
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _check(load_library().moe_graph_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def moe_profile_start(only: Optional[str] = None):

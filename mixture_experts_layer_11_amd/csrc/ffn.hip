@@ -148,10 +148,11 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st) {
     const int N = mode == 1 ? c.I : c.H;
     const long long items = N / ((mode == 1 ? 4 : 8) * kSkNT);   // skinny items per group
     for (int cls = 0; cls < 3; ++cls) {
-      // a group of class cls has at least 1, 9 or 17 rows
+      // a group of class cls has at least 1, 9 or 17 rows, and no group has
+      // more than T rows (a token picks k distinct experts)
       const int min_rows = cls == 0 ? 1 : (4 << cls) + 1;
       const int groups = P / min_rows < c.E ? P / min_rows : c.E;
-      if (groups == 0) continue;
+      if (groups == 0 || min_rows > c.T) continue;
       const unsigned grid = (unsigned)((moe::ceil_div(groups * items, 4LL) + 7) & ~7LL);   // 4 items per workgroup
       if ((e = launch_skinny<DT>(mode, cls, grid, a, st)) != hipSuccess) return e;
     }

@@ -9,6 +9,8 @@
 #include <string.h>
 
 #include "../../include/moe.h"
+#include <new>
+
 #include "moe_launch.h"
 
 namespace {
@@ -332,6 +334,62 @@ int moe_forward(const moe_cfg* cfg, const void* x, const void* w_gate, const flo
   e = moe::launch_combine(*cfg, ys, ysh, slot, wt, y, st);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/combine");
   return ok();
+}
+
+struct moe_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+int moe_graph_capture(const moe_cfg* cfg, const void* x, const void* w_gate, const float* sel_bias,
+                      const moe_weights* w, void* y, int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
+                      void* ws, size_t ws_bytes, void* hip_stream, moe_graph** out) {
+  if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (cfg && cfg->T == 0) return fail(MOE_ERR_INVALID_ARG, "T = 0: nothing to capture");
+  // One eager call: validates the arguments and creates the per-device
+  // state that is made on first use (side stream, kernel attributes).
+  int s = moe_forward(cfg, x, w_gate, sel_bias, w, y, topk_idx_out, topk_w_out, counts_out, ws, ws_bytes, hip_stream);
+  if (s) return s;
+  hipStream_t cs;
+  hipError_t e = moe::capture_stream(&cs);
+  if (e != hipSuccess) return hip_fail(e, "moe_graph_capture/stream");
+  if ((e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal)) != hipSuccess)
+    return hip_fail(e, "moe_graph_capture/begin");
+  s = moe_forward(cfg, x, w_gate, sel_bias, w, y, topk_idx_out, topk_w_out, counts_out, ws, ws_bytes, cs);
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(cs, &g);
+  if (s || e != hipSuccess) {
+    if (g) (void)hipGraphDestroy(g);
+    return s ? s : hip_fail(e, "moe_graph_capture/end");
+  }
+  hipGraphExec_t ex = nullptr;
+  if ((e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0)) != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return hip_fail(e, "moe_graph_capture/instantiate");
+  }
+  *out = new (std::nothrow) moe_graph{g, ex};
+  if (!*out) {
+    (void)hipGraphExecDestroy(ex);
+    (void)hipGraphDestroy(g);
+    return fail(MOE_ERR_HIP, "moe_graph_capture: out of host memory");
+  }
+  return ok();
+}
+
+int moe_graph_launch(const moe_graph* g, void* hip_stream) {
+  if (!g) return fail(MOE_ERR_INVALID_ARG, "graph is NULL");
+  hipError_t e = hipGraphLaunch(g->exec, static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? ok() : hip_fail(e, "moe_graph_launch");
+}
+
+int moe_graph_destroy(moe_graph* g) {
+  if (!g) return ok();
+  hipError_t e1 = hipGraphExecDestroy(g->exec);
+  hipError_t e2 = hipGraphDestroy(g->graph);
+  delete g;
+  if (e1 != hipSuccess) return hip_fail(e1, "moe_graph_destroy");
+  return e2 == hipSuccess ? ok() : hip_fail(e2, "moe_graph_destroy");
 }
 
 }  // extern "C"

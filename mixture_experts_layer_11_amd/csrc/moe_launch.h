@@ -68,6 +68,7 @@ struct SideStream {
   int cus;          // compute units of the device
 };
 hipError_t side_stream(SideStream* out);
+hipError_t capture_stream(hipStream_t* out);   // private stream for graph capture
 
 // ---- routing statistics
 hipError_t launch_routing_stats(const moe_cfg& c, const int32_t* idx, int n_ranks, int32_t* counts,

@@ -33,4 +33,20 @@ hipError_t side_stream(SideStream* out) {
   return hipSuccess;
 }
 
+// A private non-blocking stream per host thread and device, on which graphs
+// are captured (a capture must start on a stream that is not the legacy
+// default stream, and capturing on a private one leaves the caller's stream
+// free).
+hipError_t capture_stream(hipStream_t* out) {
+  thread_local std::vector<hipStream_t> per_device;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if ((int)per_device.size() <= dev) per_device.resize(dev + 1, nullptr);
+  if (!per_device[dev] && (e = hipStreamCreateWithFlags(&per_device[dev], hipStreamNonBlocking)) != hipSuccess)
+    return e;
+  *out = per_device[dev];
+  return hipSuccess;
+}
+
 }  // namespace moe

@@ -138,3 +138,27 @@ def test_binding_raises_typed_errors():
     with pytest.raises(moe.MoEError) as ei:
         moe.workspace_size(_cfg(k=0))
     assert ei.value.status == B.MOE_ERR_INVALID_ARG
+
+
+def test_graph_entry_points_validate_before_any_hip_call():
+    lib = moe.load_library()
+    cfg = _cfg()
+    _, need = _ws_status(cfg)
+    fake = 1 << 20
+    h = ctypes.c_void_p(123)
+    w = B.MoeWeights()
+    # no output handle
+    assert lib.moe_graph_capture(ctypes.byref(cfg), fake, fake, None, ctypes.byref(w), fake, None, None, None, fake,
+                                 need, None, None) == B.MOE_ERR_INVALID_ARG
+    # T = 0: nothing to capture; the handle is cleared
+    zero = _cfg(T=0)
+    assert lib.moe_graph_capture(ctypes.byref(zero), fake, fake, None, ctypes.byref(w), fake, None, None, None, fake,
+                                 need, None, ctypes.byref(h)) == B.MOE_ERR_INVALID_ARG
+    assert not h.value
+    # argument errors surface from the eager call's validation, before any launch
+    assert lib.moe_graph_capture(ctypes.byref(cfg), None, fake, None, ctypes.byref(w), fake, None, None, None, fake,
+                                 need, None, ctypes.byref(h)) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_graph_capture(ctypes.byref(_cfg(k=0)), fake, fake, None, ctypes.byref(w), fake, None, None, None,
+                                 fake, need, None, ctypes.byref(h)) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_graph_launch(None, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_graph_destroy(None) == B.MOE_OK

@@ -314,6 +314,56 @@ def test_forward_on_user_stream_is_ordered():
         assert_outputs_close(to_np(y)[keep], ref["y"][keep], tol_key(cfg), "y")
 
 
+@pytest.mark.parametrize("name", ["tiny_f32", "small_bf16", "t24_bf16", "small_fp8"])
+def test_graph_replays_match_eager(name):
+    """A captured whole-layer graph, replayed several times with eager work
+    and synchronisations in between, gives the eager result bit for bit
+    (the layer is deterministic), and follows a change of routing: the
+    per-expert counts are read on the device at every launch."""
+    cfg = SMALL[name]
+    inp, gin = _small_inputs(cfg)
+    mc = moe.cfg_from(cfg)
+    w = moe.Weights.from_inputs(gin)
+    y_ref = moe.moe_forward(mc, gin.x, gin.wg, gin.bias, w)
+    torch.cuda.synchronize()
+    x = gin.x.clone()
+    ws = moe.alloc_workspace(mc)
+    y = torch.empty_like(y_ref)
+    g = moe.MoEGraph(mc, x, gin.wg, gin.bias, w, y, ws)
+    for rep in range(3):
+        y.zero_()
+        g.launch()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), f"replay {rep}"
+        scratch = moe.moe_forward(mc, gin.x, gin.wg, gin.bias, w)     # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(scratch, y_ref)
+    # new routing: the graph must equal an eager call on the new input
+    x.copy_(torch.roll(gin.x, 1, dims=1))
+    y_new = moe.moe_forward(mc, x, gin.wg, gin.bias, w)
+    g.launch()
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_new)
+    assert not torch.equal(y_new, y_ref)
+    g.close()
+
+
+def test_graph_full_size_decode16():
+    cfg = get_config("decode16")
+    gin = make_inputs(cfg, DEV)
+    mc = moe.cfg_from(cfg)
+    w = moe.Weights.from_inputs(gin)
+    y_ref = moe.moe_forward(mc, gin.x, gin.wg, gin.bias, w)
+    ws = moe.alloc_workspace(mc)
+    y = torch.empty_like(y_ref)
+    g = moe.MoEGraph(mc, gin.x, gin.wg, gin.bias, w, y, ws)
+    for _ in range(3):
+        g.launch()
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
+    g.close()
+
+
 def test_zero_input_gives_zero_output():
     cfg = SMALL["small_bf16"]
     _, gin = _small_inputs(cfg)
