@@ -148,6 +148,7 @@ def main(argv=None):
     ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quick", action="store_true", help="no CPU baseline (tuning sweeps)")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay measurement (profiled runs)")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -241,18 +242,20 @@ def main(argv=None):
     # beside the timed steps: the same step captured once as a HIP graph
     # (moe_graph_capture) and replayed K times, which removes the host launch
     # cost of the ~15-20 kernels per step
-    graph = moe.MoEGraph(mc, inp.x, inp.wg, inp.bias, w, y, ws)
-    for _ in range(args.warmup):
-        graph.launch()
-    torch.cuda.synchronize()
-    g0 = time.perf_counter()
-    for _ in range(args.steps):
-        graph.launch()
-    torch.cuda.synchronize()
-    graph_ms = (time.perf_counter() - g0) * 1e3 / args.steps
-    graph.close()
-    graph_line = {"ms_per_step": round(graph_ms, 4), "tokens_per_s": round(cfg.T / (graph_ms * 1e-3), 1),
-                  "eager_minus_graph_us": round((ms_per_step - graph_ms) * 1e3, 2)}
+    graph_line = None
+    if not args.no_graph:
+        graph = moe.MoEGraph(mc, inp.x, inp.wg, inp.bias, w, y, ws)
+        for _ in range(args.warmup):
+            graph.launch()
+        torch.cuda.synchronize()
+        g0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.launch()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - g0) * 1e3 / args.steps
+        graph.close()
+        graph_line = {"ms_per_step": round(graph_ms, 4), "tokens_per_s": round(cfg.T / (graph_ms * 1e-3), 1),
+                      "eager_minus_graph_us": round((ms_per_step - graph_ms) * 1e3, 2)}
 
     # beside the layer, outside the timed steps: routing statistics of this
     # batch (loads over 8 expert-parallel ranks when E allows, skews, affinity)

@@ -37,6 +37,33 @@ __global__ __launch_bounds__(256) void affinity_kernel(const int32_t* __restrict
   }
 }
 
+// E <= 128: each workgroup counts a range of tokens into a private LDS copy
+// of the matrix (E*E ints <= 64 KB) and adds its non-zero entries to the
+// global one, so the atomics on hot entries mostly stay on chip.
+constexpr int kAffLdsMaxE = 128;
+
+__global__ __launch_bounds__(256) void affinity_lds_kernel(const int32_t* __restrict__ idx, int T, int k, int E,
+                                                           int tokens_per_wg, int32_t* __restrict__ A) {
+  extern __shared__ int loc[];
+  const int n = E * E;
+  for (int i = threadIdx.x; i < n; i += 256) loc[i] = 0;
+  __syncthreads();
+  const long long t0 = (long long)blockIdx.x * tokens_per_wg;
+  const long long t1 = min((long long)T, t0 + tokens_per_wg);
+  for (long long p = t0 * k + threadIdx.x; p < t1 * k; p += 256) {
+    const long long t = p / k;
+    const int ea = idx[p];
+    if (ea < 0 || ea >= E) continue;
+    for (int b = 0; b < k; ++b) {
+      const int eb = idx[t * k + b];
+      if (eb >= 0 && eb < E) atomicAdd(&loc[ea * E + eb], 1);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += 256)
+    if (loc[i]) atomicAdd(&A[i], loc[i]);
+}
+
 // One workgroup: LDS histogram of the pairs, then rank loads and skews.
 __global__ __launch_bounds__(1024) void loads_kernel(const int32_t* __restrict__ idx, int P, int E, int n_ranks,
                                                      int32_t* counts, int32_t* rank_load, float* skew) {
@@ -88,8 +115,15 @@ hipError_t launch_routing_stats(const moe_cfg& c, const int32_t* idx, int n_rank
                affinity, n);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    MOE_LAUNCH("stats_affinity", affinity_kernel, dim3((unsigned)ceil_div(P, 256LL)), dim3(256), 0, st, idx, c.T, c.k,
-               c.E, affinity);
+    if (c.E <= kAffLdsMaxE) {
+      const int wgs = ceil_div(c.T, 64) < 512 ? ceil_div(c.T, 64) : 512;    // >= 64 tokens per workgroup
+      const int per = ceil_div(c.T, wgs);
+      MOE_LAUNCH("stats_affinity", affinity_lds_kernel, dim3(wgs), dim3(256), (size_t)c.E * c.E * sizeof(int), st,
+                 idx, c.T, c.k, c.E, per, affinity);
+    } else {
+      MOE_LAUNCH("stats_affinity", affinity_kernel, dim3((unsigned)ceil_div(P, 256LL)), dim3(256), 0, st, idx, c.T,
+                 c.k, c.E, affinity);
+    }
     return hipGetLastError();
   }
   return hipSuccess;
