@@ -17,6 +17,8 @@ Names say what each workload is:
 * ``clustered2048_fp8`` 2048 tokens, 256 experts, fp8 E4M3 expert weights with
                       1x128 fp32 block scales, routing logits boosted inside
                       16 clusters of 16 experts.
+* ``decode16_fp8``, ``decode256_fp8``  the decode shapes with fp8 E4M3 expert
+                      weights in the pages' 128 x 128 scale tiles.
 """
 
 from dataclasses import dataclass, replace
@@ -36,7 +38,8 @@ class MoEConfig:
     w_dtype: str      # "f32", "bf16" or "fp8": expert weights
     routing: str      # "random", "zipf" or "clusters": how the gate data is drawn
     seed: int = 0
-    quant_block: int = 128   # fp8 block width along K (1 x quant_block scales)
+    quant_block: int = 128   # fp8 block width along K
+    w_block_rows: int = 1    # fp8 weight scale block height: 1 (1 x 128 blocks) or 128 (128 x 128 tiles)
     n_group: int = 1         # group-limited routing: E / n_group consecutive experts per group
     topk_group: int = 1      # groups kept eligible per token
     zipf_s: float = 1.1
@@ -66,6 +69,9 @@ CONFIGS = {
     "clustered2048_fp8": MoEConfig("clustered2048_fp8", T=2048,
                                    **{**_DS, "w_dtype": "fp8",
                                       "routing": "clusters"}),
+    # the decode shapes with the pages' fp8 scheme: 128 x 128 weight tiles
+    "decode16_fp8": MoEConfig("decode16_fp8", T=16, **{**_DS, "w_dtype": "fp8"}, w_block_rows=128),
+    "decode256_fp8": MoEConfig("decode256_fp8", T=256, **{**_DS, "w_dtype": "fp8"}, w_block_rows=128),
 }
 
 

@@ -69,19 +69,21 @@ def _normal(shape, std, device, seed, tensor, expert=0) -> torch.Tensor:
     return t
 
 
-def quantize_weight_fp8(w: torch.Tensor, block: int = 128):
-    """Static 1 x ``block`` fp8 E4M3 quantisation of a [N, K] fp32 weight.
+def quantize_weight_fp8(w: torch.Tensor, block: int = 128, block_rows: int = 1):
+    """Static fp8 E4M3 quantisation of a [N, K] fp32 weight in blocks of
+    ``block_rows`` x ``block`` (1 x 128 or 128 x 128): scale = amax / 448 of
+    the block (1 for an all-zero block), codes = e4m3(w / scale).
 
-    Returns (codes uint8 [N, K], scales fp32 [N, K // block]).
+    Returns (codes uint8 [N, K], scales fp32 [N // block_rows, K // block]).
     """
     n, kdim = w.shape
-    assert kdim % block == 0
-    wb = w.view(n, kdim // block, block)
-    amax = wb.abs().amax(dim=2)
+    assert kdim % block == 0 and n % block_rows == 0
+    wb = w.view(n // block_rows, block_rows, kdim // block, block)
+    amax = wb.abs().amax(dim=(1, 3))                                   # [N/br, K/b]
     scale = amax / 448.0
     scale = torch.where(amax == 0, torch.ones_like(scale), scale)
-    q = (wb / scale.unsqueeze(2)).clamp_(-448.0, 448.0)
-    codes = q.to(torch.float8_e4m3fn).view(torch.uint8).view(n, kdim)
+    q = (wb / scale[:, None, :, None]).clamp_(-448.0, 448.0)
+    codes = q.to(torch.float8_e4m3fn).view(torch.uint8).reshape(n, kdim)
     return codes, scale.contiguous()
 
 
@@ -109,7 +111,7 @@ def _expert_weights(cfg: MoEConfig, device, tensor: str, e: int, rows: int, cols
                     fan_in: int, w_out: torch.Tensor, s_out: Optional[torch.Tensor]):
     w = _normal((rows, cols), fan_in ** -0.5, device, cfg.seed, tensor, e)
     if cfg.w_dtype == "fp8":
-        codes, scale = quantize_weight_fp8(w, cfg.quant_block)
+        codes, scale = quantize_weight_fp8(w, cfg.quant_block, cfg.w_block_rows)
         w_out.copy_(codes)
         s_out.copy_(scale)
     else:
@@ -163,8 +165,9 @@ def make_inputs(cfg: MoEConfig, device="cpu") -> MoEInputs:
     qb = cfg.quant_block
     w13 = torch.empty((E, 2 * I, H), dtype=wdt, device=device)
     w2 = torch.empty((E, H, I), dtype=wdt, device=device)
-    w13_s = torch.empty((E, 2 * I, H // qb), dtype=torch.float32, device=device) if fp8 else None
-    w2_s = torch.empty((E, H, I // qb), dtype=torch.float32, device=device) if fp8 else None
+    br = cfg.w_block_rows
+    w13_s = torch.empty((E, 2 * I // br, H // qb), dtype=torch.float32, device=device) if fp8 else None
+    w2_s = torch.empty((E, H // br, I // qb), dtype=torch.float32, device=device) if fp8 else None
     for e in range(E):
         _expert_weights(cfg, device, "w13", e, 2 * I, H, H, w13[e], w13_s[e] if fp8 else None)
         _expert_weights(cfg, device, "w2", e, H, I, I, w2[e], w2_s[e] if fp8 else None)
@@ -173,8 +176,8 @@ def make_inputs(cfg: MoEConfig, device="cpu") -> MoEInputs:
     if Is > 0:
         ws13 = torch.empty((2 * Is, H), dtype=wdt, device=device)
         ws2 = torch.empty((H, Is), dtype=wdt, device=device)
-        ws13_s = torch.empty((2 * Is, H // qb), dtype=torch.float32, device=device) if fp8 else None
-        ws2_s = torch.empty((H, Is // qb), dtype=torch.float32, device=device) if fp8 else None
+        ws13_s = torch.empty((2 * Is // br, H // qb), dtype=torch.float32, device=device) if fp8 else None
+        ws2_s = torch.empty((H // br, Is // qb), dtype=torch.float32, device=device) if fp8 else None
         _expert_weights(cfg, device, "ws13", 0, 2 * Is, H, H, ws13, ws13_s)
         _expert_weights(cfg, device, "ws2", 0, H, Is, Is, ws2, ws2_s)
 

@@ -85,9 +85,13 @@ def quantize_rows_fp8(a, block: int = 128):
 _DECODE_TABLE = e4m3_decode(np.arange(256, dtype=np.uint8))
 
 
-def dequantize_weight(codes, scales, block: int = 128) -> np.ndarray:
-    """[N, K] E4M3 codes with [N, K // block] fp32 scales -> fp64 values."""
+def dequantize_weight(codes, scales, block: int = 128, block_rows: int = 1) -> np.ndarray:
+    """[N, K] E4M3 codes with fp32 scales -> fp64 values: code value times the
+    scale of its block of ``block_rows`` x ``block`` (row r, column c use
+    scales[r // block_rows, c // block]).  block_rows = 1 is one scale per row
+    per block; 128 is the 128 x 128 weight tiles of [PPLX] "Quantization"."""
     codes = np.asarray(codes, dtype=np.uint8)
     n, kdim = codes.shape
-    s = np.asarray(scales, dtype=np.float64).reshape(n, kdim // block)
-    return (_DECODE_TABLE[codes].reshape(n, kdim // block, block) * s[:, :, None]).reshape(n, kdim)
+    s = np.asarray(scales, dtype=np.float64).reshape(n // block_rows, kdim // block)
+    s_rows = np.repeat(s, block_rows, axis=0)                        # [N, K // block]
+    return (_DECODE_TABLE[codes].reshape(n, kdim // block, block) * s_rows[:, :, None]).reshape(n, kdim)

@@ -160,7 +160,8 @@ class OracleWeights:
     """fp64 expert weights, produced one expert at a time.
 
     ``expert(e)`` and ``shared()`` return (W1 [I,H], W3 [I,H], W2 [H,I]); the
-    fp8 variants are dequantised as code value times the 1 x 128 block scale.
+    fp8 variants are dequantised as code value times the scale of its
+    block_rows x 128 block (1 x 128 or 128 x 128).
     """
     E: int
     expert: Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray]]
@@ -173,11 +174,12 @@ class OracleWeights:
         cfg = inp.cfg
         fp8 = cfg.w_dtype == "fp8"
         blk = cfg.quant_block
+        brows = getattr(cfg, "w_block_rows", 1)
 
         def split(w13, w2, s13=None, s2=None):
             if fp8:
-                w13f = dequantize_weight(w13.cpu().numpy(), s13.cpu().numpy(), blk)
-                w2f = dequantize_weight(w2.cpu().numpy(), s2.cpu().numpy(), blk)
+                w13f = dequantize_weight(w13.cpu().numpy(), s13.cpu().numpy(), blk, brows)
+                w2f = dequantize_weight(w2.cpu().numpy(), s2.cpu().numpy(), blk, brows)
             else:
                 w13f, w2f = to_f64(w13), to_f64(w2)
             i = w13f.shape[0] // 2

@@ -470,3 +470,24 @@ def test_routing_stats_balanced_routing_has_unit_skew():
     idx = (np.arange(T)[:, None] * k + np.arange(k)[None, :]) % E     # every expert k*T/E times
     r = oracle.routing_stats(idx, E, 4)
     assert r["rho_rank"] == 1.0 and r["rho_expert"] == 1.0
+
+
+# --------------------------------------------------------------------------- 128 x 128 fp8 weight tiles
+
+def test_dequantize_weight_128x128_tiles():
+    """Each value is its code (decoded by torch's float8_e4m3fn, a library
+    independent of the oracle's table) times the scale of its 128 x 128 tile:
+    checked element by element with explicit loops; and 1 x 128 scales that
+    repeat a tile's scale on all its rows give the same values."""
+    rng = np.random.default_rng(3)
+    n, kdim = 256, 384
+    codes = rng.integers(0, 256, (n, kdim), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0                    # no NaN codes
+    scales = rng.uniform(0.5, 2.0, (n // 128, kdim // 128))
+    v = dequantize_weight(codes, scales, 128, 128)
+    dec = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for r in range(0, n, 7):
+        for c in range(kdim):
+            assert v[r, c] == dec[r, c] * scales[r // 128, c // 128]
+    per_row = np.repeat(scales, 128, axis=0)
+    np.testing.assert_array_equal(dequantize_weight(codes, per_row, 128, 1), v)
