@@ -52,8 +52,9 @@ def kernel_models(cfg, counts):
     a1b = 1 if fp8 else ab
     a2b = 1 if fp8 else hb_out
     qb = cfg.quant_block
-    sc13 = (2 * I * H // qb) * 4 if fp8 else 0
-    sc2 = (H * I // qb) * 4 if fp8 else 0
+    br = getattr(cfg, "w_block_rows", 1)
+    sc13 = (2 * I // br) * (H // qb) * 4 if fp8 else 0
+    sc2 = (H // br) * (I // qb) * 4 if fp8 else 0
     groups = [int(c) for c in counts]
     regions = ("skinny_m8", "skinny_m16", "skinny_m32", "tiled", "tiled128", "shared_skinny", "shared_tiled",
                "shared_tiled128")

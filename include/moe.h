@@ -76,13 +76,16 @@ typedef struct {
                           (UNSUPPORTED above), 1 <= topk_group <= n_group and
                           k <= topk_group * E / n_group (INVALID_ARG otherwise). */
   int32_t topk_group;  /* groups kept eligible per token */
+  int32_t w_block_rows; /* FP8 weight scale blocks: 1 (one scale per row per quant_block columns)
+                           or 128 (128 x 128 tiles, Perplexity, "Quantization"); ignored otherwise */
 } moe_cfg;
 
 /* Expert weights.  Routed: w13 [E, 2I, H] (rows [0,I) = gate projection W1,
  * rows [I,2I) = up projection W3), w2 [E, H, I].  Shared: ws13 [2I, H],
  * ws2 [H, I] (NULL when I_shared == 0).  For MOE_FP8_E4M3 the *_scale arrays
- * hold one fp32 scale per row per quant_block columns ([.., rows, cols/128]);
- * the value of a weight is e4m3(code) * scale.  Scales are NULL otherwise. */
+ * hold one fp32 scale per block of w_block_rows rows x quant_block columns
+ * ([.., rows / w_block_rows, cols / 128]); the value of weight (r, c) is
+ * e4m3(code) * scale[r / w_block_rows][c / 128].  Scales are NULL otherwise. */
 typedef struct {
   const void* w13;
   const float* w13_scale;

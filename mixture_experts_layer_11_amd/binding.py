@@ -39,7 +39,8 @@ class MoeCfg(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("I", ctypes.c_int32), ("I_shared", ctypes.c_int32), ("score", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32), ("quant_block", ctypes.c_int32),
-                ("routed_scale", ctypes.c_float), ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32)]
+                ("routed_scale", ctypes.c_float), ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
+                ("w_block_rows", ctypes.c_int32)]
 
 
 class MoeKernelTime(ctypes.Structure):
@@ -109,18 +110,18 @@ _SCORE = {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}
 
 
 def make_cfg(T, H, E, k, I, I_shared, score="sigmoid", act_dtype="bf16", w_dtype="bf16", quant_block=128,
-             routed_scale=1.0, n_group=1, topk_group=1) -> MoeCfg:
+             routed_scale=1.0, n_group=1, topk_group=1, w_block_rows=1) -> MoeCfg:
     return MoeCfg(int(T), int(H), int(E), int(k), int(I), int(I_shared), _SCORE[score] if isinstance(score, str) else score,
                   _DT[act_dtype] if isinstance(act_dtype, str) else act_dtype,
                   _DT[w_dtype] if isinstance(w_dtype, str) else w_dtype, int(quant_block), float(routed_scale),
-                  int(n_group), int(topk_group))
+                  int(n_group), int(topk_group), int(w_block_rows))
 
 
 def cfg_from(c) -> MoeCfg:
     """MoeCfg from any object with the layer's fields (T, H, E, k, I, I_shared, score, act_dtype, w_dtype)."""
     return make_cfg(c.T, c.H, c.E, c.k, c.I, c.I_shared, c.score, c.act_dtype, c.w_dtype,
                     getattr(c, "quant_block", 128), n_group=getattr(c, "n_group", 1),
-                    topk_group=getattr(c, "topk_group", 1))
+                    topk_group=getattr(c, "topk_group", 1), w_block_rows=getattr(c, "w_block_rows", 1))
 
 
 def workspace_size(cfg: MoeCfg) -> int:

@@ -32,6 +32,7 @@ struct Args {
   const float* w2s;
   const uint8_t* ws2;
   const float* ws2s;
+  int wsr_shift;                // fp8 weight scales: row r uses scale row r >> wsr_shift (0: 1 x 128, 7: 128 x 128)
   uint8_t* h;                   // GEMM1 out [P+T, I]
   const uint8_t* a2;            // GEMM2 A rows: h or fp8 codes of h, [P+T, I]
   const float* a2s;             // fp8: h scales [P+T, I/qb]

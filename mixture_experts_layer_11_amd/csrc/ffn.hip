@@ -237,6 +237,7 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const void* x, const int32_t* off
   a.w2s = w.w2_scale;
   a.ws2 = static_cast<const uint8_t*>(w.ws2);
   a.ws2s = w.ws2_scale;
+  a.wsr_shift = c.w_dtype == MOE_FP8_E4M3 && c.w_block_rows == 128 ? 7 : 0;
   a.h = static_cast<uint8_t*>(ws.h);
   a.y_sorted = static_cast<uint8_t*>(y_sorted);
   a.y_shared = static_cast<uint8_t*>(y_shared);

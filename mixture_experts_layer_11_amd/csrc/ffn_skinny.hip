@@ -68,10 +68,10 @@ __device__ __forceinline__ void skinny_pass(const Args& a, const Group& gr, int 
   const float* wsbase = nullptr;
   if (MODE == 1) {
     wbase = gr.routed ? a.w13 + (size_t)g * 2 * a.I * krow : a.ws13;
-    if (FP8) wsbase = gr.routed ? a.w13s + (size_t)g * 2 * a.I * nwin : a.ws13s;
+    if (FP8) wsbase = gr.routed ? a.w13s + (size_t)g * ((2 * a.I) >> a.wsr_shift) * nwin : a.ws13s;
   } else {
     wbase = gr.routed ? a.w2 + (size_t)g * a.H * krow : a.ws2;
-    if (FP8) wsbase = gr.routed ? a.w2s + (size_t)g * a.H * nwin : a.ws2s;
+    if (FP8) wsbase = gr.routed ? a.w2s + (size_t)g * (a.H >> a.wsr_shift) * nwin : a.ws2s;
   }
   // tile j of this pass -> tile index in the item (GEMM1: first half gate, second half up)
   int wrow[NTP];
@@ -159,7 +159,7 @@ __device__ __forceinline__ void skinny_pass(const Args& a, const Group& gr, int 
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) av[u][mt] = ld16(pa[mt] + off);
 #pragma unroll
-        for (int j = 0; j < NTP; ++j) sw[u][j] = wsbase[(size_t)wrow[j] * nwin + wu];
+        for (int j = 0; j < NTP; ++j) sw[u][j] = wsbase[(size_t)(wrow[j] >> a.wsr_shift) * nwin + wu];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll

@@ -122,10 +122,10 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
   const float* wsbase = nullptr;
   if (MODE == 1) {
     wbase = gr.routed ? a.w13 + (size_t)g * 2 * a.I * krow : a.ws13;
-    if (FP8) wsbase = gr.routed ? a.w13s + (size_t)g * 2 * a.I * nkb : a.ws13s;
+    if (FP8) wsbase = gr.routed ? a.w13s + (size_t)g * ((2 * a.I) >> a.wsr_shift) * nkb : a.ws13s;
   } else {
     wbase = gr.routed ? a.w2 + (size_t)g * a.H * krow : a.ws2;
-    if (FP8) wsbase = gr.routed ? a.w2s + (size_t)g * a.H * nkb : a.ws2s;
+    if (FP8) wsbase = gr.routed ? a.w2s + (size_t)g * (a.H >> a.wsr_shift) * nkb : a.ws2s;
   }
   // Weight row held by LDS B row n; columns past N (a partial last column
   // tile) are clamped to the last valid row and never stored.
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
   if constexpr (FP8) {
     const int sidx = 64 * wave + lane;
     if (sidx < TM) gs = (MODE == 1 ? a.a1s : a.a2s) + (size_t)a_src(sidx) * nkb;
-    else gs = wsbase + (size_t)b_wrow(sidx < TM + kTN ? sidx - TM : 0) * nkb;
+    else gs = wsbase + (size_t)(b_wrow(sidx < TM + kTN ? sidx - TM : 0) >> a.wsr_shift) * nkb;
   }
 
   f32x4 acc[4][NTW];

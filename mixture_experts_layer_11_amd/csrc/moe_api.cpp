@@ -78,6 +78,8 @@ int check_cfg(const moe_cfg* c) {
   if (fp8) {
     if (c->quant_block != 128) return fail(MOE_ERR_UNSUPPORTED, "fp8 block %d != 128", c->quant_block);
     if (c->I % 128) return fail(MOE_ERR_UNSUPPORTED, "fp8 needs I %% 128 == 0");
+    if (c->w_block_rows != 1 && c->w_block_rows != 128)
+      return fail(MOE_ERR_UNSUPPORTED, "fp8 weight scale blocks of %d rows (1 or 128)", c->w_block_rows);
   }
   return MOE_OK;
 }

@@ -75,6 +75,7 @@ def test_workspace_size_for_each_workload(name):
     (dict(act_dtype="f32"), B.MOE_ERR_UNSUPPORTED),
     (dict(w_dtype="fp8", quant_block=64), B.MOE_ERR_UNSUPPORTED),
     (dict(w_dtype="fp8", I=2112), B.MOE_ERR_UNSUPPORTED),
+    (dict(w_dtype="fp8", w_block_rows=64), B.MOE_ERR_UNSUPPORTED),
     (dict(n_group=3, topk_group=1), B.MOE_ERR_INVALID_ARG),              # E = 256 not a multiple of 3
     (dict(n_group=8, topk_group=9), B.MOE_ERR_INVALID_ARG),              # topk_group > n_group
     (dict(n_group=8, topk_group=0), B.MOE_ERR_INVALID_ARG),

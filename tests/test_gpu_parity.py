@@ -53,6 +53,11 @@ SMALL = {
     "t24_bf16": get_config("decode16").with_(name="t24_bf16", T=24, H=512, E=16, k=4, I=256, I_shared=256),
     "t12_fp8": get_config("clustered2048_fp8").with_(name="t12_fp8", T=12, H=512, E=16, k=2, I=256, I_shared=256),
     "t20_f32": get_config("tiny_f32").with_(name="t20_f32", T=20, E=8, k=2),
+    # fp8 weights in 128 x 128 scale tiles: tiled and streaming groups, both shared-expert paths
+    "small_fp8_tiles": get_config("decode16_fp8").with_(name="small_fp8_tiles", T=150, H=512, E=16, k=4, I=256,
+                                                        I_shared=256),
+    "t12_fp8_tiles": get_config("decode16_fp8").with_(name="t12_fp8_tiles", T=12, H=512, E=16, k=2, I=256,
+                                                      I_shared=256),
 }
 
 
@@ -392,7 +397,7 @@ def test_all_tokens_to_one_expert():
 
 # ------------------------------------------------------------------ full-size workloads (sampled outputs)
 
-FULL = ["decode16", "decode256", "prefill8192_ep8", "clustered2048_fp8"]
+FULL = ["decode16", "decode256", "prefill8192_ep8", "clustered2048_fp8", "decode16_fp8", "decode256_fp8"]
 
 
 @pytest.mark.parametrize("name", FULL)
