@@ -2,7 +2,8 @@
 //
 // Perplexity's "Lower latency and higher throughput with multi-node DeepSeek
 // deployment" (section "MoE router") notes that dense dispatch consumes the
-// routing aggregated per expert rather than per token.  Three small kernels:
+// routing aggregated per expert rather than per token.  Up to 4096 pairs one
+// workgroup does it all (dispatch_small_kernel); above, three kernels:
 //   1. count:   LDS-atomic histogram of each segment of 256 pairs;
 //   2. scan:    per expert, running sum over segments (segment bases and the
 //               totals), then an exclusive scan over experts (offsets);
@@ -135,6 +136,77 @@ __global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* __r
   }
 }
 
+// Up to kSmallP pairs (decode batches): the whole dispatch in one workgroup
+// of 16 waves, saving two launches.  LDS histogram -> exclusive scan ->
+// pairs in chunks of 1024 in order: a pair's slot is its expert's running
+// base, plus the counts of its expert in the chunk's earlier waves, plus its
+// rank among equal experts of lower lane (the same 64-step register scan).
+constexpr int kSmallP = 4096;
+
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __restrict__ idx, int P, int E,
+                                                              int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ sorted_pair,
+                                                              int32_t* __restrict__ pair_slot) {
+  __shared__ int hist[256];
+  __shared__ int run[256];
+  __shared__ int wcnt[16][256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < 256) hist[tid] = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += 1024) {
+    const int e = idx[p];
+    if (e >= 0 && e < E) atomicAdd(&hist[e], 1);
+  }
+  __syncthreads();
+  // exclusive scan of the expert totals by the first 256 threads
+  int v = tid < 256 ? hist[tid] : 0;
+  if (tid < 256) run[tid] = v;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {
+    const int u = (tid < 256 && tid >= d) ? run[tid - d] : 0;
+    __syncthreads();
+    if (tid < 256) run[tid] += u;
+    __syncthreads();
+  }
+  if (tid < E) {
+    counts[tid] = v;
+    offsets[tid] = run[tid] - v;
+  }
+  if (tid == 0) offsets[E] = run[E - 1];
+  __syncthreads();
+  if (tid < 256) run[tid] -= v;                      // running base: exclusive offsets
+  for (int c = 0; c < P; c += 1024) {
+    for (int i = tid; i < 16 * 256; i += 1024) (&wcnt[0][0])[i] = 0;
+    const int p = c + tid;
+    int e = p < P ? idx[p] : -1;
+    if (e < 0 || e >= E) e = -1;
+    int rank = 0, same = 0;
+    for (int j = 0; j < 64; ++j) {
+      const int ej = __builtin_amdgcn_readlane(e, j);
+      const int eq = (ej == e) ? 1 : 0;
+      same += eq;
+      rank += (j < lane) ? eq : 0;
+    }
+    __syncthreads();
+    if (e >= 0 && rank == same - 1) wcnt[wave][e] = same;   // last occurrence in the wave
+    __syncthreads();
+    if (e >= 0) {
+      int slot = run[e] + rank;
+      for (int w = 0; w < wave; ++w) slot += wcnt[w][e];
+      sorted_pair[slot] = p;
+      pair_slot[p] = slot;
+    }
+    __syncthreads();
+    if (tid < E) {
+      int add = 0;
+      for (int w = 0; w < 16; ++w) add += wcnt[w][tid];
+      run[tid] += add;
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace
 
 namespace moe {
@@ -146,6 +218,11 @@ size_t dispatch_ws_bytes(const moe_cfg& c) { return 2 * (size_t)dispatch_nseg(c)
 hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, int32_t* counts, int32_t* offsets,
                            int32_t* sorted_pair, int32_t* pair_slot, int32_t* seg_ws, hipStream_t st) {
   const int P = c.T * c.k;
+  if (P <= kSmallP) {
+    MOE_LAUNCH("dispatch_small", dispatch_small_kernel, dim3(1), dim3(1024), 0, st, idx, P, c.E, counts, offsets,
+               sorted_pair, pair_slot);
+    return hipGetLastError();
+  }
   const int nseg = dispatch_nseg(c);
   int32_t* seg_counts = seg_ws;
   int32_t* seg_base = seg_ws + (size_t)nseg * c.E;

@@ -38,15 +38,16 @@ struct Args {
   const float* a2s;             // fp8: h scales [P+T, I/qb]
   uint8_t* y_sorted;            // act dtype (fp32 when DT is fp32, else bf16)
   uint8_t* y_shared;
-  const int32_t* plan;          // see ffn_plan_kernel: list sizes, 3 skinny lists of G, fat (group,row0) pairs
+  const int32_t* plan;          // see ffn_plan_kernel: list sizes, 3 skinny lists of 2G, tile (group,row0) pairs
   int G;
+  int halves;                   // T <= 16: every group in the <= 8-row list, in 8-row halves (shared expert too)
   int fat_cap;                  // capacity of the plan's 256-row tile list (the 128-row list follows it)
   int mid_rest;                 // 1: a group's last m mod 256 rows take 128-row tiles; 0: one more 256-row tile
 };
 
 struct Group {
   int m;         // rows
-  int slot0;     // first row in the [P+T] row space of h (routed: offsets[g]; shared: P)
+  int slot0;     // first row in the [P+T] row space of h (routed: offsets[g]; shared: P + first token)
   bool routed;
 };
 
@@ -64,9 +65,28 @@ __device__ __forceinline__ Group group_of(const Args& a, int g) {
   return r;
 }
 
-// Token (row of x) feeding row r of group g in GEMM1.
+// A skinny list entry: group g (low 16 bits) and, in halves mode, which
+// 8-row half of it (bit 16): the half's rows start 8 rows further in h.
+__device__ __forceinline__ Group group_of_entry(const Args& a, int ent, int* g) {
+  *g = ent & 0xFFFF;
+  Group r = group_of(a, *g);
+  if (a.halves) {                 // entry = rows [8 * half, 8 * half + 8) of the group
+    const int half = ent >> 16;
+    r.slot0 += 8 * half;
+    r.m = min(8, r.m - 8 * half);
+  }
+  return r;
+}
+
+// Token (row of x) feeding row r of group g in GEMM1 (the shared expert's
+// rows are the tokens, from P on in h's row space).
 __device__ __forceinline__ int gemm1_src_row(const Args& a, const Group& gr, int r) {
-  return gr.routed ? a.sorted_pair[gr.slot0 + r] / a.k : r;
+  return gr.routed ? a.sorted_pair[gr.slot0 + r] / a.k : gr.slot0 - a.P + r;
+}
+
+// Row of y_sorted (routed) or y_shared (shared) for row r of a group.
+__device__ __forceinline__ int out_row(const Args& a, const Group& gr, int r) {
+  return gr.routed ? gr.slot0 + r : gr.slot0 - a.P + r;
 }
 
 template <int DT> struct HOut;  // element type of h
@@ -94,7 +114,7 @@ __device__ __forceinline__ void store_y(uint8_t* y, size_t idx, float v) {
 
 constexpr int kSkNT = 8;   // 8-row weight tiles per routed skinny item (even: gate/up halves in GEMM1)
 constexpr int kShNT = 2;   // 8-row weight tiles per item of the skinny shared expert
-constexpr int kShKS = 8;   // waves splitting K in the skinny shared expert's workgroups
+constexpr int kShKS = 4;   // waves splitting K in the skinny shared expert's workgroups
 constexpr int kTM = 256;   // tiled GEMM: tile rows (tokens)
 constexpr int kTN = 256;   // tiled GEMM: tile columns (weight rows; GEMM1: 128 gate + 128 up)
 

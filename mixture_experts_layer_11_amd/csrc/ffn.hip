@@ -51,14 +51,18 @@ __global__ __launch_bounds__(512) void ffn_plan_kernel(Args a) {
   // skinny class: 0 for 1..8 rows, 1 for 9..16, 2 for 17..32; larger groups
   // take floor(m / 256) full tiles, and their last m mod 256 rows one more
   // 256-row tile or (mid_rest) ceil((m mod 256) / 128) 128-row tiles.  The
-  // shared expert is in no list: it has launches of its own.
+  // shared expert has launches of its own, except in halves mode (T <= 16):
+  // there every group, the shared expert included, enters the <= 8-row list
+  // as one or two 8-row halves, so the other lists stay empty.
   const bool shared = g == a.E;
-  const int cls = (m > 0 && m <= kSkinnyRows && !shared) ? (m <= 8 ? 0 : m <= 16 ? 1 : 2) : -1;
+  const bool listed = m > 0 && m <= kSkinnyRows && (!shared || a.halves);
+  const int cls = listed ? (a.halves || m <= 8 ? 0 : m <= 16 ? 1 : 2) : -1;
+  const int nent = cls < 0 ? 0 : (a.halves ? (m + 7) / 8 : 1);   // list entries of this group
   const bool tiled = m > kSkinnyRows && !shared;
   const int tiles = tiled ? (a.mid_rest ? m / kTileRows : (m + kTileRows - 1) / kTileRows) : 0;
   const int mids = tiled && a.mid_rest ? (m % kTileRows + kMidRows - 1) / kMidRows : 0;
 #pragma unroll
-  for (int c = 0; c < 3; ++c) sk[c][g] = cls == c ? 1 : 0;
+  for (int c = 0; c < 3; ++c) sk[c][g] = cls == c ? nent : 0;
   ft[g] = tiles;
   mt[g] = mids;
   __syncthreads();
@@ -82,8 +86,8 @@ __global__ __launch_bounds__(512) void ffn_plan_kernel(Args a) {
     plan[3] = ft[511];
     plan[4] = mt[511];
   }
-  if (cls >= 0) plan[kPlanHead + cls * a.G + sk[cls][g] - 1] = g;
-  int32_t* fat = plan + kPlanHead + 3 * a.G;
+  for (int h = 0; h < nent; ++h) plan[kPlanHead + cls * 2 * a.G + sk[cls][g] - nent + h] = g | (h << 16);
+  int32_t* fat = plan + kPlanHead + 6 * a.G;
   const int t0 = ft[g] - tiles;
   for (int i = 0; i < tiles; ++i) {
     fat[2 * (t0 + i)] = g;
@@ -140,9 +144,12 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st) {
   const int tiled_groups = c.T > kSkinnyRows ? (P / (kSkinnyRows + 1) < c.E ? P / (kSkinnyRows + 1) : c.E) : 0;
   const int max_fat = tiled_groups > 0 ? P / kTileRows + (a.mid_rest ? 0 : tiled_groups) : 0;
   const int max_mid = a.mid_rest ? 2 * tiled_groups : 0;
+  // halves mode: the shared expert's rows [P, P + T) of h are the routed lists' too
+  const int qrows = P + (a.halves && a.has_shared ? c.T : 0);
   for (int mode = 1; mode <= 2; ++mode) {
     if (mode == 2 && DT == MOE_FP8_E4M3) {
-      e = moe::launch_quant_fp8(P, c.I, a.qb, a.h, MOE_F32, const_cast<uint8_t*>(a.a2), const_cast<float*>(a.a2s), st);
+      e = moe::launch_quant_fp8(qrows, c.I, a.qb, a.h, MOE_F32, const_cast<uint8_t*>(a.a2), const_cast<float*>(a.a2s),
+                                st);
       if (e != hipSuccess) return e;
     }
     const int N = mode == 1 ? c.I : c.H;
@@ -151,7 +158,11 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st) {
       // a group of class cls has at least 1, 9 or 17 rows, and no group has
       // more than T rows (a token picks k distinct experts)
       const int min_rows = cls == 0 ? 1 : (4 << cls) + 1;
-      const int groups = P / min_rows < c.E ? P / min_rows : c.E;
+      int groups = P / min_rows < c.E ? P / min_rows : c.E;
+      if (a.halves) {            // every half has at least one row; two halves of the shared expert
+        if (cls > 0) continue;
+        groups = (P < 2 * c.E ? P : 2 * c.E) + (a.has_shared ? 2 : 0);
+      }
       if (groups == 0 || min_rows > c.T) continue;
       const unsigned grid = (unsigned)((moe::ceil_div(groups * items, 4LL) + 7) & ~7LL);   // 4 items per workgroup
       if ((e = launch_skinny<DT>(mode, cls, grid, a, st)) != hipSuccess) return e;
@@ -178,7 +189,7 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st) {
 // st, where running beside the routed kernels would only add contention.
 template <int DT>
 hipError_t run_ffn(const moe_cfg& c, const Args& a, hipStream_t st) {
-  if (!a.has_shared) return run_routed<DT>(c, a, st);
+  if (!a.has_shared || a.halves) return run_routed<DT>(c, a, st);
   moe::SideStream side;
   hipError_t e = moe::side_stream(&side);
   if (e != hipSuccess) return e;
@@ -209,8 +220,8 @@ int ffn_fat_cap(const moe_cfg& c) { return c.T * c.k / kTileRows + (c.w_dtype ==
 
 size_t ffn_plan_ints(const moe_cfg& c) {
   const int G = c.E + (c.I_shared > 0 ? 1 : 0);
-  // 128-row tiles: at most two per routed group
-  return kPlanHead + 3 * (size_t)G + 2 * (size_t)ffn_fat_cap(c) + 2 * (size_t)(2 * c.E);
+  // three skinny lists of up to 2G entries (halves); 128-row tiles: at most two per routed group
+  return kPlanHead + 6 * (size_t)G + 2 * (size_t)ffn_fat_cap(c) + 2 * (size_t)(2 * c.E);
 }
 
 size_t ffn_h_elem_bytes(const moe_cfg& c) { return c.w_dtype == MOE_BF16 ? 2 : 4; }
@@ -244,6 +255,7 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const void* x, const int32_t* off
   a.plan = ws.plan;
   a.G = c.E + (a.has_shared ? 1 : 0);
   a.fat_cap = ffn_fat_cap(c);
+  a.halves = c.T <= 16;
   a.mid_rest = c.w_dtype == MOE_FP8_E4M3;   // HBM-bound medium groups: deeper pipeline on 128-row tiles
   if (c.w_dtype == MOE_FP8_E4M3) {
     hipError_t e = launch_quant_fp8(c.T, c.H, c.quant_block, x, MOE_BF16, ws.xq, ws.xs, st);

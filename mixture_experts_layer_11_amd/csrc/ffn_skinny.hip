@@ -229,7 +229,7 @@ __device__ __forceinline__ void skinny_pass(const Args& a, const Group& gr, int 
         }
       } else {
         uint8_t* ybase = gr.routed ? a.y_sorted : a.y_shared;
-        const size_t yrow = (size_t)(gr.routed ? gr.slot0 + r : r) * a.H;
+        const size_t yrow = (size_t)out_row(a, gr, r) * a.H;
 #pragma unroll
         for (int j = 0; j < NTP; ++j) store_y<DT>(ybase, yrow + it * cols_per_item + 8 * (p * NTP + j) + r8, acc[mt][j][i]);
       }
@@ -273,9 +273,9 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(Args a) {
   const int item = ((blockIdx.x & 7) * per_xcd + local) * 4 + wave;
   const int gi = item / items;
   if (gi >= a.plan[CLS]) return;
-  const int g = a.plan[kPlanHead + CLS * a.G + gi];
+  int g;
+  const Group gr = group_of_entry(a, a.plan[kPlanHead + CLS * 2 * a.G + gi], &g);
   const int it = item - gi * items;
-  const Group gr = group_of(a, g);
   skinny_pass<DT, MODE, MT, NT, NT, 1, 1>(a, gr, g, it, 0, lane, 0, nullptr);
 }
 

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
     row0 = TM == 256 ? tile * 256 : (a.T / 256) * 256 + tile * 128;   // 128-row tiles only with mid_rest
   } else {
     if (tile >= a.plan[TM == 256 ? 3 : 4]) return;
-    const int32_t* list = a.plan + kPlanHead + 3 * a.G + (TM == 256 ? 0 : 2 * a.fat_cap);
+    const int32_t* list = a.plan + kPlanHead + 6 * a.G + (TM == 256 ? 0 : 2 * a.fat_cap);
     g = list[2 * tile];
     row0 = list[2 * tile + 1];
   }
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
         }
       } else {
         uint8_t* ybase = gr.routed ? a.y_sorted : a.y_shared;
-        const size_t yrow = (size_t)(gr.routed ? gr.slot0 + row0 + r : row0 + r) * a.H;
+        const size_t yrow = (size_t)out_row(a, gr, row0 + r) * a.H;
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
           const int col = nt * kTN + wn * WN + j * 16 + row;

@@ -53,6 +53,11 @@ SMALL = {
     "t24_bf16": get_config("decode16").with_(name="t24_bf16", T=24, H=512, E=16, k=4, I=256, I_shared=256),
     "t12_fp8": get_config("clustered2048_fp8").with_(name="t12_fp8", T=12, H=512, E=16, k=2, I=256, I_shared=256),
     "t20_f32": get_config("tiny_f32").with_(name="t20_f32", T=20, E=8, k=2),
+    # T <= 16: groups of 9..16 rows and the shared expert run as 8-row halves in the <= 8-row launch
+    "t16_e4_halves_bf16": get_config("decode16").with_(name="t16_e4_halves_bf16", T=16, H=512, E=4, k=2, I=256,
+                                                       I_shared=256),
+    # 17..32 tokens: the split-K shared-expert kernel, fp8
+    "t20_fp8": get_config("clustered2048_fp8").with_(name="t20_fp8", T=20, H=512, E=16, k=2, I=256, I_shared=256),
     # fp8 weights in 128 x 128 scale tiles: tiled and streaming groups, both shared-expert paths
     "small_fp8_tiles": get_config("decode16_fp8").with_(name="small_fp8_tiles", T=150, H=512, E=16, k=4, I=256,
                                                         I_shared=256),
@@ -195,8 +200,10 @@ def _distinct_topk(rng, T, E, k):
     return np.argsort(rng.random((T, E)), axis=1)[:, :k]
 
 
+# single-workgroup path up to 4096 pairs (several 1024-pair chunks at 512 x 8),
+# the three-kernel path above (513 x 8 = 4104 pairs and more)
 @pytest.mark.parametrize("T,E,k", [(1, 1, 1), (33, 4, 4), (200, 32, 4), (1000, 256, 8), (8192, 32, 8),
-                                   (2048, 256, 8), (16, 256, 8)])
+                                   (2048, 256, 8), (16, 256, 8), (512, 256, 8), (513, 256, 8), (300, 3, 2)])
 def test_dispatch_exact(T, E, k):
     rng = np.random.default_rng(T * 7 + E)
     idx = _distinct_topk(rng, T, E, k)
@@ -208,8 +215,9 @@ def test_dispatch_exact(T, E, k):
         np.testing.assert_array_equal(to_np(g), ref[name], err_msg=name)
 
 
-def test_dispatch_all_pairs_to_one_expert():
-    T, E, k = 65536, 8, 1
+@pytest.mark.parametrize("T", [4096, 65536])
+def test_dispatch_all_pairs_to_one_expert(T):
+    E, k = 8, 1
     idx = np.full((T, k), 5)
     cfg = moe.make_cfg(T, 128, E, k, 64, 64)
     got = moe.moe_dispatch(cfg, torch.from_numpy(idx.astype(np.int32)).to(DEV))
