@@ -178,30 +178,35 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
 #pragma unroll
   for (int p = 0; p < NST - 1; ++p)
     if (p < nkt) tile_issue<DT, TM>(smem, ga, gb, gs, p, p, wave);
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int st = kt % NST;
-    // wait until this thread's loads of slice kt have landed; later slices may stay in flight
-    if (NST > 2 && kt + 1 < nkt) wait_vmcnt<C::PER_SLICE>();
-    else wait_vmcnt<0>();
-    barrier_no_fence();                            // everyone's slice kt is in LDS; stage (kt-1) % NST is free
-    if (kt + NST - 1 < nkt) tile_issue<DT, TM>(smem, ga, gb, gs, kt + NST - 1, (kt + NST - 1) % NST, wave);
-    const uint8_t* la = smem + st * C::STAGE;
-    const uint8_t* lb = la + TM * SL;
+  bool full_tile = false;
+  if constexpr (!FP8) full_tile = mval == 4;
+  if (full_tile) {
+    // Full tiles (all 64 rows of every M tile valid; bf16 and fp32 weights,
+    // two stages): one straight-line block per slice, so the scheduling
+    // hints below can order the fragment reads, the next slice's direct
+    // loads and the MFMAs.  The first half's reads go first; the next slice's
+    // loads are issued while they are in flight, spread over the first
+    // MFMAs, so a wave never stalls on a full load queue while it has MFMAs
+    // ready; the second half's reads are interleaved with the rest of the
+    // first half's MFMAs.  The last slice reloads itself into the free stage,
+    // which keeps the block free of branches.
     if constexpr (!FP8) {
-      // Full tiles: all fragments of the slice are read first and the MFMAs
-      // follow in the same straight-line block, so the compiler can start the
-      // first half's MFMAs while the second half's reads are in flight.  Only
-      // a group's last, partial tile takes the guarded path that skips M tiles.
-      if (mval == 4) {
+      static_assert(NST == 2, "the full-tile loop assumes two stages");
+      for (int kt = 0; kt < nkt; ++kt) {
+        wait_vmcnt<0>();                           // this thread's loads of slice kt have landed
+        barrier_no_fence();                        // everyone's have, and the other stage is free
+        const uint8_t* la = smem + (kt & 1) * C::STAGE;
+        const uint8_t* lb = la + TM * SL;
         i32x4 fa[SL / 64][4], fb[SL / 64][NTW];
 #pragma unroll
         for (int fs = 0; fs < SL / 64; ++fs) {
-#pragma unroll
-          for (int j = 0; j < NTW; ++j)
-            fb[fs][j] = *reinterpret_cast<const i32x4*>(&lb[C::off(wn * WN + j * 16 + row, fs * 4 + grp)]);
+          if (fs == 1) tile_issue<DT, TM>(smem, ga, gb, gs, min(kt + 1, nkt - 1), (kt + 1) & 1, wave);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             fa[fs][i] = *reinterpret_cast<const i32x4*>(&la[C::off(wm * 64 + i * 16 + row, fs * 4 + grp)]);
+#pragma unroll
+          for (int j = 0; j < NTW; ++j)
+            fb[fs][j] = *reinterpret_cast<const i32x4*>(&lb[C::off(wn * WN + j * 16 + row, fs * 4 + grp)]);
         }
 #pragma unroll
         for (int fs = 0; fs < SL / 64; ++fs)
@@ -209,71 +214,90 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
           for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < NTW; ++j) F::mma(acc[i][j], fa[fs][i], fb[fs][j]);
-        // Instruction order for the scheduler: the first half's reads, then
-        // the second half's reads interleaved 1:2 with the first half's
-        // MFMAs, then the rest, so LDS latency hides behind MFMAs.
         if constexpr (DT == MOE_BF16) {
           constexpr int R = 4 + NTW;                 // fragment reads per half
+          constexpr int L = C::LPA + C::LPB;         // direct loads per slice
           __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
 #pragma unroll
-          for (int q = 0; q < R; ++q) {
+          for (int q = 0; q < L; ++q) {              // 1 load : 2 MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          }
+#pragma unroll
+          for (int q = 0; q < R; ++q) {              // 1 read : 2 MFMAs
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
           }
-          __builtin_amdgcn_sched_group_barrier(0x008, 8 * NTW - 2 * R, 0);
-        }
-      } else if (mval > 0) {
-#pragma unroll
-        for (int fs = 0; fs < SL / 64; ++fs) {
-          i32x4 fb[NTW];
-#pragma unroll
-          for (int j = 0; j < NTW; ++j)
-            fb[j] = *reinterpret_cast<const i32x4*>(&lb[C::off(wn * WN + j * 16 + row, fs * 4 + grp)]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (i < mval) {
-              const i32x4 fa = *reinterpret_cast<const i32x4*>(&la[C::off(wm * 64 + i * 16 + row, fs * 4 + grp)]);
-#pragma unroll
-              for (int j = 0; j < NTW; ++j) F::mma(acc[i][j], fa, fb[j]);
-            }
+          __builtin_amdgcn_sched_group_barrier(0x008, 8 * NTW - 2 * R - 2 * L, 0);
         }
       }
-    } else {
-      const float* sa_l = lds_s + st * C::NSC;
-      const float* sb_l = sa_l + TM;
-      // groups of 4 column tiles keep the B fragments within the register budget
+    }
+  } else {
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int st = kt % NST;
+      // wait until this thread's loads of slice kt have landed; later slices may stay in flight
+      if (NST > 2 && kt + 1 < nkt) wait_vmcnt<C::PER_SLICE>();
+      else wait_vmcnt<0>();
+      barrier_no_fence();                          // everyone's slice kt is in LDS; stage (kt-1) % NST is free
+      if (kt + NST - 1 < nkt) tile_issue<DT, TM>(smem, ga, gb, gs, kt + NST - 1, (kt + NST - 1) % NST, wave);
+      const uint8_t* la = smem + st * C::STAGE;
+      const uint8_t* lb = la + TM * SL;
+      if constexpr (!FP8) {
+        // a group's last, partial tile: skip the M tiles without valid rows
+        if (mval > 0) {
 #pragma unroll
-      for (int jh = 0; jh < NTW / 4; ++jh) {
-        i32x4 fb0[4], fb1[4];
-        float sb[4];
+          for (int fs = 0; fs < SL / 64; ++fs) {
+            i32x4 fb[NTW];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int n = wn * WN + (4 * jh + jj) * 16 + row;
-          fb0[jj] = *reinterpret_cast<const i32x4*>(&lb[C::off(n, grp)]);
-          fb1[jj] = *reinterpret_cast<const i32x4*>(&lb[C::off(n, 4 + grp)]);
-          sb[jj] = sb_l[n];
+            for (int j = 0; j < NTW; ++j)
+              fb[j] = *reinterpret_cast<const i32x4*>(&lb[C::off(wn * WN + j * 16 + row, fs * 4 + grp)]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (i < mval) {
+                const i32x4 fa = *reinterpret_cast<const i32x4*>(&la[C::off(wm * 64 + i * 16 + row, fs * 4 + grp)]);
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) F::mma(acc[i][j], fa, fb[j]);
+              }
+          }
         }
+      } else {
+        const float* sa_l = lds_s + st * C::NSC;
+        const float* sb_l = sa_l + TM;
+        // groups of 4 column tiles keep the B fragments within the register budget
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (i < mval) {
-            const int r = wm * 64 + i * 16 + row;
-            const i32x4 fa0 = *reinterpret_cast<const i32x4*>(&la[C::off(r, grp)]);
-            const i32x4 fa1 = *reinterpret_cast<const i32x4*>(&la[C::off(r, 4 + grp)]);
-            float sa[4];
+        for (int jh = 0; jh < NTW / 4; ++jh) {
+          i32x4 fb0[4], fb1[4];
+          float sb[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) sa[q] = sa_l[wm * 64 + i * 16 + 4 * grp + q];
+          for (int jj = 0; jj < 4; ++jj) {
+            const int n = wn * WN + (4 * jh + jj) * 16 + row;
+            fb0[jj] = *reinterpret_cast<const i32x4*>(&lb[C::off(n, grp)]);
+            fb1[jj] = *reinterpret_cast<const i32x4*>(&lb[C::off(n, 4 + grp)]);
+            sb[jj] = sb_l[n];
+          }
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const f32x4 p = F::mma128(fa0, fa1, fb0[jj], fb1[jj]);
+          for (int i = 0; i < 4; ++i) {
+            if (i < mval) {
+              const int r = wm * 64 + i * 16 + row;
+              const i32x4 fa0 = *reinterpret_cast<const i32x4*>(&la[C::off(r, grp)]);
+              const i32x4 fa1 = *reinterpret_cast<const i32x4*>(&la[C::off(r, 4 + grp)]);
+              float sa[4];
 #pragma unroll
-              for (int q = 0; q < 4; ++q)
-                acc[i][4 * jh + jj][q] = fmaf(p[q], sa[q] * sb[jj], acc[i][4 * jh + jj][q]);
+              for (int q = 0; q < 4; ++q) sa[q] = sa_l[wm * 64 + i * 16 + 4 * grp + q];
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj) {
+                const f32x4 p = F::mma128(fa0, fa1, fb0[jj], fb1[jj]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                  acc[i][4 * jh + jj][q] = fmaf(p[q], sa[q] * sb[jj], acc[i][4 * jh + jj][q]);
+              }
             }
           }
         }
       }
     }
   }
+  wait_vmcnt<0>();   // the full-tile loop's last reload is still in flight
 
   // ---- epilogue: lane holds rows wm*64 + i*16 + 4*grp + q, columns wn*WN + j*16 + row
 #pragma unroll
