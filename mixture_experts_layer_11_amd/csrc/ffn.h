@@ -112,6 +112,15 @@ __device__ __forceinline__ void store_y(uint8_t* y, size_t idx, float v) {
     reinterpret_cast<uint16_t*>(y)[idx] = f32_to_bf16(v);
 }
 
+// s_waitcnt that waits for vmcnt <= n only (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// s_waitcnt lgkmcnt(0) only: this wave's LDS reads have completed.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
+
 constexpr int kSkNT = 8;   // 8-row weight tiles per routed skinny item (even: gate/up halves in GEMM1)
 constexpr int kShNT = 2;   // 8-row weight tiles per item of the skinny shared expert
 constexpr int kShKS = 4;   // waves splitting K in the skinny shared expert's workgroups

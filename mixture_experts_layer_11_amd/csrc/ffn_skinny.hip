@@ -33,6 +33,45 @@ __device__ __forceinline__ i32x4 ldw16(const uint8_t* p) {
 
 __device__ __forceinline__ int sk_chunk(int lane) { return 4 * ((lane >> 3) & 1) + (lane >> 4); }
 
+// Fold the two K halves and store: lanes L = 16*h + r (h < 2, r < 8) end up
+// holding tokens 4*h + i (i = 0..3) of each M tile for weight row r of each
+// tile.  GEMM1 applies SwiGLU to the gate/up tile pairs.
+template <int DT, int MODE, int MT, int NT, int NTP>
+__device__ __forceinline__ void skinny_epilogue(const Args& a, const Group& gr, int it, int p, int lane,
+                                                f32x4 (&acc)[MT][NTP]) {
+  const int r8 = lane & 7;
+  const int cols_per_item = MODE == 1 ? 4 * NT : 8 * NT;   // h columns (GEMM1) or y columns (GEMM2)
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < NTP; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[mt][j][i] += __shfl_xor(acc[mt][j][i], 40, 64);
+  if ((lane & 8) || lane >= 32) return;
+  const int hh = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = mt * 8 + 4 * hh + i;
+      if (r >= gr.m) continue;
+      if (MODE == 1) {
+        const size_t hrow = (size_t)(gr.slot0 + r) * a.I;
+#pragma unroll
+        for (int j = 0; j < NTP / 2; ++j) {
+          const float gv = acc[mt][j][i], uv = acc[mt][j + NTP / 2][i];
+          store_h<DT>(a.h, hrow + it * cols_per_item + 8 * (p * (NTP / 2) + j) + r8, silu(gv) * uv);
+        }
+      } else {
+        uint8_t* ybase = gr.routed ? a.y_sorted : a.y_shared;
+        const size_t yrow = (size_t)out_row(a, gr, r) * a.H;
+#pragma unroll
+        for (int j = 0; j < NTP; ++j) store_y<DT>(ybase, yrow + it * cols_per_item + 8 * (p * NTP + j) + r8, acc[mt][j][i]);
+      }
+    }
+  }
+}
+
 // One pass over the full K for NTP of the wave's NT weight tiles (pass p),
 // against MT M tiles of 8 tokens (MT * 8 >= group rows).  Rows beyond the
 // group's count are clamped to its last row: their results are never stored,
@@ -204,37 +243,156 @@ __device__ __forceinline__ void skinny_pass(const Args& a, const Group& gr, int 
     if (ks > 0) return;
   }
 
-  // Fold the two K halves: lanes L = 16*h + r (h < 2, r < 8) end up holding
-  // tokens 4*h + i (i = 0..3) of each M tile for weight row r of each tile.
+  skinny_epilogue<DT, MODE, MT, NT, NTP>(a, gr, it, p, lane, acc);
+}
+
+// Streaming through a per-wave LDS ring, for the many-row classes.  Wide
+// items (NT tiles) against up to 32 rows need most of the register file, so
+// one wave per SIMD is resident and only the wave's own queue of loads can
+// hide the HBM latency.  Each K window of the item (the NT weight tiles' and
+// MT activation tiles' 1 KB blocks, plus for fp8 the window's weight and
+// activation scales) goes global -> LDS directly into slot w % D of the
+// wave's ring; the wave issues window w + D as soon as it has read window w
+// back into registers, so D windows are always in flight.  The LDS copy of a
+// block keeps the lane order of the register load (lane l's 16 bytes at
+// l * 16), so reading it back is one conflict-free ds_read_b128 per block.
+// Only this wave touches its ring: the waits are vmcnt waits, no barriers.
+//
+// fp8 scales of a window: lane l fetches the weight scale of tile (l & 7),
+// row (l >> 3) of the item, so a lane's 8 tile scales for its own row r8 sit
+// at floats 8 * r8 .. 8 * r8 + 7; lanes l < 32 fetch the activation scale of
+// M tile (l >> 3), row (l & 7), and a lane's 4 rows (4 * ((lane >> 4) & 1) + i)
+// of each M tile are consecutive.
+template <int DT, int MT, int NT> struct RingCfg {
+  static constexpr bool FP8 = DT == MOE_FP8_E4M3;
+  static constexpr int NL = NT + MT + (FP8 ? 2 : 0);             // direct loads per window
+  static constexpr int WIN = (NT + MT) * 1024 + (FP8 ? 512 : 0);  // LDS bytes per window
+};
+
+template <int DT, int MODE, int MT, int NT, int D>
+__device__ __forceinline__ void skinny_ring(const Args& a, const Group& gr, int g, int it, int lane, uint8_t* ring) {
+  using F = Frag<DT>;
+  using R = RingCfg<DT, MT, NT>;
+  constexpr bool FP8 = R::FP8;
+  const int r8 = lane & 7;
+  const int ch16 = sk_chunk(lane) * 16;
+  const int cols_per_item = MODE == 1 ? 4 * NT : 8 * NT;
+  const int K = MODE == 1 ? a.H : a.I;
+  const size_t krow = (size_t)K * F::ESZ;
+  const int nwin = (int)(krow / 128);
+
+  const uint8_t* abase = MODE == 1 ? a.a1 : a.a2;
+  const uint8_t* wbase;
+  const float* wsbase = nullptr;
+  if (MODE == 1) {
+    wbase = gr.routed ? a.w13 + (size_t)g * 2 * a.I * krow : a.ws13;
+    if (FP8) wsbase = gr.routed ? a.w13s + (size_t)g * ((2 * a.I) >> a.wsr_shift) * nwin : a.ws13s;
+  } else {
+    wbase = gr.routed ? a.w2 + (size_t)g * a.H * krow : a.ws2;
+    if (FP8) wsbase = gr.routed ? a.w2s + (size_t)g * (a.H >> a.wsr_shift) * nwin : a.ws2s;
+  }
+  // weight row of tile j for item row r (GEMM1: first half gate tiles, second half the matching up tiles)
+  auto wrow_of = [&](int j, int r) -> int {
+    return MODE == 1 ? (j < NT / 2 ? 0 : a.I) + it * cols_per_item + 8 * (j % (NT / 2)) + r
+                     : it * cols_per_item + 8 * j + r;
+  };
+  // token row (GEMM1) or h row (GEMM2) of group row r, clamped: clamped rows feed C rows never stored
+  auto src_row = [&](int r) -> int {
+    r = min(r, gr.m - 1);
+    return MODE == 1 ? gemm1_src_row(a, gr, r) : gr.slot0 + r;
+  };
+  // one per-lane weight pointer; tile j sits a wave-uniform distance further
+  const uint8_t* pb0 = wbase + (size_t)wrow_of(0, r8) * krow + ch16;
+  size_t tile_off[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) tile_off[j] = (size_t)(wrow_of(j, 0) - wrow_of(0, 0)) * krow;
+  const uint8_t* pa[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) pa[mt] = abase + (size_t)src_row(mt * 8 + r8) * krow + ch16;
+  const float* psw = nullptr;
+  const float* psa = nullptr;
+  if constexpr (FP8) {
+    psw = wsbase + (size_t)(wrow_of(lane & 7, lane >> 3) >> a.wsr_shift) * nwin;
+    const int l32 = lane & 31;
+    psa = (MODE == 1 ? a.a1s : a.a2s) + (size_t)src_row(min(l32 >> 3, MT - 1) * 8 + (l32 & 7)) * nwin;
+  }
+
+  auto issue = [&](uint8_t* base, int w) {
+    const size_t off = (size_t)w * 128;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) __builtin_amdgcn_global_load_lds(pb0 + (tile_off[j] + off), base + j * 1024, 16, 0, 2);   // nt
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) __builtin_amdgcn_global_load_lds(pa[mt] + off, base + (NT + mt) * 1024, 16, 0, 0);
+    if constexpr (FP8) {
+      __builtin_amdgcn_global_load_lds(psw + w, base + (NT + MT) * 1024, 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(psa + w, base + (NT + MT) * 1024 + 256, 4, 0, 0);
+    }
+  };
+
+  f32x4 acc[MT][NT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int j = 0; j < NTP; ++j)
+    for (int j = 0; j < NT; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const uint8_t* base) {
+    i32x4 b[NT], av[MT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[mt][j][i] += __shfl_xor(acc[mt][j][i], 40, 64);
-  if ((lane & 8) || lane >= 32) return;
-  const int hh = lane >> 4;
+    for (int j = 0; j < NT; ++j) b[j] = *reinterpret_cast<const i32x4*>(base + j * 1024 + lane * 16);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) av[mt] = *reinterpret_cast<const i32x4*>(base + (NT + mt) * 1024 + lane * 16);
+    if constexpr (!FP8) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = mt * 8 + 4 * hh + i;
-      if (r >= gr.m) continue;
-      if (MODE == 1) {
-        const size_t hrow = (size_t)(gr.slot0 + r) * a.I;
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int j = 0; j < NTP / 2; ++j) {
-          const float gv = acc[mt][j][i], uv = acc[mt][j + NTP / 2][i];
-          store_h<DT>(a.h, hrow + it * cols_per_item + 8 * (p * (NTP / 2) + j) + r8, silu(gv) * uv);
+        for (int j = 0; j < NT; ++j) F::mma(acc[mt][j], av[mt], b[j]);
+    } else {
+      const float* sb = reinterpret_cast<const float*>(base + (NT + MT) * 1024);
+      float sw[NT], sa[MT][4];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) sw[j] = sb[8 * r8 + j];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sa[mt][i] = sb[64 + mt * 8 + 4 * ((lane >> 4) & 1) + i];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          // a 16-byte chunk is 16 fp8 values: two 16x16x32 MFMAs (8 bytes per lane each)
+          f32x4 pr = {0.f, 0.f, 0.f, 0.f};
+          pr = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(((const long*)&av[mt])[0], ((const long*)&b[j])[0], pr, 0, 0, 0);
+          pr = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(((const long*)&av[mt])[1], ((const long*)&b[j])[1], pr, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mt][j][i] = fmaf(pr[i], sa[mt][i] * sw[j], acc[mt][j][i]);
         }
-      } else {
-        uint8_t* ybase = gr.routed ? a.y_sorted : a.y_shared;
-        const size_t yrow = (size_t)out_row(a, gr, r) * a.H;
-#pragma unroll
-        for (int j = 0; j < NTP; ++j) store_y<DT>(ybase, yrow + it * cols_per_item + 8 * (p * NTP + j) + r8, acc[mt][j][i]);
-      }
     }
+  };
+
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (d < nwin) issue(ring + d * R::WIN, d);
+  int w = 0, slot = 0;
+  // steady state: windows w .. w + D - 1 in flight; consume w, refill its slot with w + D
+  for (; w + D < nwin; ++w) {
+    wait_vmcnt<(D - 1) * R::NL>();
+    uint8_t* base = ring + slot * R::WIN;
+    compute(base);
+    wait_lgkm0();   // the slot's reads are done before its refill can land
+    issue(base, w + D);
+    slot = slot + 1 == D ? 0 : slot + 1;
   }
+  // drain: the last (at most D) windows are in flight, nothing more to issue
+  for (; w < nwin; ++w) {
+    const int later = nwin - 1 - w;   // windows issued after w
+    static_assert(D <= 4, "drain waits cover at most 3 later windows");
+    if (later >= 3) wait_vmcnt<3 * R::NL>();
+    else if (later == 2) wait_vmcnt<2 * R::NL>();
+    else if (later == 1) wait_vmcnt<R::NL>();
+    else wait_vmcnt<0>();
+    compute(ring + slot * R::WIN);
+    slot = slot + 1 == D ? 0 : slot + 1;
+  }
+  skinny_epilogue<DT, MODE, MT, NT, NT>(a, gr, it, 0, lane, acc);
 }
 
 // All NT tiles of an item with MT M tiles: NT / NTP passes.
@@ -253,6 +411,18 @@ __device__ __forceinline__ void skinny_tile(const Args& a, const Group& gr, int 
 // uses the same wide items: each activation fragment then serves 8 weight
 // tiles, which keeps the activation re-reads (one per item) a small share of
 // the load instructions even at 32 rows.
+// Which routed classes stream through the LDS ring (measured on MI355X):
+// every GEMM1 class, every fp8 class, and the 17..32-row class.  bf16/fp32
+// GEMM2 items of up to 16 rows are short (K = I) and run faster with four
+// register-streaming waves per SIMD than with one ring wave.
+template <int DT, int MODE, int CLS> constexpr bool sk_use_ring() {
+  return MODE == 1 || CLS == 2 || DT == MOE_FP8_E4M3;
+}
+constexpr int kRingDepth = 3;   // windows in flight per wave
+template <int DT, int MODE, int CLS> constexpr size_t sk_ring_bytes() {
+  return sk_use_ring<DT, MODE, CLS>() ? (size_t)4 * kRingDepth * RingCfg<DT, 1 << CLS, kSkNT>::WIN : 0;
+}
+
 template <int DT, int MODE, int CLS>
 __global__ __launch_bounds__(256) void ffn_skinny_kernel(Args a) {
   constexpr int MT = 1 << CLS;
@@ -276,7 +446,11 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(Args a) {
   int g;
   const Group gr = group_of_entry(a, a.plan[kPlanHead + CLS * 2 * a.G + gi], &g);
   const int it = item - gi * items;
-  skinny_pass<DT, MODE, MT, NT, NT, 1, 1>(a, gr, g, it, 0, lane, 0, nullptr);
+  if constexpr (sk_use_ring<DT, MODE, CLS>()) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t sk_ring[];
+    skinny_ring<DT, MODE, MT, NT, kRingDepth>(a, gr, g, it, lane, sk_ring + wave * kRingDepth * RingCfg<DT, MT, NT>::WIN);
+  } else
+    skinny_pass<DT, MODE, MT, NT, NT, 1, 1>(a, gr, g, it, 0, lane, 0, nullptr);
 }
 
 // The shared expert when T <= kSkinnyRows: its row count is known on the
@@ -292,20 +466,36 @@ __global__ __launch_bounds__(64 * kShKS) void ffn_shared_skinny_kernel(Args a) {
   skinny_tile<DT, MODE, MT, kShNT, kShKS>(a, gr, a.E, blockIdx.x, lane, ks, red);
 }
 
+template <int DT, int MODE, int CLS>
+hipError_t launch_sk(const char* name, unsigned grid, const Args& a, hipStream_t st) {
+  constexpr size_t lds = sk_ring_bytes<DT, MODE, CLS>();
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  if constexpr (lds > 0) {
+    static bool attr_set = false;   // raise the dynamic-LDS limit once per process
+    if (!attr_set) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_skinny_kernel<DT, MODE, CLS>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      attr_set = true;
+    }
+  }
+  MOE_LAUNCH(name, (ffn_skinny_kernel<DT, MODE, CLS>), dim3(grid), dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
 template <int DT>
 hipError_t launch_skinny_t(int mode, int cls, unsigned grid, const Args& a, hipStream_t st) {
   static const char* const kName[2][3] = {
       {"ffn_gemm1_skinny_m8", "ffn_gemm1_skinny_m16", "ffn_gemm1_skinny_m32"},
       {"ffn_gemm2_skinny_m8", "ffn_gemm2_skinny_m16", "ffn_gemm2_skinny_m32"}};
   const char* name = kName[mode - 1][cls];
-#define MOE_SK(M, CLS) MOE_LAUNCH(name, (ffn_skinny_kernel<DT, M, CLS>), dim3(grid), dim3(256), 0, st, a)
+#define MOE_SK(M, CLS) return launch_sk<DT, M, CLS>(name, grid, a, st)
   if (mode == 1) {
     if (cls == 0) MOE_SK(1, 0); else if (cls == 1) MOE_SK(1, 1); else MOE_SK(1, 2);
   } else {
     if (cls == 0) MOE_SK(2, 0); else if (cls == 1) MOE_SK(2, 1); else MOE_SK(2, 2);
   }
 #undef MOE_SK
-  return hipGetLastError();
 }
 
 template <int DT>

@@ -51,12 +51,6 @@ template <int DT, int TM> struct TileCfg {
   __device__ static __forceinline__ int off(int r, int c) { return r * SL + ((c ^ (r & 7)) << 4); }
 };
 
-// s_waitcnt that waits for vmcnt <= n only (expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // Workgroup barrier without the memory fence of __syncthreads(), whose
 // release would wait for every outstanding load, including the direct-to-LDS
 // loads of later slices that are meant to stay in flight.  The caller first
