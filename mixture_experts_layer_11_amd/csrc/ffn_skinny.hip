@@ -246,27 +246,34 @@ __device__ __forceinline__ void skinny_pass(const Args& a, const Group& gr, int 
   skinny_epilogue<DT, MODE, MT, NT, NTP>(a, gr, it, p, lane, acc);
 }
 
-// Streaming through a per-wave LDS ring, for the many-row classes.  Wide
-// items (NT tiles) against up to 32 rows need most of the register file, so
-// one wave per SIMD is resident and only the wave's own queue of loads can
-// hide the HBM latency.  Each K window of the item (the NT weight tiles' and
-// MT activation tiles' 1 KB blocks, plus for fp8 the window's weight and
-// activation scales) goes global -> LDS directly into slot w % D of the
-// wave's ring; the wave issues window w + D as soon as it has read window w
-// back into registers, so D windows are always in flight.  The LDS copy of a
-// block keeps the lane order of the register load (lane l's 16 bytes at
-// l * 16), so reading it back is one conflict-free ds_read_b128 per block.
-// Only this wave touches its ring: the waits are vmcnt waits, no barriers.
+// Streaming through a per-wave LDS ring.  Each K window of the item (the NT
+// weight tiles' and MT activation tiles' 8-row x 128-byte blocks, plus for
+// fp8 the window's weight and activation scales) goes global -> LDS directly
+// into slot w % D of the wave's ring, and the wave issues window w + D as
+// soon as it has read window w back into registers, so D windows are always
+// in flight: the wave's own queue, not other waves, hides the HBM latency,
+// and the wide items can use most of the register file.  Only this wave
+// touches its ring, so the waits are vmcnt waits and there are no barriers.
 //
-// fp8 scales of a window: lane l fetches the weight scale of tile (l & 7),
-// row (l >> 3) of the item, so a lane's 8 tile scales for its own row r8 sit
-// at floats 8 * r8 .. 8 * r8 + 7; lanes l < 32 fetch the activation scale of
-// M tile (l >> 3), row (l & 7), and a lane's 4 rows (4 * ((lane >> 4) & 1) + i)
-// of each M tile are consecutive.
+// Each direct load reads 8 whole rows x 128 bytes (lane L: row L / 8, chunk
+// (L % 8) ^ (L / 8)), stored row-major with 16-byte chunk c of row r at chunk
+// c ^ r.  Read back, 16 rows (two blocks) form one operand of a full 16x16
+// MFMA tile: activation rows along M, weight rows along N; 8 lanes reading
+// the same chunk of 8 rows hit 8 distinct 16-byte slots, free of bank
+// conflicts.  The 8-row class pairs its M tile with itself (the upper 8 C
+// rows are discarded).  bf16/fp32 take the window as two K steps (chunks
+// 4s + g for lane group g), fp8 as one 16x16x128 step (chunks g and g + 4).
+//
+// fp8 scales of a window: lane L fetches the weight scale of item row L
+// (tile L / 8, row L % 8) and, for L < 32, the activation scale of group row
+// L; a lane's C values then need the weight scale of its column and the
+// activation scales of 4 consecutive rows per M pair.
 template <int DT, int MT, int NT> struct RingCfg {
   static constexpr bool FP8 = DT == MOE_FP8_E4M3;
   static constexpr int NL = NT + MT + (FP8 ? 2 : 0);             // direct loads per window
   static constexpr int WIN = (NT + MT) * 1024 + (FP8 ? 512 : 0);  // LDS bytes per window
+  static constexpr int MP = MT > 1 ? MT / 2 : 1;                  // 16-row M pairs
+  static constexpr int NP = NT / 2;                               // 16-row N pairs
 };
 
 template <int DT, int MODE, int MT, int NT, int D>
@@ -274,8 +281,8 @@ __device__ __forceinline__ void skinny_ring(const Args& a, const Group& gr, int 
   using F = Frag<DT>;
   using R = RingCfg<DT, MT, NT>;
   constexpr bool FP8 = R::FP8;
-  const int r8 = lane & 7;
-  const int ch16 = sk_chunk(lane) * 16;
+  constexpr int MP = R::MP, NP = R::NP;
+  static_assert(NT % 2 == 0 && (MODE == 2 || NT % 4 == 0), "GEMM1 pairs gate and up 16-row blocks");
   const int cols_per_item = MODE == 1 ? 4 * NT : 8 * NT;
   const int K = MODE == 1 ? a.H : a.I;
   const size_t krow = (size_t)K * F::ESZ;
@@ -291,7 +298,7 @@ __device__ __forceinline__ void skinny_ring(const Args& a, const Group& gr, int 
     wbase = gr.routed ? a.w2 + (size_t)g * a.H * krow : a.ws2;
     if (FP8) wsbase = gr.routed ? a.w2s + (size_t)g * (a.H >> a.wsr_shift) * nwin : a.ws2s;
   }
-  // weight row of tile j for item row r (GEMM1: first half gate tiles, second half the matching up tiles)
+  // weight row of tile j, row r (GEMM1: first half gate tiles, second half the matching up tiles)
   auto wrow_of = [&](int j, int r) -> int {
     return MODE == 1 ? (j < NT / 2 ? 0 : a.I) + it * cols_per_item + 8 * (j % (NT / 2)) + r
                      : it * cols_per_item + 8 * j + r;
@@ -301,20 +308,20 @@ __device__ __forceinline__ void skinny_ring(const Args& a, const Group& gr, int 
     r = min(r, gr.m - 1);
     return MODE == 1 ? gemm1_src_row(a, gr, r) : gr.slot0 + r;
   };
-  // one per-lane weight pointer; tile j sits a wave-uniform distance further
-  const uint8_t* pb0 = wbase + (size_t)wrow_of(0, r8) * krow + ch16;
-  size_t tile_off[NT];
+  // this lane's direct-load slot: row lr of each block, global chunk lc (stored at chunk lane % 8)
+  const int lr = lane >> 3, lc = (lane & 7) ^ lr;
+  const uint8_t* pb0 = wbase + (size_t)wrow_of(0, lr) * krow + lc * 16;
+  size_t tile_off[NT];   // tile j sits a wave-uniform distance from tile 0
 #pragma unroll
   for (int j = 0; j < NT; ++j) tile_off[j] = (size_t)(wrow_of(j, 0) - wrow_of(0, 0)) * krow;
   const uint8_t* pa[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) pa[mt] = abase + (size_t)src_row(mt * 8 + r8) * krow + ch16;
+  for (int mt = 0; mt < MT; ++mt) pa[mt] = abase + (size_t)src_row(mt * 8 + lr) * krow + lc * 16;
   const float* psw = nullptr;
   const float* psa = nullptr;
   if constexpr (FP8) {
-    psw = wsbase + (size_t)(wrow_of(lane & 7, lane >> 3) >> a.wsr_shift) * nwin;
-    const int l32 = lane & 31;
-    psa = (MODE == 1 ? a.a1s : a.a2s) + (size_t)src_row(min(l32 >> 3, MT - 1) * 8 + (l32 & 7)) * nwin;
+    psw = wsbase + (size_t)(wrow_of(lane >> 3, lane & 7) >> a.wsr_shift) * nwin;
+    psa = (MODE == 1 ? a.a1s : a.a2s) + (size_t)src_row(lane & 31) * nwin;
   }
 
   auto issue = [&](uint8_t* base, int w) {
@@ -329,41 +336,59 @@ __device__ __forceinline__ void skinny_ring(const Args& a, const Group& gr, int 
     }
   };
 
-  f32x4 acc[MT][NT];
+  // operand reads: row n (0..15) of the 16-row pair starting at block blk0, logical chunk c
+  const int n16 = lane & 15, grp = lane >> 4;
+  const int rsw = (n16 & 7) * 128;
+  auto frag = [&](const uint8_t* base, int blk, int c) -> i32x4 {
+    return *reinterpret_cast<const i32x4*>(base + blk * 1024 + rsw + (((c ^ n16) & 7) << 4));
+  };
+
+  f32x4 acc[MP][NP];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int mp = 0; mp < MP; ++mp)
 #pragma unroll
-    for (int j = 0; j < NT; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int np = 0; np < NP; ++np) acc[mp][np] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](const uint8_t* base) {
-    i32x4 b[NT], av[MT];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) b[j] = *reinterpret_cast<const i32x4*>(base + j * 1024 + lane * 16);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) av[mt] = *reinterpret_cast<const i32x4*>(base + (NT + mt) * 1024 + lane * 16);
+    const int ablk = NT + min(n16 >> 3, MT - 1);   // 8-row class: rows 8..15 repeat rows 0..7
+    const int bblk = n16 >> 3;
     if constexpr (!FP8) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int s = 0; s < 2; ++s) {
+        i32x4 fa[MP], fb[NP];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) F::mma(acc[mt][j], av[mt], b[j]);
+        for (int mp = 0; mp < MP; ++mp) fa[mp] = frag(base, ablk + 2 * mp, 4 * s + grp);
+#pragma unroll
+        for (int np = 0; np < NP; ++np) fb[np] = frag(base, bblk + 2 * np, 4 * s + grp);
+#pragma unroll
+        for (int mp = 0; mp < MP; ++mp)
+#pragma unroll
+          for (int np = 0; np < NP; ++np) F::mma(acc[mp][np], fa[mp], fb[np]);
+      }
     } else {
       const float* sb = reinterpret_cast<const float*>(base + (NT + MT) * 1024);
-      float sw[NT], sa[MT][4];
+      i32x4 fa0[MP], fa1[MP], fb0[NP], fb1[NP];
+      float sw[NP];
+      f32x4 sa[MP];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) sw[j] = sb[8 * r8 + j];
+      for (int mp = 0; mp < MP; ++mp) {
+        fa0[mp] = frag(base, ablk + 2 * mp, grp);
+        fa1[mp] = frag(base, ablk + 2 * mp, grp + 4);
+        // C rows 4 * grp + i of the pair; the 8-row class repeats its 8 rows
+        sa[mp] = *reinterpret_cast<const f32x4*>(sb + 64 + (MT > 1 ? 16 * mp + 4 * grp : 4 * (grp & 1)));
+      }
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int np = 0; np < NP; ++np) {
+        fb0[np] = frag(base, bblk + 2 * np, grp);
+        fb1[np] = frag(base, bblk + 2 * np, grp + 4);
+        sw[np] = sb[16 * np + n16];
+      }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sa[mt][i] = sb[64 + mt * 8 + 4 * ((lane >> 4) & 1) + i];
+      for (int mp = 0; mp < MP; ++mp)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+        for (int np = 0; np < NP; ++np) {
+          const f32x4 pr = F::mma128(fa0[mp], fa1[mp], fb0[np], fb1[np]);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          // a 16-byte chunk is 16 fp8 values: two 16x16x32 MFMAs (8 bytes per lane each)
-          f32x4 pr = {0.f, 0.f, 0.f, 0.f};
-          pr = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(((const long*)&av[mt])[0], ((const long*)&b[j])[0], pr, 0, 0, 0);
-          pr = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(((const long*)&av[mt])[1], ((const long*)&b[j])[1], pr, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mt][j][i] = fmaf(pr[i], sa[mt][i] * sw[j], acc[mt][j][i]);
+          for (int i = 0; i < 4; ++i) acc[mp][np][i] = fmaf(pr[i], sa[mp][i] * sw[np], acc[mp][np][i]);
         }
     }
   };
@@ -392,7 +417,28 @@ __device__ __forceinline__ void skinny_ring(const Args& a, const Group& gr, int 
     compute(ring + slot * R::WIN);
     slot = slot + 1 == D ? 0 : slot + 1;
   }
-  skinny_epilogue<DT, MODE, MT, NT, NT>(a, gr, it, 0, lane, acc);
+
+  // epilogue: lane holds C rows 4 * grp + i of each M pair, column n16 of each N pair
+#pragma unroll
+  for (int mp = 0; mp < MP; ++mp) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * mp + 4 * grp + i;
+      if (r >= gr.m || r >= 8 * MT) continue;
+      if (MODE == 1) {
+        const size_t hrow = (size_t)(gr.slot0 + r) * a.I;
+#pragma unroll
+        for (int np = 0; np < NP / 2; ++np)   // gate pair np, up pair np + NP / 2
+          store_h<DT>(a.h, hrow + it * cols_per_item + 16 * np + n16,
+                      silu(acc[mp][np][i]) * acc[mp][np + NP / 2][i]);
+      } else {
+        uint8_t* ybase = gr.routed ? a.y_sorted : a.y_shared;
+        const size_t yrow = (size_t)out_row(a, gr, r) * a.H;
+#pragma unroll
+        for (int np = 0; np < NP; ++np) store_y<DT>(ybase, yrow + it * cols_per_item + 16 * np + n16, acc[mp][np][i]);
+      }
+    }
+  }
 }
 
 // All NT tiles of an item with MT M tiles: NT / NTP passes.
