@@ -3,27 +3,25 @@
 // Perplexity's "Lower latency and higher throughput with multi-node DeepSeek
 // deployment" (section "GroupGEMM") finds the grouped GEMM bandwidth-bound
 // while the rows per expert are few; here each weight byte is read from HBM
-// exactly once, straight into MFMA registers, against the group's rows.
+// exactly once, in whole 128-byte cache lines, against the group's rows.
+//
+// Routed groups stream through a per-wave LDS ring (skinny_ring below).  The
+// decode shared expert of 17..32 tokens streams straight into registers
+// (skinny_pass), with this layout: one wave load instruction covers 8 weight
+// rows x one 128-byte window: lane l reads row (l % 8), 16-byte chunk c(l) =
+// 4 * ((l >> 3) & 1) + (l >> 4).  Fed as the B operand of a 16x16 MFMA,
+// column n (lane l % 16) thus holds weight row n % 8, and columns n and n + 8
+// hold the two complementary 64-byte halves of the window.  The A operand
+// mirrors this: M row m holds token m % 8 with the same chunk rule.  The
+// diagonal 8x8 blocks of the 16x16 result are then the two K halves of the
+// same (token, row) dot products and the off-diagonal blocks are discarded:
+// out[t][r] = C[t][r] + C[t+8][r+8], which sits in lanes L and L ^ 40.
 
 #include "ffn.h"
 
 namespace {
 
 using namespace moe::ffn;
-
-//
-// Streaming layout.  A weight row is read in 128-byte windows (one cache
-// line).  One wave load instruction covers 8 weight rows x one window: lane l
-// reads row (l % 8), 16-byte chunk c(l) = 4 * ((l >> 3) & 1) + (l >> 4).  Fed
-// as the B operand of a 16x16 MFMA, column n (lane l % 16) thus holds weight
-// row n % 8, and columns n and n + 8 hold the two complementary 64-byte halves
-// of the window.  The A operand mirrors this: M row m holds token m % 8 with
-// the same chunk rule.  The diagonal 8x8 blocks of the 16x16 result are then
-// the two K halves of the same (token, row) dot products and the off-diagonal
-// blocks are discarded: out[t][r] = C[t][r] + C[t+8][r+8], which sits in lanes
-// L and L ^ 40.  Half of each MFMA is wasted, which costs nothing in this
-// bandwidth-bound regime, and every load instruction reads whole cache lines.
-
 
 // Weights are read exactly once: nontemporal loads keep them from displacing
 // the reused activation rows in the caches.
@@ -453,20 +451,15 @@ __device__ __forceinline__ void skinny_tile(const Args& a, const Group& gr, int 
 
 // Routed skinny groups of class CLS (MT = 1, 2, 4 M tiles of 8 tokens).
 // One wave = one work item (group, column block of kSkNT weight tiles) in a
-// single pass over K; waves past the class's list exit at once.  Every class
-// uses the same wide items: each activation fragment then serves 8 weight
-// tiles, which keeps the activation re-reads (one per item) a small share of
-// the load instructions even at 32 rows.
-// Which routed classes stream through the LDS ring (measured on MI355X):
-// every GEMM1 class, every fp8 class, and the 17..32-row class.  bf16/fp32
-// GEMM2 items of up to 16 rows are short (K = I) and run faster with four
-// register-streaming waves per SIMD than with one ring wave.
-template <int DT, int MODE, int CLS> constexpr bool sk_use_ring() {
-  return MODE == 1 || CLS == 2 || DT == MOE_FP8_E4M3;
-}
-constexpr int kRingDepth = 3;   // windows in flight per wave
-template <int DT, int MODE, int CLS> constexpr size_t sk_ring_bytes() {
-  return sk_use_ring<DT, MODE, CLS>() ? (size_t)4 * kRingDepth * RingCfg<DT, 1 << CLS, kSkNT>::WIN : 0;
+// single pass over K through its LDS ring; waves past the class's list exit
+// at once.  Every class uses the same wide items: each activation block then
+// serves 8 weight tiles, which keeps the activation re-reads (one per item) a
+// small share of the loads even at 32 rows.  The ring (3 windows x 9..12.5 KB
+// per wave) takes 108..150 KB per workgroup: one workgroup per CU, one wave
+// per SIMD.
+constexpr int kRingDepth = 3;   // K windows in flight per wave
+template <int DT, int CLS> constexpr size_t sk_ring_bytes() {   // 4 waves per workgroup
+  return (size_t)4 * kRingDepth * RingCfg<DT, 1 << CLS, kSkNT>::WIN;
 }
 
 template <int DT, int MODE, int CLS>
@@ -492,11 +485,8 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(Args a) {
   int g;
   const Group gr = group_of_entry(a, a.plan[kPlanHead + CLS * 2 * a.G + gi], &g);
   const int it = item - gi * items;
-  if constexpr (sk_use_ring<DT, MODE, CLS>()) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t sk_ring[];
-    skinny_ring<DT, MODE, MT, NT, kRingDepth>(a, gr, g, it, lane, sk_ring + wave * kRingDepth * RingCfg<DT, MT, NT>::WIN);
-  } else
-    skinny_pass<DT, MODE, MT, NT, NT, 1, 1>(a, gr, g, it, 0, lane, 0, nullptr);
+  extern __shared__ __attribute__((aligned(16))) uint8_t sk_ring[];
+  skinny_ring<DT, MODE, MT, NT, kRingDepth>(a, gr, g, it, lane, sk_ring + wave * kRingDepth * RingCfg<DT, MT, NT>::WIN);
 }
 
 // The shared expert when T <= kSkinnyRows: its row count is known on the
@@ -514,16 +504,14 @@ __global__ __launch_bounds__(64 * kShKS) void ffn_shared_skinny_kernel(Args a) {
 
 template <int DT, int MODE, int CLS>
 hipError_t launch_sk(const char* name, unsigned grid, const Args& a, hipStream_t st) {
-  constexpr size_t lds = sk_ring_bytes<DT, MODE, CLS>();
+  constexpr size_t lds = sk_ring_bytes<DT, CLS>();
   static_assert(lds <= 160 * 1024, "LDS budget");
-  if constexpr (lds > 0) {
-    static bool attr_set = false;   // raise the dynamic-LDS limit once per process
-    if (!attr_set) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_skinny_kernel<DT, MODE, CLS>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      attr_set = true;
-    }
+  static bool attr_set = false;   // raise the dynamic-LDS limit once per process
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_skinny_kernel<DT, MODE, CLS>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
   }
   MOE_LAUNCH(name, (ffn_skinny_kernel<DT, MODE, CLS>), dim3(grid), dim3(256), lds, st, a);
   return hipGetLastError();
