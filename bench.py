@@ -61,12 +61,14 @@ def kernel_models(cfg, counts):
     m = {f"ffn_gemm{g}_{r}": {"bytes": 0, "flops": 0} for g in (1, 2) for r in regions}
     # (rows, region): a group of > 32 rows takes 256-row tiles; with fp8
     # weights only its floor(m / 256) full tiles do, and its other m mod 256
-    # rows take the 128-row kernel.  Each kernel that serves a group streams
+    # rows take the 128-row kernel (routed groups: when they are at most 128,
+    # else one more 256-row tile).  Each kernel that serves a group streams
     # that group's weights once.
     def tiled(mg, pre):
-        if not fp8:
+        rest = mg % 256
+        if not fp8 or (not pre and rest > 128):
             return [(mg, pre + "tiled")]
-        return [(mg // 256 * 256, pre + "tiled"), (mg % 256, pre + "tiled128")]
+        return [(mg - rest, pre + "tiled"), (rest, pre + "tiled128")]
     items = []
     for mg in [int(c) for c in counts]:
         if mg <= SKINNY_ROWS:

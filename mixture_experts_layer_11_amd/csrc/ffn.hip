@@ -50,7 +50,8 @@ __global__ __launch_bounds__(512) void ffn_plan_kernel(Args a) {
   if (g < a.G) m = g < a.E ? a.offsets[g + 1] - a.offsets[g] : a.T;
   // skinny class: 0 for 1..8 rows, 1 for 9..16, 2 for 17..32; larger groups
   // take floor(m / 256) full tiles, and their last m mod 256 rows one more
-  // 256-row tile or (mid_rest) ceil((m mod 256) / 128) 128-row tiles.  The
+  // 256-row tile, or with mid_rest one 128-row tile if they are at most 128
+  // (one 256-row tile above that, which reads the weights once).  The
   // shared expert has launches of its own, except in halves mode (T <= 16):
   // there every group, the shared expert included, enters the <= 8-row list
   // as one or two 8-row halves, so the other lists stay empty.
@@ -59,8 +60,10 @@ __global__ __launch_bounds__(512) void ffn_plan_kernel(Args a) {
   const int cls = listed ? (a.halves || m <= 8 ? 0 : m <= 16 ? 1 : 2) : -1;
   const int nent = cls < 0 ? 0 : (a.halves ? (m + 7) / 8 : 1);   // list entries of this group
   const bool tiled = m > kSkinnyRows && !shared;
-  const int tiles = tiled ? (a.mid_rest ? m / kTileRows : (m + kTileRows - 1) / kTileRows) : 0;
-  const int mids = tiled && a.mid_rest ? (m % kTileRows + kMidRows - 1) / kMidRows : 0;
+  const int rest = m % kTileRows;
+  const bool rest_fat = a.mid_rest && rest > kMidRows;   // one partial 256-row tile reads the weights once
+  const int tiles = tiled ? (a.mid_rest ? m / kTileRows + (rest_fat ? 1 : 0) : (m + kTileRows - 1) / kTileRows) : 0;
+  const int mids = tiled && a.mid_rest && !rest_fat ? (rest + kMidRows - 1) / kMidRows : 0;
 #pragma unroll
   for (int c = 0; c < 3; ++c) sk[c][g] = cls == c ? nent : 0;
   ft[g] = tiles;
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(512) void ffn_plan_kernel(Args a) {
   const int m0 = mt[g] - mids;
   for (int i = 0; i < mids; ++i) {
     mid[2 * (m0 + i)] = g;
-    mid[2 * (m0 + i) + 1] = tiles * kTileRows + i * kMidRows;
+    mid[2 * (m0 + i) + 1] = (m / kTileRows) * kTileRows + i * kMidRows;
   }
 }
 
@@ -139,11 +142,12 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st) {
   const int P = a.P;
   // Upper bounds of the tile lists: a token picks k distinct experts, so a
   // routed group has at most T rows and none is tiled when T <= kSkinnyRows.
-  // Otherwise at most P / 256 full tiles, and at most two 128-row tiles per
-  // tiled group, of which there are at most min(E, P / (kSkinnyRows + 1)).
+  // Otherwise at most P / 256 full tiles plus one partial tile per tiled
+  // group (256 rows, or with mid_rest 128 rows), of which there are at most
+  // min(E, P / (kSkinnyRows + 1)).
   const int tiled_groups = c.T > kSkinnyRows ? (P / (kSkinnyRows + 1) < c.E ? P / (kSkinnyRows + 1) : c.E) : 0;
-  const int max_fat = tiled_groups > 0 ? P / kTileRows + (a.mid_rest ? 0 : tiled_groups) : 0;
-  const int max_mid = a.mid_rest ? 2 * tiled_groups : 0;
+  const int max_fat = tiled_groups > 0 ? P / kTileRows + tiled_groups : 0;
+  const int max_mid = a.mid_rest ? tiled_groups : 0;
   // halves mode: the shared expert's rows [P, P + T) of h are the routed lists' too
   const int qrows = P + (a.halves && a.has_shared ? c.T : 0);
   for (int mode = 1; mode <= 2; ++mode) {
@@ -215,13 +219,13 @@ hipError_t run_ffn(const moe_cfg& c, const Args& a, hipStream_t st) {
 namespace moe {
 
 // Capacity of the 256-row tile list: at most P / 256 full tiles, plus one
-// partial tile per routed group unless those rows take 128-row tiles.
-int ffn_fat_cap(const moe_cfg& c) { return c.T * c.k / kTileRows + (c.w_dtype == MOE_FP8_E4M3 ? 0 : c.E); }
+// partial tile per routed group.
+int ffn_fat_cap(const moe_cfg& c) { return c.T * c.k / kTileRows + c.E; }
 
 size_t ffn_plan_ints(const moe_cfg& c) {
   const int G = c.E + (c.I_shared > 0 ? 1 : 0);
-  // three skinny lists of up to 2G entries (halves); 128-row tiles: at most two per routed group
-  return kPlanHead + 6 * (size_t)G + 2 * (size_t)ffn_fat_cap(c) + 2 * (size_t)(2 * c.E);
+  // three skinny lists of up to 2G entries (halves); 128-row tiles: at most one per routed group
+  return kPlanHead + 6 * (size_t)G + 2 * (size_t)ffn_fat_cap(c) + 2 * (size_t)c.E;
 }
 
 size_t ffn_h_elem_bytes(const moe_cfg& c) { return c.w_dtype == MOE_BF16 ? 2 : 4; }
