@@ -17,8 +17,13 @@ resident in HBM.  Prints ONE JSON line:
              `traffic` is the measured HBM bytes per launch from rocprofv3
              counters (profiles/traffic_<kernel>_<workload>.json) when those
              were taken on the current kernel source, else null.
+* step_spread  median / p10 / p90 of single steps, each bracketed by HIP
+             events, in a pass of its own after the timed steps.
+* input_gen_s  seconds spent drawing the synthetic inputs (outside every
+             timed figure).
 * cpu_baseline  the fp64 oracle timed on the host on a bounded sample of the
-             same workload (first n tokens, single thread), as tokens/s.
+             same workload (first n tokens, single thread), as tokens/s,
+             with the host's CPU model, logical CPUs and RAM.
 
 Only one GPU is used; --gpus above 1 exits with a message.
 """
@@ -36,6 +41,8 @@ METRIC = "MoE-layer tokens/s at 1 GPU + achieved HBM GB/s (decode) / MFMA % (pre
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 SKINNY_ROWS = 32          # groups with at most this many rows take the streaming (skinny) kernels
+
+
 def kernel_models(cfg, counts):
     """Algorithmic bytes and FLOPs of each kernel per launch, from the counts.
 
@@ -56,8 +63,7 @@ def kernel_models(cfg, counts):
     sc13 = (2 * I // br) * (H // qb) * 4 if fp8 else 0
     sc2 = (H // br) * (I // qb) * 4 if fp8 else 0
     groups = [int(c) for c in counts]
-    regions = ("skinny_m8", "skinny_m16", "skinny_m32", "tiled", "tiled128", "shared_skinny", "shared_tiled",
-               "shared_tiled128")
+    regions = ("skinny", "tiled", "tiled128", "shared_skinny", "shared_tiled", "shared_tiled128")
     m = {f"ffn_gemm{g}_{r}": {"bytes": 0, "flops": 0} for g in (1, 2) for r in regions}
     # (rows, region): a group of > 32 rows takes 256-row tiles; with fp8
     # weights only its floor(m / 256) full tiles do, and its other m mod 256
@@ -72,7 +78,7 @@ def kernel_models(cfg, counts):
     items = []
     for mg in [int(c) for c in counts]:
         if mg <= SKINNY_ROWS:
-            items.append((mg, "skinny_m8" if mg <= 8 else "skinny_m16" if mg <= 16 else "skinny_m32"))
+            items.append((mg, "skinny"))
         else:
             items += tiled(mg, "")
     if cfg.I_shared:
@@ -116,6 +122,23 @@ def traffic_for(kernel, workload):
     if d.get("source_hash") != kernel_source_hash(kernel):
         return None
     return d.get("bytes_per_launch")
+
+
+def host_info():
+    """CPU model, logical CPUs and RAM of the host the oracle is timed on."""
+    model, ram_gb = None, None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemTotal"):
+                ram_gb = round(int(line.split()[1]) / 2**20, 1)
+                break
+    except OSError:
+        pass
+    return {"cpu": model, "nproc": os.cpu_count(), "ram_gib": ram_gb}
 
 
 def cpu_baseline(inp_gpu, n_tokens):
@@ -170,7 +193,10 @@ def main(argv=None):
         return 1
     moe.load_library()
     cfg = get_config(args.workload)
+    tg = time.perf_counter()
     inp = make_inputs(cfg, "cuda")
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - tg   # input generation, reported apart from every timed figure
     mc = moe.cfg_from(cfg)
     ws = moe.alloc_workspace(mc)
     w = moe.Weights.from_inputs(inp)
@@ -239,6 +265,18 @@ def main(argv=None):
     roof["kernel_avg_us"] = round(avg_ms * 1e3, 2)
     roof["algorithmic_per_launch"] = models.get(dom, {})
 
+    # per-step spread, in a pass of its own after the timed region: each step
+    # bracketed by events on the caller's stream (the side stream joins it)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a0, a1 in evs:
+        a0.record()
+        step()
+        a1.record()
+    torch.cuda.synchronize()
+    per_step = sorted(a0.elapsed_time(a1) for a0, a1 in evs)
+    pct = lambda q: per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]   # noqa: E731
+    step_spread = {"median_ms": round(pct(0.5), 4), "p10_ms": round(pct(0.1), 4), "p90_ms": round(pct(0.9), 4)}
+
     layer_gbps = layer["bytes"] / (ms_per_step * 1e-3) / 1e9
     layer_tflops = layer["flops"] / (ms_per_step * 1e-3) / 1e12
 
@@ -279,7 +317,7 @@ def main(argv=None):
     if not (args.no_cpu_baseline or args.quick):
         n = min(args.cpu_tokens, cfg.T)
         dt = cpu_baseline(inp, n)
-        cpu = {"value": round(n / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        cpu = {"value": round(n / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle", "host": host_info(),
                "sample": f"first {n} of {cfg.T} tokens of {cfg.name}: fp64 numpy oracle, token by token "
                          f"(routing, fp64 upcast of each touched expert, SwiGLU, weighted sum), 1 thread, "
                          f"inputs already in host memory; {dt:.2f} s"}
@@ -305,6 +343,8 @@ def main(argv=None):
                   "hbm_frac": round(layer_gbps / HBM_PEAK_GBPS, 4), "TFLOPs": round(layer_tflops, 2),
                   "gpu_event_ms_per_step": round(gpu_ms / args.steps, 4)},
         "kernels": {n: kernel_line(n, v, models) for n, v in sorted(breakdown.items())},
+        "step_spread": step_spread,
+        "input_gen_s": round(gen_s, 2),
         "graph": graph_line,
         "routing_stats": routing_stats,
         "cpu_baseline": cpu,

@@ -129,9 +129,9 @@ constexpr int kTN = 256;   // tiled GEMM: tile columns (weight rows; GEMM1: 128 
 
 // Launchers (explicitly instantiated for MOE_F32, MOE_BF16, MOE_FP8_E4M3).
 // mode 1 = gate/up GEMM with SwiGLU, mode 2 = down GEMM.
-// Routed skinny class cls (0: 1..8 rows, 1: 9..16, 2: 17..32) over `grid` workgroups.
+// The routed skinny classes (1..8, 9..16, 17..32 rows) in one launch of `grid` workgroups.
 template <int DT>
-hipError_t launch_skinny(int mode, int cls, unsigned grid, const Args& a, hipStream_t st);
+hipError_t launch_skinny(int mode, unsigned grid, const Args& a, hipStream_t st);
 // The shared expert when T <= kSkinnyRows.
 template <int DT>
 hipError_t launch_shared_skinny(int mode, int T, const Args& a, hipStream_t st);

@@ -158,6 +158,7 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st) {
     }
     const int N = mode == 1 ? c.I : c.H;
     const long long items = N / ((mode == 1 ? 4 : 8) * kSkNT);   // skinny items per group
+    long long bands = 0;   // workgroups per XCD over the three class bands (the kernel's order)
     for (int cls = 0; cls < 3; ++cls) {
       // a group of class cls has at least 1, 9 or 17 rows, and no group has
       // more than T rows (a token picks k distinct experts)
@@ -168,9 +169,9 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st) {
         groups = (P < 2 * c.E ? P : 2 * c.E) + (a.has_shared ? 2 : 0);
       }
       if (groups == 0 || min_rows > c.T) continue;
-      const unsigned grid = (unsigned)((moe::ceil_div(groups * items, 4LL) + 7) & ~7LL);   // 4 items per workgroup
-      if ((e = launch_skinny<DT>(mode, cls, grid, a, st)) != hipSuccess) return e;
+      bands += moe::ceil_div(moe::ceil_div(groups * items, 4LL), 8LL);   // 4 items per workgroup
     }
+    if (bands > 0 && (e = launch_skinny<DT>(mode, (unsigned)(8 * bands), a, st)) != hipSuccess) return e;
     const int ntn = mode == 1 ? moe::ceil_div(c.I, kTN / 2) : moe::ceil_div(c.H, kTN);
     if (max_fat > 0 && (e = launch_tiled<DT>(mode, false, kTileRows, (unsigned)(max_fat * ntn), ntn, a, st)) != hipSuccess)
       return e;

@@ -458,35 +458,43 @@ __device__ __forceinline__ void skinny_tile(const Args& a, const Group& gr, int 
 // per wave) takes 108..150 KB per workgroup: one workgroup per CU, one wave
 // per SIMD.
 constexpr int kRingDepth = 3;   // K windows in flight per wave
-template <int DT, int CLS> constexpr size_t sk_ring_bytes() {   // 4 waves per workgroup
-  return (size_t)4 * kRingDepth * RingCfg<DT, 1 << CLS, kSkNT>::WIN;
-}
+constexpr size_t sk_ring_bytes(int wave_win) { return (size_t)4 * kRingDepth * wave_win; }   // 4 waves
 
-template <int DT, int MODE, int CLS>
+// One launch for the three row classes.  Workgroups reach the 8 XCDs
+// round-robin (blockIdx % 8).  Each class takes a contiguous band of
+// blockIdx, the 17..32-row class first (its items take longest, so they
+// start first), then 9..16, then 1..8 rows; inside a band XCD x takes the
+// contiguous range x * per_xcd ... of the class's items, so the items of a
+// group run on one or two XCDs and its activation rows, re-read by every
+// item, stay in that XCD's L2.  The 4 waves of a workgroup are independent
+// (each streams its own item through its own ring, sized for 32 rows), so a
+// workgroup may straddle two groups or classes.  Bands are sized from the
+// device-side list lengths; the host sizes the grid from upper bounds and
+// workgroups past the bands exit at once.
+template <int DT, int MODE>
 __global__ __launch_bounds__(256) void ffn_skinny_kernel(Args a) {
-  constexpr int MT = 1 << CLS;
   constexpr int NT = kSkNT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cols_per_item = MODE == 1 ? 4 * NT : 8 * NT;
   const int items = (MODE == 1 ? a.I : a.H) / cols_per_item;
-  // XCD-aware order: workgroups go to the 8 XCDs round-robin (blockIdx % 8),
-  // so XCD x takes the contiguous range x * per_xcd ... of the class's real
-  // work.  The items of a group then run on one or two XCDs and its
-  // activation rows, re-read by every item, stay in that XCD's L2 instead of
-  // being fetched into all eight.  The grid is a multiple of 8 and at least
-  // 8 * per_xcd workgroups.
-  const int real_wg = (a.plan[CLS] * items + 3) >> 2;
-  const int per_xcd = (real_wg + 7) >> 3;
-  const int local = blockIdx.x >> 3;
-  if (local >= per_xcd) return;
+  int local = blockIdx.x >> 3, cls = 2, n = 0, per_xcd = 0;
+  for (; cls >= 0; --cls) {
+    n = a.plan[cls] * items;                  // items of this class
+    per_xcd = (((n + 3) >> 2) + 7) >> 3;      // its workgroups per XCD
+    if (local < per_xcd) break;
+    local -= per_xcd;
+  }
+  if (cls < 0) return;
   const int item = ((blockIdx.x & 7) * per_xcd + local) * 4 + wave;
-  const int gi = item / items;
-  if (gi >= a.plan[CLS]) return;
+  if (item >= n) return;
+  const int gi = item / items, it = item - gi * items;
   int g;
-  const Group gr = group_of_entry(a, a.plan[kPlanHead + CLS * 2 * a.G + gi], &g);
-  const int it = item - gi * items;
+  const Group gr = group_of_entry(a, a.plan[kPlanHead + cls * 2 * a.G + gi], &g);
   extern __shared__ __attribute__((aligned(16))) uint8_t sk_ring[];
-  skinny_ring<DT, MODE, MT, NT, kRingDepth>(a, gr, g, it, lane, sk_ring + wave * kRingDepth * RingCfg<DT, MT, NT>::WIN);
+  uint8_t* ring = sk_ring + wave * kRingDepth * RingCfg<DT, 4, NT>::WIN;
+  if (cls == 2) skinny_ring<DT, MODE, 4, NT, kRingDepth>(a, gr, g, it, lane, ring);
+  else if (cls == 1) skinny_ring<DT, MODE, 2, NT, kRingDepth>(a, gr, g, it, lane, ring);
+  else skinny_ring<DT, MODE, 1, NT, kRingDepth>(a, gr, g, it, lane, ring);
 }
 
 // The shared expert when T <= kSkinnyRows: its row count is known on the
@@ -502,34 +510,20 @@ __global__ __launch_bounds__(64 * kShKS) void ffn_shared_skinny_kernel(Args a) {
   skinny_tile<DT, MODE, MT, kShNT, kShKS>(a, gr, a.E, blockIdx.x, lane, ks, red);
 }
 
-template <int DT, int MODE, int CLS>
-hipError_t launch_sk(const char* name, unsigned grid, const Args& a, hipStream_t st) {
-  constexpr size_t lds = sk_ring_bytes<DT, CLS>();
+template <int DT, int MODE>
+hipError_t launch_sk(unsigned grid, const Args& a, hipStream_t st) {
+  constexpr size_t lds = sk_ring_bytes(RingCfg<DT, 4, kSkNT>::WIN);
   static_assert(lds <= 160 * 1024, "LDS budget");
   static bool attr_set = false;   // raise the dynamic-LDS limit once per process
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_skinny_kernel<DT, MODE, CLS>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_skinny_kernel<DT, MODE>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  MOE_LAUNCH(name, (ffn_skinny_kernel<DT, MODE, CLS>), dim3(grid), dim3(256), lds, st, a);
+  MOE_LAUNCH(MODE == 1 ? "ffn_gemm1_skinny" : "ffn_gemm2_skinny", (ffn_skinny_kernel<DT, MODE>), dim3(grid), dim3(256),
+             lds, st, a);
   return hipGetLastError();
-}
-
-template <int DT>
-hipError_t launch_skinny_t(int mode, int cls, unsigned grid, const Args& a, hipStream_t st) {
-  static const char* const kName[2][3] = {
-      {"ffn_gemm1_skinny_m8", "ffn_gemm1_skinny_m16", "ffn_gemm1_skinny_m32"},
-      {"ffn_gemm2_skinny_m8", "ffn_gemm2_skinny_m16", "ffn_gemm2_skinny_m32"}};
-  const char* name = kName[mode - 1][cls];
-#define MOE_SK(M, CLS) return launch_sk<DT, M, CLS>(name, grid, a, st)
-  if (mode == 1) {
-    if (cls == 0) MOE_SK(1, 0); else if (cls == 1) MOE_SK(1, 1); else MOE_SK(1, 2);
-  } else {
-    if (cls == 0) MOE_SK(2, 0); else if (cls == 1) MOE_SK(2, 1); else MOE_SK(2, 2);
-  }
-#undef MOE_SK
 }
 
 template <int DT>
@@ -553,8 +547,8 @@ namespace moe {
 namespace ffn {
 
 template <int DT>
-hipError_t launch_skinny(int mode, int cls, unsigned grid, const Args& a, hipStream_t st) {
-  return launch_skinny_t<DT>(mode, cls, grid, a, st);
+hipError_t launch_skinny(int mode, unsigned grid, const Args& a, hipStream_t st) {
+  return mode == 1 ? launch_sk<DT, 1>(grid, a, st) : launch_sk<DT, 2>(grid, a, st);
 }
 template <int DT>
 hipError_t launch_shared_skinny(int mode, int T, const Args& a, hipStream_t st) {
@@ -562,7 +556,7 @@ hipError_t launch_shared_skinny(int mode, int T, const Args& a, hipStream_t st) 
 }
 
 #define MOE_INST(DT)                                                                                \
-  template hipError_t launch_skinny<DT>(int, int, unsigned, const Args&, hipStream_t);              \
+  template hipError_t launch_skinny<DT>(int, unsigned, const Args&, hipStream_t);                   \
   template hipError_t launch_shared_skinny<DT>(int, int, const Args&, hipStream_t);
 MOE_INST(MOE_F32)
 MOE_INST(MOE_BF16)

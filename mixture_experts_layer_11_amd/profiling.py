@@ -1,7 +1,7 @@
 """Profiling helpers: library kernel names, rocprofv3 names, counter summaries.
 
 The library's profiler (moe_profile_start/stop) names kernels by role
-("ffn_gemm1_skinny_m8", ...); rocprofv3 reports demangled template names.
+("ffn_gemm1_skinny", ...); rocprofv3 reports demangled template names.
 ``rocprof_name`` maps one to the other for a given weight dtype, and
 ``kernel_source_hash`` fingerprints the sources a kernel is built from, so a
 stored counter reading is only used while the kernel is unchanged.
@@ -10,7 +10,7 @@ CLI (writes profiles/<kernel>_<workload>.md and
 profiles/traffic_<kernel>_<workload>.json from rocprofv3 CSV output):
 
   python -m mixture_experts_layer_11_amd.profiling --workload decode16 \\
-      --kernel ffn_gemm1_skinny_m8 --stats RUN_kernel_stats.csv \\
+      --kernel ffn_gemm1_skinny --stats RUN_kernel_stats.csv \\
       --fetch FETCH_counter_collection.csv --write WRITE_counter_collection.csv \\
       --copy-fetch COPYF.csv --copy-write COPYW.csv --copy-bytes 1073741824 \\
       --bench-log BENCH.log --command "..." [--command "..."]
@@ -27,7 +27,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 
 KERNEL_SOURCES = {
-    **{f"ffn_gemm{g}_skinny_m{m}": "ffn_skinny.hip" for g in (1, 2) for m in (8, 16, 32)},
+    "ffn_gemm1_skinny": "ffn_skinny.hip", "ffn_gemm2_skinny": "ffn_skinny.hip",
     "ffn_gemm1_shared_skinny": "ffn_skinny.hip", "ffn_gemm2_shared_skinny": "ffn_skinny.hip",
     **{f"ffn_gemm{g}_{s}tiled{t}": "ffn_tiled.hip" for g in (1, 2) for s in ("", "shared_") for t in ("", "128")},
     "ffn_plan": "ffn.hip",
@@ -54,10 +54,8 @@ def kernel_source_hash(kernel: str) -> str:
 def rocprof_name(kernel: str, w_dtype: str) -> str:
     """Prefix of the demangled name rocprofv3 reports for a library kernel."""
     dt = _DT[w_dtype]
-    if kernel.startswith("ffn_gemm") and "_skinny_m" in kernel:
-        mode = int(kernel[8])
-        cls = {"8": 0, "16": 1, "32": 2}[kernel.rsplit("_m", 1)[1]]
-        return f"void (anonymous namespace)::ffn_skinny_kernel<{dt}, {mode}, {cls}>"
+    if kernel in ("ffn_gemm1_skinny", "ffn_gemm2_skinny"):
+        return f"void (anonymous namespace)::ffn_skinny_kernel<{dt}, {int(kernel[8])}>"
     if kernel.startswith("ffn_gemm") and "_tiled" in kernel:
         shared = "true" if "_shared_" in kernel else "false"
         tm = 128 if kernel.endswith("128") else 256

@@ -63,6 +63,13 @@ SMALL = {
                                                         I_shared=256),
     "t12_fp8_tiles": get_config("decode16_fp8").with_(name="t12_fp8_tiles", T=12, H=512, E=16, k=2, I=256,
                                                       I_shared=256),
+    # fp8 groups of ~150 and ~350 rows: a partial 256-row tile for 129..255 rows left, a 128-row tile below.
+    # I = 2048 as in the real layer: one h code that rounds the other way at a boundary (fp32 vs fp64 h)
+    # moves a whole y row by ~ulp / sqrt(I), which at I = 256 can reach the 6e-2 element bound.
+    "fp8_rest_tiles": get_config("clustered2048_fp8").with_(name="fp8_rest_tiles", routing="random", T=300, H=512,
+                                                           E=4, k=2, I=2048, I_shared=2048),
+    "fp8_full_and_rest": get_config("decode16_fp8").with_(name="fp8_full_and_rest", T=700, H=512, E=4, k=2,
+                                                         I=2048, I_shared=2048),
 }
 
 
