@@ -4,31 +4,45 @@
 //
 // y[t] = y_shared[t] + sum_j w[t,j] * y_sorted[pair_slot[t*k + j]], fp32
 // accumulation in the fixed order shared, j = 0..k-1.  Inputs and output are
-// in the activation dtype.  One workgroup per token; each thread owns 4
-// consecutive hidden columns.
+// in the activation dtype; every row is read once (nontemporal loads).
 
 #include "moe_common.h"
 #include "moe_launch.h"
 
 namespace {
 
+// 8 consecutive values of a row as fp32 (16 bytes of bf16, 32 of fp32).
 template <int DT>
-__device__ __forceinline__ f32x4 load4(const void* base, size_t idx) {
+__device__ __forceinline__ void load8(const void* base, size_t idx, float (&v)[8]) {
   if constexpr (DT == MOE_BF16) {
-    const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
-    return f32x4{bf16_to_f32((uint16_t)v.x), bf16_to_f32((uint16_t)(v.x >> 16)), bf16_to_f32((uint16_t)v.y),
-                 bf16_to_f32((uint16_t)(v.y >> 16))};
+    const i32x4 q = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(base) + idx));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32((uint16_t)q[i]);
+      v[2 * i + 1] = bf16_to_f32((uint16_t)((uint32_t)q[i] >> 16));
+    }
   } else {
-    return *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + idx);
+    const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + idx);
+    const f32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = a[i];
+      v[4 + i] = b[i];
+    }
   }
 }
 
-template <int OUT_DT>
+// One workgroup per token; each thread owns 8 consecutive hidden columns per
+// step.  KT = k when the launch knows it at compile time (k = 8, the layer's
+// top-8), else 0: with a fixed k the k row loads of a step are all issued
+// before the first FMA, so a thread keeps k + 1 loads in flight.
+template <int OUT_DT, int KT>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y_sorted,
                                                       const void* __restrict__ y_shared,
                                                       const int32_t* __restrict__ pair_slot,
-                                                      const float* __restrict__ topk_w, int H, int k,
+                                                      const float* __restrict__ topk_w, int H, int k_rt,
                                                       void* __restrict__ y) {
+  const int k = KT > 0 ? KT : k_rt;
   const int t = blockIdx.x;
   __shared__ int slot[64];
   __shared__ float wt[64];
@@ -37,22 +51,40 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     wt[threadIdx.x] = topk_w[(size_t)t * k + threadIdx.x];
   }
   __syncthreads();
-  for (int c = threadIdx.x * 4; c < H; c += blockDim.x * 4) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (y_shared) acc = load4<OUT_DT>(y_shared, (size_t)t * H + c);
-    for (int j = 0; j < k; ++j) {
-      const f32x4 v = load4<OUT_DT>(y_sorted, (size_t)slot[j] * H + c);
-      const float w = wt[j];
+  for (int c = threadIdx.x * 8; c < H; c += blockDim.x * 8) {
+    float acc[8];
+    if (y_shared) {
+      load8<OUT_DT>(y_shared, (size_t)t * H + c, acc);
+    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    }
+    if constexpr (KT > 0) {
+      float v[KT][8];
+#pragma unroll
+      for (int j = 0; j < KT; ++j) load8<OUT_DT>(y_sorted, (size_t)slot[j] * H + c, v[j]);
+#pragma unroll
+      for (int j = 0; j < KT; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wt[j], v[j][i], acc[i]);
+    } else {
+      for (int j = 0; j < k; ++j) {
+        float v[8];
+        load8<OUT_DT>(y_sorted, (size_t)slot[j] * H + c, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wt[j], v[i], acc[i]);
+      }
     }
     if constexpr (OUT_DT == MOE_BF16) {
-      uint16_t* o = static_cast<uint16_t*>(y) + (size_t)t * H + c;
-      const uint32_t lo = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
-      const uint32_t hi = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
-      *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
+      i32x4 q;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        q[i] = (int)((uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16));
+      __builtin_nontemporal_store(q, reinterpret_cast<i32x4*>(static_cast<uint16_t*>(y) + (size_t)t * H + c));
     } else {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(y) + (size_t)t * H + c) = acc;
+      f32x4* o = reinterpret_cast<f32x4*>(static_cast<float*>(y) + (size_t)t * H + c);
+      __builtin_nontemporal_store(f32x4{acc[0], acc[1], acc[2], acc[3]}, o);
+      __builtin_nontemporal_store(f32x4{acc[4], acc[5], acc[6], acc[7]}, o + 1);
     }
   }
 }
@@ -63,12 +95,15 @@ namespace moe {
 
 hipError_t launch_combine(const moe_cfg& c, const void* y_sorted, const void* y_shared,
                           const int32_t* pair_slot, const float* topk_w, void* y, hipStream_t st) {
-  if (c.act_dtype == MOE_BF16)
-    MOE_LAUNCH("combine", combine_kernel<MOE_BF16>, dim3(c.T), dim3(256), 0, st, y_sorted, y_shared, pair_slot, topk_w,
-                       c.H, c.k, y);
-  else
-    MOE_LAUNCH("combine", combine_kernel<MOE_F32>, dim3(c.T), dim3(256), 0, st, y_sorted, y_shared, pair_slot, topk_w,
-                       c.H, c.k, y);
+#define MOE_CB(DT, KT)                                                                                         \
+  MOE_LAUNCH("combine", (combine_kernel<DT, KT>), dim3(c.T), dim3(256), 0, st, y_sorted, y_shared, pair_slot, \
+             topk_w, c.H, c.k, y)
+  if (c.act_dtype == MOE_BF16) {
+    if (c.k == 8) MOE_CB(MOE_BF16, 8); else MOE_CB(MOE_BF16, 0);
+  } else {
+    if (c.k == 8) MOE_CB(MOE_F32, 8); else MOE_CB(MOE_F32, 0);
+  }
+#undef MOE_CB
   return hipGetLastError();
 }
 
