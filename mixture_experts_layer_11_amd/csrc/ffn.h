@@ -118,6 +118,21 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+// vmcnt <= n for a wave-uniform n known only at run time (0 <= n < 48).
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+#define MOE_WC(K) \
+  case K:         \
+    wait_vmcnt<K>(); \
+    break;
+#define MOE_WC8(K) MOE_WC(K) MOE_WC(K + 1) MOE_WC(K + 2) MOE_WC(K + 3) MOE_WC(K + 4) MOE_WC(K + 5) MOE_WC(K + 6) MOE_WC(K + 7)
+  switch (n) {
+    MOE_WC8(0) MOE_WC8(8) MOE_WC8(16) MOE_WC8(24) MOE_WC8(32) MOE_WC8(40)
+    default: wait_vmcnt<0>();
+  }
+#undef MOE_WC8
+#undef MOE_WC
+}
+
 // s_waitcnt lgkmcnt(0) only: this wave's LDS reads have completed.
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
 

@@ -266,18 +266,20 @@ __device__ __forceinline__ void skinny_pass(const Args& a, const Group& gr, int 
 // (tile L / 8, row L % 8) and, for L < 32, the activation scale of group row
 // L; a lane's C values then need the weight scale of its column and the
 // activation scales of 4 consecutive rows per M pair.
-template <int DT, int MT, int NT> struct RingCfg {
+template <int DT, int MT, int NT, int D> struct RingCfg {
   static constexpr bool FP8 = DT == MOE_FP8_E4M3;
-  static constexpr int NL = NT + MT + (FP8 ? 2 : 0);             // direct loads per window
-  static constexpr int WIN = (NT + MT) * 1024 + (FP8 ? 512 : 0);  // LDS bytes per window
-  static constexpr int MP = MT > 1 ? MT / 2 : 1;                  // 16-row M pairs
-  static constexpr int NP = NT / 2;                               // 16-row N pairs
+  static constexpr int NB = NT + MT;                   // 1 KB blocks (direct loads) per window
+  static constexpr int WIN = NB * 1024;                // LDS bytes per ring slot
+  static constexpr int SCL = FP8 ? 4096 : 0;           // fp8 scale area after the D slots
+  static constexpr int WAVE_BYTES = D * WIN + SCL;     // one wave's LDS
+  static constexpr int MP = MT > 1 ? MT / 2 : 1;       // 16-row M pairs
+  static constexpr int NP = NT / 2;                    // 16-row N pairs
 };
 
 template <int DT, int MODE, int MT, int NT, int D>
 __device__ __forceinline__ void skinny_ring(const Args& a, const Group& gr, int g, int it, int lane, uint8_t* ring) {
   using F = Frag<DT>;
-  using R = RingCfg<DT, MT, NT>;
+  using R = RingCfg<DT, MT, NT, D>;
   constexpr bool FP8 = R::FP8;
   constexpr int MP = R::MP, NP = R::NP;
   static_assert(NT % 2 == 0 && (MODE == 2 || NT % 4 == 0), "GEMM1 pairs gate and up 16-row blocks");
@@ -322,15 +324,36 @@ __device__ __forceinline__ void skinny_ring(const Args& a, const Group& gr, int 
     psa = (MODE == 1 ? a.a1s : a.a2s) + (size_t)src_row(lane & 31) * nwin;
   }
 
-  auto issue = [&](uint8_t* base, int w) {
+  // fp8 scales: when nwin % 4 == 0 (K a multiple of 512), one 16-byte load
+  // per lane fetches 4 windows' scales of its row, into one of two 2 KB
+  // blocks (weight scales, then activation scales) of the scale area: each
+  // scale row's cache line is touched once per 4 windows, not every window
+  // (a window's 64 weight scales lie in 64 different rows and lines).  Else
+  // each window's scales go, 4 bytes per lane, into a 512-byte slot per ring
+  // slot.
+  uint8_t* scl = ring + D * R::WIN;
+  const bool blk4 = FP8 && (nwin & 3) == 0;
+  auto loads_of = [&](int w) -> int {   // direct loads of window w
+    return R::NB + (FP8 ? (blk4 ? ((w & 3) == 0 ? 2 : 0) : 2) : 0);
+  };
+  auto issue = [&](int sl, int w) {
+    uint8_t* base = ring + sl * R::WIN;
     const size_t off = (size_t)w * 128;
 #pragma unroll
     for (int j = 0; j < NT; ++j) __builtin_amdgcn_global_load_lds(pb0 + (tile_off[j] + off), base + j * 1024, 16, 0, 2);   // nt
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) __builtin_amdgcn_global_load_lds(pa[mt] + off, base + (NT + mt) * 1024, 16, 0, 0);
     if constexpr (FP8) {
-      __builtin_amdgcn_global_load_lds(psw + w, base + (NT + MT) * 1024, 4, 0, 0);
-      __builtin_amdgcn_global_load_lds(psa + w, base + (NT + MT) * 1024 + 256, 4, 0, 0);
+      if (blk4) {
+        if ((w & 3) == 0) {
+          uint8_t* sbk = scl + ((w >> 2) & 1) * 2048;
+          __builtin_amdgcn_global_load_lds(psw + w, sbk, 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(psa + w, sbk + 1024, 16, 0, 0);
+        }
+      } else {
+        __builtin_amdgcn_global_load_lds(psw + w, scl + sl * 512, 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(psa + w, scl + sl * 512 + 256, 4, 0, 0);
+      }
     }
   };
 
@@ -346,7 +369,8 @@ __device__ __forceinline__ void skinny_ring(const Args& a, const Group& gr, int 
   for (int mp = 0; mp < MP; ++mp)
 #pragma unroll
     for (int np = 0; np < NP; ++np) acc[mp][np] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const uint8_t* base) {
+  auto compute = [&](int sl, int w) {
+    const uint8_t* base = ring + sl * R::WIN;
     const int ablk = NT + min(n16 >> 3, MT - 1);   // 8-row class: rows 8..15 repeat rows 0..7
     const int bblk = n16 >> 3;
     if constexpr (!FP8) {
@@ -363,22 +387,36 @@ __device__ __forceinline__ void skinny_ring(const Args& a, const Group& gr, int 
           for (int np = 0; np < NP; ++np) F::mma(acc[mp][np], fa[mp], fb[np]);
       }
     } else {
-      const float* sb = reinterpret_cast<const float*>(base + (NT + MT) * 1024);
       i32x4 fa0[MP], fa1[MP], fb0[NP], fb1[NP];
       float sw[NP];
       f32x4 sa[MP];
+      // C rows 4 * grp + i of M pair mp (the 8-row class repeats its 8 rows); column n16 of N pair np
+      auto srow = [&](int mp, int i) -> int { return MT > 1 ? 16 * mp + 4 * grp + i : (4 * grp + i) & 7; };
+      if (blk4) {   // [row][4 windows] floats: weight scales, then activation scales
+        const float* sbk = reinterpret_cast<const float*>(scl + ((w >> 2) & 1) * 2048);
+        const int wi = w & 3;
+#pragma unroll
+        for (int mp = 0; mp < MP; ++mp)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sa[mp][i] = sbk[256 + srow(mp, i) * 4 + wi];
+#pragma unroll
+        for (int np = 0; np < NP; ++np) sw[np] = sbk[(16 * np + n16) * 4 + wi];
+      } else {
+        const float* sb = reinterpret_cast<const float*>(scl + sl * 512);
+#pragma unroll
+        for (int mp = 0; mp < MP; ++mp) sa[mp] = *reinterpret_cast<const f32x4*>(sb + 64 + srow(mp, 0));
+#pragma unroll
+        for (int np = 0; np < NP; ++np) sw[np] = sb[16 * np + n16];
+      }
 #pragma unroll
       for (int mp = 0; mp < MP; ++mp) {
         fa0[mp] = frag(base, ablk + 2 * mp, grp);
         fa1[mp] = frag(base, ablk + 2 * mp, grp + 4);
-        // C rows 4 * grp + i of the pair; the 8-row class repeats its 8 rows
-        sa[mp] = *reinterpret_cast<const f32x4*>(sb + 64 + (MT > 1 ? 16 * mp + 4 * grp : 4 * (grp & 1)));
       }
 #pragma unroll
       for (int np = 0; np < NP; ++np) {
         fb0[np] = frag(base, bblk + 2 * np, grp);
         fb1[np] = frag(base, bblk + 2 * np, grp + 4);
-        sw[np] = sb[16 * np + n16];
       }
 #pragma unroll
       for (int mp = 0; mp < MP; ++mp)
@@ -393,26 +431,23 @@ __device__ __forceinline__ void skinny_ring(const Args& a, const Group& gr, int 
 
 #pragma unroll
   for (int d = 0; d < D; ++d)
-    if (d < nwin) issue(ring + d * R::WIN, d);
+    if (d < nwin) issue(d, d);
+  static_assert(D <= 4, "vmcnt counts of up to 3 later windows");
   int w = 0, slot = 0;
-  // steady state: windows w .. w + D - 1 in flight; consume w, refill its slot with w + D
-  for (; w + D < nwin; ++w) {
-    wait_vmcnt<(D - 1) * R::NL>();
-    uint8_t* base = ring + slot * R::WIN;
-    compute(base);
-    wait_lgkm0();   // the slot's reads are done before its refill can land
-    issue(base, w + D);
-    slot = slot + 1 == D ? 0 : slot + 1;
-  }
-  // drain: the last (at most D) windows are in flight, nothing more to issue
+  // windows w + 1 .. w + D - 1 (those issued) stay in flight while w is consumed
   for (; w < nwin; ++w) {
-    const int later = nwin - 1 - w;   // windows issued after w
-    static_assert(D <= 4, "drain waits cover at most 3 later windows");
-    if (later >= 3) wait_vmcnt<3 * R::NL>();
-    else if (later == 2) wait_vmcnt<2 * R::NL>();
-    else if (later == 1) wait_vmcnt<R::NL>();
-    else wait_vmcnt<0>();
-    compute(ring + slot * R::WIN);
+    int later = 0;
+#pragma unroll
+    for (int d = 1; d < D; ++d)
+      if (w + d < nwin) later += loads_of(w + d);
+    if (FP8) wait_vmcnt_dyn(later);
+    else if (w + D - 1 < nwin) wait_vmcnt<(D - 1) * R::NB>();
+    else wait_vmcnt_dyn(later);
+    compute(slot, w);
+    if (w + D < nwin) {
+      wait_lgkm0();   // the slot's reads are done before its refill can land
+      issue(slot, w + D);
+    }
     slot = slot + 1 == D ? 0 : slot + 1;
   }
 
@@ -458,7 +493,7 @@ __device__ __forceinline__ void skinny_tile(const Args& a, const Group& gr, int 
 // per wave) takes 108..150 KB per workgroup: one workgroup per CU, one wave
 // per SIMD.
 constexpr int kRingDepth = 3;   // K windows in flight per wave
-constexpr size_t sk_ring_bytes(int wave_win) { return (size_t)4 * kRingDepth * wave_win; }   // 4 waves
+constexpr size_t sk_ring_bytes(int wave_bytes) { return (size_t)4 * wave_bytes; }   // 4 waves
 
 // One launch for the three row classes.  Workgroups reach the 8 XCDs
 // round-robin (blockIdx % 8).  Each class takes a contiguous band of
@@ -491,7 +526,7 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(Args a) {
   int g;
   const Group gr = group_of_entry(a, a.plan[kPlanHead + cls * 2 * a.G + gi], &g);
   extern __shared__ __attribute__((aligned(16))) uint8_t sk_ring[];
-  uint8_t* ring = sk_ring + wave * kRingDepth * RingCfg<DT, 4, NT>::WIN;
+  uint8_t* ring = sk_ring + wave * RingCfg<DT, 4, NT, kRingDepth>::WAVE_BYTES;
   if (cls == 2) skinny_ring<DT, MODE, 4, NT, kRingDepth>(a, gr, g, it, lane, ring);
   else if (cls == 1) skinny_ring<DT, MODE, 2, NT, kRingDepth>(a, gr, g, it, lane, ring);
   else skinny_ring<DT, MODE, 1, NT, kRingDepth>(a, gr, g, it, lane, ring);
@@ -512,7 +547,7 @@ __global__ __launch_bounds__(64 * kShKS) void ffn_shared_skinny_kernel(Args a) {
 
 template <int DT, int MODE>
 hipError_t launch_sk(unsigned grid, const Args& a, hipStream_t st) {
-  constexpr size_t lds = sk_ring_bytes(RingCfg<DT, 4, kSkNT>::WIN);
+  constexpr size_t lds = sk_ring_bytes(RingCfg<DT, 4, kSkNT, kRingDepth>::WAVE_BYTES);
   static_assert(lds <= 160 * 1024, "LDS budget");
   static bool attr_set = false;   // raise the dynamic-LDS limit once per process
   if (!attr_set) {
