@@ -46,7 +46,10 @@ template <int DT, int TM> struct TileCfg {
   static constexpr int NSC = 512;                             // fp8 scale slots per stage: 8 waves x 64
   static constexpr int STAGE = (TM + kTN) * SL;               // tile bytes per stage (A then B)
   static constexpr int PER_SLICE = LPA + LPB + (DT == MOE_FP8_E4M3 ? 1 : 0);   // loads per thread per slice
-  static constexpr size_t LDS_BYTES = (size_t)NST * STAGE + (DT == MOE_FP8_E4M3 ? (size_t)NST * NSC * 4 : 0);
+  // fp8 scale area: per-slice scales [NST][NSC] floats, or, when the slice
+  // count is a multiple of 4, two blocks of [NSC][4 slices] floats
+  static constexpr size_t SCB = (size_t)2 * NSC * 16;
+  static constexpr size_t LDS_BYTES = (size_t)NST * STAGE + (DT == MOE_FP8_E4M3 ? SCB : 0);
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   __device__ static __forceinline__ int off(int r, int c) { return r * SL + ((c ^ (r & 7)) << 4); }
 };
@@ -59,8 +62,12 @@ template <int DT, int TM> struct TileCfg {
 // the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
-// Issue the direct global -> LDS loads of slice kt into stage st.
-template <int DT, int TM>
+// Issue the direct global -> LDS loads of slice kt into stage st.  fp8
+// scales (slot 64 * wave + lane): with BLK, a 16-byte load every 4th slice
+// fetches 4 slices' scales of the slot's row into block (kt / 4) % 2, so
+// each scale row's cache line is touched once per 4 slices (a slice's 512
+// scales lie in 512 different rows); else 4 bytes per slice into stage st.
+template <int DT, int TM, bool BLK>
 __device__ __forceinline__ void tile_issue(uint8_t* smem, const uint8_t* const* ga, const uint8_t* const* gb,
                                            const float* gs, int kt, int st, int wave) {
   using C = TileCfg<DT, TM>;
@@ -72,12 +79,20 @@ __device__ __forceinline__ void tile_issue(uint8_t* smem, const uint8_t* const* 
 #pragma unroll
   for (int i = 0; i < C::LPB; ++i) __builtin_amdgcn_global_load_lds(gb[i] + off, lb + i * 1024, 16, 0, 0);
   if constexpr (DT == MOE_FP8_E4M3) {
-    float* ls = reinterpret_cast<float*>(smem + C::NST * C::STAGE) + st * C::NSC + wave * 64;
-    __builtin_amdgcn_global_load_lds(gs + kt, ls, 4, 0, 0);
+    uint8_t* sc = smem + C::NST * C::STAGE;
+    if constexpr (BLK) {
+      if ((kt & 3) == 0) {
+        const float* src = gs + kt;
+        uint8_t* dst = sc + (((kt >> 2) & 1) * C::NSC + wave * 64) * 16;
+        __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+      }
+    } else {
+      __builtin_amdgcn_global_load_lds(gs + kt, sc + (st * C::NSC + wave * 64) * 4, 4, 0, 0);
+    }
   }
 }
 
-template <int DT, int MODE, bool SHARED, int TM>
+template <int DT, int MODE, bool SHARED, int TM, bool BLK>
 __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
   using F = Frag<DT>;
   using C = TileCfg<DT, TM>;
@@ -171,7 +186,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
 
 #pragma unroll
   for (int p = 0; p < NST - 1; ++p)
-    if (p < nkt) tile_issue<DT, TM>(smem, ga, gb, gs, p, p, wave);
+    if (p < nkt) tile_issue<DT, TM, BLK>(smem, ga, gb, gs, p, p, wave);
   bool full_tile = false;
   if constexpr (!FP8) full_tile = mval == 4;
   if (full_tile) {
@@ -194,7 +209,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
         i32x4 fa[SL / 64][4], fb[SL / 64][NTW];
 #pragma unroll
         for (int fs = 0; fs < SL / 64; ++fs) {
-          if (fs == 1) tile_issue<DT, TM>(smem, ga, gb, gs, min(kt + 1, nkt - 1), (kt + 1) & 1, wave);
+          if (fs == 1) tile_issue<DT, TM, false>(smem, ga, gb, gs, min(kt + 1, nkt - 1), (kt + 1) & 1, wave);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             fa[fs][i] = *reinterpret_cast<const i32x4*>(&la[C::off(wm * 64 + i * 16 + row, fs * 4 + grp)]);
@@ -230,10 +245,14 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
     for (int kt = 0; kt < nkt; ++kt) {
       const int st = kt % NST;
       // wait until this thread's loads of slice kt have landed; later slices may stay in flight
-      if (NST > 2 && kt + 1 < nkt) wait_vmcnt<C::PER_SLICE>();
-      else wait_vmcnt<0>();
+      if (NST > 2 && kt + 1 < nkt) {
+        if (FP8 && BLK) wait_vmcnt_dyn(C::LPA + C::LPB + (((kt + 1) & 3) == 0 ? 1 : 0));
+        else wait_vmcnt<C::PER_SLICE>();
+      } else {
+        wait_vmcnt<0>();
+      }
       barrier_no_fence();                          // everyone's slice kt is in LDS; stage (kt-1) % NST is free
-      if (kt + NST - 1 < nkt) tile_issue<DT, TM>(smem, ga, gb, gs, kt + NST - 1, (kt + NST - 1) % NST, wave);
+      if (kt + NST - 1 < nkt) tile_issue<DT, TM, BLK>(smem, ga, gb, gs, kt + NST - 1, (kt + NST - 1) % NST, wave);
       const uint8_t* la = smem + st * C::STAGE;
       const uint8_t* lb = la + TM * SL;
       if constexpr (!FP8) {
@@ -255,8 +274,10 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
           }
         }
       } else {
-        const float* sa_l = lds_s + st * C::NSC;
-        const float* sb_l = sa_l + TM;
+        // scales of slot s (A row s, then B row s - TM) for slice kt
+        constexpr int SS = BLK ? 4 : 1;   // floats between consecutive slots
+        const float* sp = BLK ? lds_s + (size_t)((kt >> 2) & 1) * C::NSC * 4 + (kt & 3) : lds_s + st * C::NSC;
+        auto scale = [&](int slot) -> float { return sp[slot * SS]; };
         // groups of 4 column tiles keep the B fragments within the register budget
 #pragma unroll
         for (int jh = 0; jh < NTW / 4; ++jh) {
@@ -267,7 +288,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
             const int n = wn * WN + (4 * jh + jj) * 16 + row;
             fb0[jj] = *reinterpret_cast<const i32x4*>(&lb[C::off(n, grp)]);
             fb1[jj] = *reinterpret_cast<const i32x4*>(&lb[C::off(n, 4 + grp)]);
-            sb[jj] = sb_l[n];
+            sb[jj] = scale(TM + n);
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -277,7 +298,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
               const i32x4 fa1 = *reinterpret_cast<const i32x4*>(&la[C::off(r, 4 + grp)]);
               float sa[4];
 #pragma unroll
-              for (int q = 0; q < 4; ++q) sa[q] = sa_l[wm * 64 + i * 16 + 4 * grp + q];
+              for (int q = 0; q < 4; ++q) sa[q] = scale(wm * 64 + i * 16 + 4 * grp + q);
 #pragma unroll
               for (int jj = 0; jj < 4; ++jj) {
                 const f32x4 p = F::mma128(fa0, fa1, fb0[jj], fb1[jj]);
@@ -322,17 +343,17 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
   }
 }
 
-template <int DT, int MODE, bool SHARED, int TM>
+template <int DT, int MODE, bool SHARED, int TM, bool BLK>
 hipError_t launch_fat(const char* name, unsigned grid, int ntn, const Args& a, hipStream_t st) {
   using C = TileCfg<DT, TM>;
   static bool attr_set = false;   // raise the dynamic-LDS limit once per process
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_fat_kernel<DT, MODE, SHARED, TM>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_fat_kernel<DT, MODE, SHARED, TM, BLK>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  MOE_LAUNCH(name, (ffn_fat_kernel<DT, MODE, SHARED, TM>), dim3(grid), dim3(512), C::LDS_BYTES, st, a, ntn);
+  MOE_LAUNCH(name, (ffn_fat_kernel<DT, MODE, SHARED, TM, BLK>), dim3(grid), dim3(512), C::LDS_BYTES, st, a, ntn);
   return hipGetLastError();
 }
 
@@ -347,7 +368,11 @@ hipError_t launch_tiled(int mode, bool shared, int tm, unsigned grid, int ntn, c
       {{"ffn_gemm1_tiled", "ffn_gemm1_tiled128"}, {"ffn_gemm1_shared_tiled", "ffn_gemm1_shared_tiled128"}},
       {{"ffn_gemm2_tiled", "ffn_gemm2_tiled128"}, {"ffn_gemm2_shared_tiled", "ffn_gemm2_shared_tiled128"}}};
   const char* name = kName[mode - 1][shared ? 1 : 0][tm == 128 ? 1 : 0];
-#define MOE_TL(M, S, TMV) launch_fat<DT, M, S, TMV>(name, grid, ntn, a, st)
+  // fp8 scale blocks of 4 slices need the slice count K / 128 to be a multiple of 4
+  const bool blk = DT == MOE_FP8_E4M3 && (((mode == 1 ? a.H : a.I) / 128) & 3) == 0;
+#define MOE_TL(M, S, TMV)                                                                      \
+  (DT == MOE_FP8_E4M3 && blk ? launch_fat<DT, M, S, TMV, DT == MOE_FP8_E4M3>(name, grid, ntn, a, st) \
+                             : launch_fat<DT, M, S, TMV, false>(name, grid, ntn, a, st))
   if (tm == 256) {
     if (mode == 1) return shared ? MOE_TL(1, true, 256) : MOE_TL(1, false, 256);
     return shared ? MOE_TL(2, true, 256) : MOE_TL(2, false, 256);

@@ -70,6 +70,9 @@ SMALL = {
                                                            E=4, k=2, I=2048, I_shared=2048),
     "fp8_full_and_rest": get_config("decode16_fp8").with_(name="fp8_full_and_rest", T=700, H=512, E=4, k=2,
                                                          I=2048, I_shared=2048),
+    # K / 128 not a multiple of 4 in either GEMM (5 and 9 scale blocks): scales fetched one slice at a time
+    "fp8_k_not_4x": get_config("clustered2048_fp8").with_(name="fp8_k_not_4x", routing="random", T=300, H=640,
+                                                         E=4, k=2, I=1152, I_shared=1152),
 }
 
 
