@@ -88,16 +88,20 @@ def _small_inputs(cfg):
 
 # ------------------------------------------------------------------ quantiser
 
+@pytest.mark.parametrize("block", [64, 128, 192, 256])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_quantize_fp8_bit_exact(dtype):
+def test_quantize_fp8_bit_exact(dtype, block):
+    # 37 rows of 1536: a ragged last workgroup for every block width (the
+    # 64/128/256 kernel puts block / 8 lanes on a block, 192 one wave)
     g = torch.Generator().manual_seed(5)
-    a = torch.randn(37, 1024, generator=g) * torch.logspace(-6, 3, 1024)[None, :]
-    a[3, 256:384] = 0.0
-    a[4, :128] = 1e-30
+    a = torch.randn(37, 1536, generator=g) * torch.logspace(-6, 3, 1536)[None, :]
+    a[3, :768] = 0.0           # all-zero blocks: scale 1
+    a[4, :256] = 1e-30         # blocks of subnormal ratios
+    a[5, 7] = 448.0 * 3        # saturating neighbourhood of the block maximum
     a = a.to(dtype)
-    codes, scales = moe.moe_quantize_fp8(a.to(DEV), 128)
+    codes, scales = moe.moe_quantize_fp8(a.to(DEV), block)
     torch.cuda.synchronize()
-    oc, os_, _ = oracle.quantize_rows_fp8(oracle.to_f64(a), 128)
+    oc, os_, _ = oracle.quantize_rows_fp8(oracle.to_f64(a), block)
     np.testing.assert_array_equal(to_np(codes), oc)
     np.testing.assert_array_equal(to_np(scales).astype(np.float64), os_)
 
