@@ -31,7 +31,8 @@ KERNEL_SOURCES = {
     "ffn_gemm1_shared_skinny": "ffn_skinny.hip", "ffn_gemm2_shared_skinny": "ffn_skinny.hip",
     **{f"ffn_gemm{g}_{s}tiled{t}": "ffn_tiled.hip" for g in (1, 2) for s in ("", "shared_") for t in ("", "128")},
     "ffn_plan": "ffn.hip",
-    "route_gate_fused": "route.hip", "route_gate_split": "route.hip", "route_reduce_select": "route.hip",
+    "route_gate_fused": "route.hip", "route_gate_split": "route.hip", "route_gate_tiled": "route.hip",
+    "route_reduce_select": "route.hip",
     "dispatch_count": "dispatch.hip", "dispatch_scan": "dispatch.hip", "dispatch_scatter": "dispatch.hip",
     "quant_fp8": "quant.hip", "combine": "combine.hip",
 }
@@ -69,6 +70,7 @@ def rocprof_name(kernel: str, w_dtype: str) -> str:
              "dispatch_scatter": "(anonymous namespace)::dispatch_scatter_kernel",
              "route_gate_fused": "void (anonymous namespace)::gate_kernel<",
              "route_gate_split": "void (anonymous namespace)::gate_kernel<",
+             "route_gate_tiled": "void (anonymous namespace)::gate_tile_kernel<",
              "combine": "void (anonymous namespace)::combine_kernel<",
              "quant_fp8": "void (anonymous namespace)::quant_fp8_kernel<"}
     return fixed[kernel]

@@ -133,9 +133,35 @@ def test_route_full_size(name):
     _route_check(cfg, x.cpu(), wg.cpu(), bias.cpu())
 
 
+# 512 tokens and more (bf16): the LDS-staged router, one case per expert-count
+# class (32, 64, 128, 256 LDS expert rows), with K split over workgroups
+# (partial logits + reduce) or in one range (selection in the workgroup),
+# ragged token tiles and expert counts below the class size.
+_D16, _PF = get_config("decode16"), get_config("prefill8192_ep8")
+MANY = {
+    "many_e256_split": _D16.with_(name="many_e256_split", T=600, H=2048),
+    "many_e256_one_range": _D16.with_(name="many_e256_one_range", T=16400, H=256),
+    "many_e200_k6_split": _D16.with_(name="many_e200_k6_split", T=530, H=1024, E=200, k=6),
+    "many_e128_split": _D16.with_(name="many_e128_split", T=520, H=2048, E=128),
+    "many_e64_split": _D16.with_(name="many_e64_split", T=777, H=4096, E=64),
+    "many_e48_softmax_one_range": _D16.with_(name="many_e48_softmax_one_range", T=2100, H=512, E=48, k=4,
+                                             score="softmax"),
+    "many_e32_split": _PF.with_(name="many_e32_split", T=1000, H=2048),
+    "many_e32_one_range": _PF.with_(name="many_e32_one_range", T=700, H=512),
+    "many_e256_groups_split": _D16.with_(name="many_e256_groups_split", T=1030, H=1024, n_group=8, topk_group=4),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MANY))
+def test_route_many_tokens(name):
+    cfg = MANY[name]
+    x, wg, bias = make_router_inputs(cfg, "cpu")
+    _route_check(cfg, x, wg, bias)
+
+
 # Group-limited routing: DeepSeek-V3-like groups (256 experts in 8 groups,
-# 4 kept) on the split-K router, a prefill-sized call on the fused router,
-# softmax scoring in fp32, and the all-groups case.
+# 4 kept) on the split-K router, a prefill-sized call on the LDS-staged
+# router, softmax scoring in fp32, and the all-groups case.
 GROUPED = {
     "groups_e256_g8_t4": get_config("decode16").with_(name="groups_e256_g8_t4", T=64, H=1024, n_group=8,
                                                      topk_group=4),
