@@ -70,6 +70,9 @@ SMALL = {
                                                            E=4, k=2, I=2048, I_shared=2048),
     "fp8_full_and_rest": get_config("decode16_fp8").with_(name="fp8_full_and_rest", T=700, H=512, E=4, k=2,
                                                          I=2048, I_shared=2048),
+    # 512+ bf16 tokens: the LDS-staged router with K split in two, tiled and streaming groups
+    "t600_e32_bf16": get_config("decode16").with_(name="t600_e32_bf16", routing="zipf", T=600, H=2048, E=32, k=4,
+                                                  I=256, I_shared=256),
     # K / 128 not a multiple of 4 in either GEMM (5 and 9 scale blocks): scales fetched one slice at a time
     "fp8_k_not_4x": get_config("clustered2048_fp8").with_(name="fp8_k_not_4x", routing="random", T=300, H=640,
                                                          E=4, k=2, I=1152, I_shared=1152),
@@ -367,7 +370,7 @@ def test_forward_on_user_stream_is_ordered():
         assert_outputs_close(to_np(y)[keep], ref["y"][keep], tol_key(cfg), "y")
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "small_bf16", "t24_bf16", "small_fp8"])
+@pytest.mark.parametrize("name", ["tiny_f32", "small_bf16", "t24_bf16", "small_fp8", "t600_e32_bf16", "fp8_k_not_4x"])
 def test_graph_replays_match_eager(name):
     """A captured whole-layer graph, replayed several times with eager work
     and synchronisations in between, gives the eager result bit for bit
