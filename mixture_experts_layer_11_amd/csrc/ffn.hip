@@ -134,8 +134,15 @@ hipError_t run_shared(const moe_cfg& c, const Args& a, hipStream_t st) {
 // The routed experts, on the stream it is given: plan, then per projection
 // the three skinny classes and the tiled groups.  Grids are sized on the
 // host from upper bounds; workgroups beyond the device-side lists exit.
-template <int DT>
-hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st) {
+// run_routed calls hook(2 * mode - 2) before and hook(2 * mode - 1) after
+// the streaming launch of each GEMM (mode 1, 2); run_ffn forks the shared
+// expert there.
+struct NoHook {
+  hipError_t operator()(int) const { return hipSuccess; }
+};
+
+template <int DT, typename Hook = NoHook>
+hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st, const Hook& hook = Hook()) {
   MOE_LAUNCH("ffn_plan", ffn_plan_kernel, dim3(1), dim3(512), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -171,7 +178,9 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st) {
       if (groups == 0 || min_rows > c.T) continue;
       bands += moe::ceil_div(moe::ceil_div(groups * items, 4LL), 8LL);   // 4 items per workgroup
     }
+    if ((e = hook(2 * mode - 2)) != hipSuccess) return e;
     if (bands > 0 && (e = launch_skinny<DT>(mode, (unsigned)(8 * bands), a, st)) != hipSuccess) return e;
+    if ((e = hook(2 * mode - 1)) != hipSuccess) return e;
     const int ntn = mode == 1 ? moe::ceil_div(c.I, kTN / 2) : moe::ceil_div(c.H, kTN);
     if (max_fat > 0 && (e = launch_tiled<DT>(mode, false, kTileRows, (unsigned)(max_fat * ntn), ntn, a, st)) != hipSuccess)
       return e;
@@ -186,12 +195,15 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st) {
 // st (an event records st's position, the side stream waits on it) and
 // joined back at the end (st waits on an event recorded after the shared
 // launches), so it overlaps the routed experts instead of running alone on
-// part of the device.  It is enqueued first so that its large workgroups
-// find free CUs before the routed kernels fill the device.  Both halves
-// write disjoint rows of h and separate outputs.  A skinny shared expert
-// (T <= kSkinnyRows) streams weights like the routed skinny kernels and one
-// that fills the device is compute-bound like the routed tiles: both stay on
-// st, where running beside the routed kernels would only add contention.
+// part of the device.  The fork comes right before the routed GEMM2 stage:
+// the routed GEMM1, the longer of the two, keeps the whole device, and the
+// shared expert runs beside the routed GEMM2 (measured against forking at
+// the start: decode256 2.825 -> 2.766 ms, decode256_fp8 1.537 -> 1.522 ms,
+// clustered2048_fp8 2.715 -> 2.675 ms).  Both write disjoint rows of h and
+// separate outputs.  A skinny shared expert (T <= kSkinnyRows) streams
+// weights like the routed skinny kernels and one that fills the device is
+// compute-bound like the routed tiles: both stay on st, where running beside
+// the routed kernels would only add contention.
 template <int DT>
 hipError_t run_ffn(const moe_cfg& c, const Args& a, hipStream_t st) {
   if (!a.has_shared || a.halves) return run_routed<DT>(c, a, st);
@@ -205,10 +217,16 @@ hipError_t run_ffn(const moe_cfg& c, const Args& a, hipStream_t st) {
     e = run_shared<DT>(c, a, st);
     return e != hipSuccess ? e : run_routed<DT>(c, a, st);
   }
-  if ((e = hipEventRecord(side.fork, st)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(side.stream, side.fork, 0)) != hipSuccess) return e;
-  hipError_t es = run_shared<DT>(c, a, side.stream);
-  hipError_t er = es == hipSuccess ? run_routed<DT>(c, a, st) : hipSuccess;
+  hipError_t es = hipSuccess;
+  auto fork = [&](int at) -> hipError_t {   // at 2: the routed GEMM2 stage is next
+    if (at != 2) return hipSuccess;
+    hipError_t ef = hipEventRecord(side.fork, st);
+    if (ef == hipSuccess) ef = hipStreamWaitEvent(side.stream, side.fork, 0);
+    if (ef != hipSuccess) return ef;
+    es = run_shared<DT>(c, a, side.stream);
+    return es;
+  };
+  hipError_t er = run_routed<DT>(c, a, st, fork);
   // join even after a failed launch, so that work queued later on st never
   // runs ahead of work already queued on the side stream
   if ((e = hipEventRecord(side.join, side.stream)) == hipSuccess) e = hipStreamWaitEvent(st, side.join, 0);
