@@ -336,9 +336,20 @@ __device__ __forceinline__ void skinny_ring(const Args& a, const Group& gr, int 
   auto loads_of = [&](int w) -> int {   // direct loads of window w
     return R::NB + (FP8 ? (blk4 ? ((w & 3) == 0 ? 2 : 0) : 2) : 0);
   };
+  // The item's K windows are taken in the rotated order w0, w0 + 1, ..,
+  // nwin - 1, 0, .., w0 - 1 (w below counts steps; window (w + w0) % nwin is
+  // read).  With rows a power of two bytes long, every row's window w sits at
+  // the same address modulo the row length, and waves that all start at
+  // window 0 crowd the same HBM channels: a start that differs from item to
+  // item spreads them (4 KB rows: 6.0 -> 7.1 TB/s in a read-only probe of
+  // this access pattern; decode16's GEMM2 397 -> 375 us).  fp8 keeps the
+  // plain order: its 2 KB GEMM2 rows measured 1% slower rotated (by whole
+  // 4-window scale blocks, which the blocked scales need).
+  const int w0 = !FP8 && (krow & (krow - 1)) == 0 ? (g * 7 + it * 5) % nwin : 0;
   auto issue = [&](int sl, int w) {
     uint8_t* base = ring + sl * R::WIN;
-    const size_t off = (size_t)w * 128;
+    const int wa = w + w0 < nwin ? w + w0 : w + w0 - nwin;   // the window read at step w
+    const size_t off = (size_t)wa * 128;
 #pragma unroll
     for (int j = 0; j < NT; ++j) __builtin_amdgcn_global_load_lds(pb0 + (tile_off[j] + off), base + j * 1024, 16, 0, 2);   // nt
 #pragma unroll
@@ -347,12 +358,12 @@ __device__ __forceinline__ void skinny_ring(const Args& a, const Group& gr, int 
       if (blk4) {
         if ((w & 3) == 0) {
           uint8_t* sbk = scl + ((w >> 2) & 1) * 2048;
-          __builtin_amdgcn_global_load_lds(psw + w, sbk, 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(psa + w, sbk + 1024, 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(psw + wa, sbk, 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(psa + wa, sbk + 1024, 16, 0, 0);
         }
       } else {
-        __builtin_amdgcn_global_load_lds(psw + w, scl + sl * 512, 4, 0, 0);
-        __builtin_amdgcn_global_load_lds(psa + w, scl + sl * 512 + 256, 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(psw + wa, scl + sl * 512, 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(psa + wa, scl + sl * 512 + 256, 4, 0, 0);
       }
     }
   };
