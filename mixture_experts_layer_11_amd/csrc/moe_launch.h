@@ -67,7 +67,8 @@ struct SideStream {
   hipEvent_t join;
   int cus;          // compute units of the device
 };
-hipError_t side_stream(SideStream* out);
+constexpr int kSideStreams = 2;                   // per host thread and device
+hipError_t side_stream(SideStream* out, int which = 0);
 hipError_t capture_stream(hipStream_t* out);   // private stream for graph capture
 
 // ---- routing statistics

@@ -14,13 +14,14 @@
 
 namespace moe {
 
-hipError_t side_stream(SideStream* out) {
+hipError_t side_stream(SideStream* out, int which) {
   thread_local std::vector<SideStream> per_device;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if ((int)per_device.size() <= dev) per_device.resize(dev + 1);
-  SideStream& s = per_device[dev];
+  if (which < 0 || which >= kSideStreams) return hipErrorInvalidValue;
+  if ((int)per_device.size() <= dev * kSideStreams + which) per_device.resize((dev + 1) * kSideStreams);
+  SideStream& s = per_device[dev * kSideStreams + which];
   if (!s.stream) {
     SideStream n{};
     if ((e = hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking)) != hipSuccess) return e;
