@@ -13,25 +13,26 @@
 //                 routed experts plus the shared expert as group E) into two
 //                 regimes: "skinny" groups with 1..kSkinnyRows rows (in three
 //                 classes by row count) and "fat" groups, cut into
-//                 kTileRows-row tiles.
-//   skinny GEMM   (ffn_skinny.hip) one wave streams 8 weight rows x 128-byte
-//                 windows of an expert's weight matrix straight from HBM into
-//                 MFMA B registers (each weight byte is read once) against
+//                 kTileRows-row tiles (fp8: the last 1..128 rows of a group
+//                 into one kMidRows-row tile).
+//   skinny GEMM   (ffn_skinny.hip) one wave takes an item of 64 weight rows
+//                 and streams its 128-byte K windows global -> LDS through a
+//                 ring of its own (each weight byte is read once) against
 //                 the group's <= 32 rows.  Bandwidth-bound decode regime.
-//   tiled GEMM    (ffn_tiled.hip) 256 x 256 output tiles per workgroup, K
-//                 staged through LDS in double-buffered 128-byte slices
-//                 loaded global -> LDS directly, 8 waves of 64 x 128 with
-//                 16x16 MFMAs.  Compute-bound prefill regime.
+//   tiled GEMM    (ffn_tiled.hip) 256 x 256 (or 128 x 256) output tiles per
+//                 workgroup, K staged through LDS in 128-byte slices loaded
+//                 global -> LDS directly, 8 waves with 16x16 MFMAs.
+//                 Compute-bound prefill regime.
 //
 // GEMM1 (mode 1) produces h = SiLU(A W1^T) * (A W3^T): every output tile holds
 // matching gate and up columns (16-column blocks interleaved gate, up, gate,
 // up), so SwiGLU is applied in registers.  GEMM2 (mode 2) is the down
 // projection into y_sorted (routed) or y_shared.
 //
-// FP8 E4M3 weights carry one fp32 scale per row per 128 K-values and the
-// activations one scale per row per 128: each 128-wide K block is one
-// 16x16x128 MFMA with unit block exponents, promoted to fp32 with
-// scale_a[row] * scale_w[col] and accumulated on the vector ALU.
+// FP8 E4M3 weights carry one fp32 scale per row (or per 128 rows) per 128
+// K-values and the activations one scale per row per 128: each 128-wide K
+// block is one 16x16x128 MFMA with unit block exponents, promoted to fp32
+// with scale_a[row] * scale_w[col] and accumulated on the vector ALU.
 
 #include "ffn.h"
 

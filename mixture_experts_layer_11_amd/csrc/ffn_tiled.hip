@@ -27,10 +27,10 @@ using namespace moe::ffn;
 // chunk c ^ (r & 7), which keeps the fragment reads of 16 consecutive rows
 // free of bank conflicts; the direct loads write chunks in lane order, so
 // each lane fetches the global chunk that belongs at its position.  fp8
-// scales of the slice (one per A row and per B row) go global -> LDS the same
-// way, 4 bytes per lane, so every thread issues the same number of loads per
-// slice and the wait counts are uniform.  Waves whose 64 rows lie beyond the
-// tile's valid rows skip their MFMAs.
+// scales (one per A row and per B row per slice) go global -> LDS the same
+// way: 16 bytes per lane every 4th slice into one of two 4-slice blocks when
+// the slice count is a multiple of 4, else 4 bytes per lane per slice.
+// Waves whose 64 rows lie beyond the tile's valid rows skip their MFMAs.
 
 template <int DT, int TM> struct TileCfg {
   static constexpr int SL = 128;                              // bytes of K per slice and row
