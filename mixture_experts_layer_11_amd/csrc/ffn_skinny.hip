@@ -560,13 +560,8 @@ template <int DT, int MODE>
 hipError_t launch_sk(unsigned grid, const Args& a, hipStream_t st) {
   constexpr size_t lds = sk_ring_bytes(RingCfg<DT, 4, kSkNT, kRingDepth>::WAVE_BYTES);
   static_assert(lds <= 160 * 1024, "LDS budget");
-  static bool attr_set = false;   // raise the dynamic-LDS limit once per process
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_skinny_kernel<DT, MODE>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = moe::ensure_dynamic_lds(reinterpret_cast<const void*>(&ffn_skinny_kernel<DT, MODE>), (int)lds);
+  if (e != hipSuccess) return e;
   MOE_LAUNCH(MODE == 1 ? "ffn_gemm1_skinny" : "ffn_gemm2_skinny", (ffn_skinny_kernel<DT, MODE>), dim3(grid), dim3(256),
              lds, st, a);
   return hipGetLastError();

@@ -346,13 +346,9 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
 template <int DT, int MODE, bool SHARED, int TM, bool BLK>
 hipError_t launch_fat(const char* name, unsigned grid, int ntn, const Args& a, hipStream_t st) {
   using C = TileCfg<DT, TM>;
-  static bool attr_set = false;   // raise the dynamic-LDS limit once per process
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_fat_kernel<DT, MODE, SHARED, TM, BLK>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = moe::ensure_dynamic_lds(reinterpret_cast<const void*>(&ffn_fat_kernel<DT, MODE, SHARED, TM, BLK>),
+                                          (int)C::LDS_BYTES);
+  if (e != hipSuccess) return e;
   MOE_LAUNCH(name, (ffn_fat_kernel<DT, MODE, SHARED, TM, BLK>), dim3(grid), dim3(512), C::LDS_BYTES, st, a, ntn);
   return hipGetLastError();
 }

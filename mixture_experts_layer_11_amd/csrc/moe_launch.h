@@ -68,6 +68,9 @@ struct SideStream {
   int cus;          // compute units of the device
 };
 constexpr int kSideStreams = 2;                   // per host thread and device
+// Raises a kernel's dynamic-LDS limit to `bytes` on the current device, once
+// per (kernel, device); safe to call from several host threads.
+hipError_t ensure_dynamic_lds(const void* kernel, int bytes);
 hipError_t side_stream(SideStream* out, int which = 0);
 hipError_t capture_stream(hipStream_t* out);   // private stream for graph capture
 

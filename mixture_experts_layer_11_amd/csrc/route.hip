@@ -523,13 +523,9 @@ template <int EP, int TT, int WE, int NST, bool FUSED>
 static hipError_t launch_gate_tile(const moe_cfg& c, dim3 grid, const uint8_t* xb, const uint8_t* wb, int s,
                                    float* part, const RouteOut& o, hipStream_t st) {
   using C = GateCfg<EP, TT, WE, NST>;
-  static bool attr_set = false;   // raise the dynamic-LDS limit once per process
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gate_tile_kernel<EP, TT, WE, NST, FUSED>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = moe::ensure_dynamic_lds(reinterpret_cast<const void*>(&gate_tile_kernel<EP, TT, WE, NST, FUSED>),
+                                          (int)C::LDS_BYTES);
+  if (e != hipSuccess) return e;
   MOE_LAUNCH("route_gate_tiled", (gate_tile_kernel<EP, TT, WE, NST, FUSED>), grid, dim3(256), C::LDS_BYTES, st, xb,
              wb, c.T, c.H, s, part, o);
   return hipGetLastError();

@@ -1,4 +1,5 @@
-// Side stream for work that overlaps the caller's stream.
+// Side streams for work that overlaps the caller's stream, the graph-capture
+// stream, and the per-device dynamic-LDS limits of the library's kernels.
 //
 // One non-blocking stream (default priority) and two timing-free events per
 // host thread and device, created on first use and kept until the process
@@ -8,6 +9,9 @@
 // later work on it.  Per-thread resources keep calls from different host
 // threads from sharing the events.
 
+#include <mutex>
+#include <set>
+#include <utility>
 #include <vector>
 
 #include "moe_launch.h"
@@ -47,6 +51,19 @@ hipError_t capture_stream(hipStream_t* out) {
   if (!per_device[dev] && (e = hipStreamCreateWithFlags(&per_device[dev], hipStreamNonBlocking)) != hipSuccess)
     return e;
   *out = per_device[dev];
+  return hipSuccess;
+}
+
+hipError_t ensure_dynamic_lds(const void* kernel, int bytes) {
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;   // (kernel, device)
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({kernel, dev})) return hipSuccess;
+  if ((e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes)) != hipSuccess) return e;
+  done.insert({kernel, dev});
   return hipSuccess;
 }
 
