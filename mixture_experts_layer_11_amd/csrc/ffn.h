@@ -136,7 +136,12 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
 // s_waitcnt lgkmcnt(0) only: this wave's LDS reads have completed.
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4)); }
 
-constexpr int kSkNT = 8;   // 8-row weight tiles per routed skinny item (even: gate/up halves in GEMM1)
+// 8-row weight tiles per routed skinny item (GEMM1: gate/up halves, so a
+// multiple of 4).  bf16 GEMM1 takes half-width items: each workgroup's work
+// then lasts half as long, which halves the launch's draining tail, where
+// fewer and fewer CUs keep loads in flight (decode16 GEMM1 748 -> 730 us);
+// elsewhere the wider items measured faster.
+__host__ __device__ constexpr int sk_nt(int dt, int mode) { return dt == MOE_BF16 && mode == 1 ? 4 : 8; }
 constexpr int kShNT = 2;   // 8-row weight tiles per item of the skinny shared expert
 constexpr int kShKS = 4;   // waves splitting K in the skinny shared expert's workgroups
 constexpr int kTM = 256;   // tiled GEMM: tile rows (tokens)

@@ -165,7 +165,7 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st, const Hoo
       if (e != hipSuccess) return e;
     }
     const int N = mode == 1 ? c.I : c.H;
-    const long long items = N / ((mode == 1 ? 4 : 8) * kSkNT);   // skinny items per group
+    const long long items = N / ((mode == 1 ? 4 : 8) * sk_nt(DT, mode));   // skinny items per group
     long long bands = 0;   // workgroups per XCD over the three class bands (the kernel's order)
     for (int cls = 0; cls < 3; ++cls) {
       // a group of class cls has at least 1, 9 or 17 rows, and no group has

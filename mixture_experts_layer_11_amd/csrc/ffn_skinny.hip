@@ -270,7 +270,11 @@ template <int DT, int MT, int NT, int D> struct RingCfg {
   static constexpr bool FP8 = DT == MOE_FP8_E4M3;
   static constexpr int NB = NT + MT;                   // 1 KB blocks (direct loads) per window
   static constexpr int WIN = NB * 1024;                // LDS bytes per ring slot
-  static constexpr int SCL = FP8 ? 4096 : 0;           // fp8 scale area after the D slots
+  // fp8 4-window scale blocks: the windows in flight (D + 1) span at most
+  // (D + 3) / 4 + 1 blocks, each 2 KB (weight then activation scales); the
+  // per-window path takes 512 bytes per ring slot
+  static constexpr int SBUF = (D + 3) / 4 + 1;
+  static constexpr int SCL = FP8 ? (SBUF * 2048 > D * 512 ? SBUF * 2048 : D * 512) : 0;   // after the D slots
   static constexpr int WAVE_BYTES = D * WIN + SCL;     // one wave's LDS
   static constexpr int MP = MT > 1 ? MT / 2 : 1;       // 16-row M pairs
   static constexpr int NP = NT / 2;                    // 16-row N pairs
@@ -325,7 +329,7 @@ __device__ __forceinline__ void skinny_ring(const Args& a, const Group& gr, int 
   }
 
   // fp8 scales: when nwin % 4 == 0 (K a multiple of 512), one 16-byte load
-  // per lane fetches 4 windows' scales of its row, into one of two 2 KB
+  // per lane fetches 4 windows' scales of its row, into one of SBUF 2 KB
   // blocks (weight scales, then activation scales) of the scale area: each
   // scale row's cache line is touched once per 4 windows, not every window
   // (a window's 64 weight scales lie in 64 different rows and lines).  Else
@@ -357,7 +361,7 @@ __device__ __forceinline__ void skinny_ring(const Args& a, const Group& gr, int 
     if constexpr (FP8) {
       if (blk4) {
         if ((w & 3) == 0) {
-          uint8_t* sbk = scl + ((w >> 2) & 1) * 2048;
+          uint8_t* sbk = scl + ((w >> 2) % R::SBUF) * 2048;
           __builtin_amdgcn_global_load_lds(psw + wa, sbk, 16, 0, 0);
           __builtin_amdgcn_global_load_lds(psa + wa, sbk + 1024, 16, 0, 0);
         }
@@ -404,7 +408,7 @@ __device__ __forceinline__ void skinny_ring(const Args& a, const Group& gr, int 
       // C rows 4 * grp + i of M pair mp (the 8-row class repeats its 8 rows); column n16 of N pair np
       auto srow = [&](int mp, int i) -> int { return MT > 1 ? 16 * mp + 4 * grp + i : (4 * grp + i) & 7; };
       if (blk4) {   // [row][4 windows] floats: weight scales, then activation scales
-        const float* sbk = reinterpret_cast<const float*>(scl + ((w >> 2) & 1) * 2048);
+        const float* sbk = reinterpret_cast<const float*>(scl + ((w >> 2) % R::SBUF) * 2048);
         const int wi = w & 3;
 #pragma unroll
         for (int mp = 0; mp < MP; ++mp)
@@ -443,7 +447,7 @@ __device__ __forceinline__ void skinny_ring(const Args& a, const Group& gr, int 
 #pragma unroll
   for (int d = 0; d < D; ++d)
     if (d < nwin) issue(d, d);
-  static_assert(D <= 4, "vmcnt counts of up to 3 later windows");
+  static_assert((D - 1) * (R::NB + 2) < 64, "vmcnt counts of the later windows");
   int w = 0, slot = 0;
   // windows w + 1 .. w + D - 1 (those issued) stay in flight while w is consumed
   for (; w < nwin; ++w) {
@@ -496,30 +500,29 @@ __device__ __forceinline__ void skinny_tile(const Args& a, const Group& gr, int 
 }
 
 // Routed skinny groups of class CLS (MT = 1, 2, 4 M tiles of 8 tokens).
-// One wave = one work item (group, column block of kSkNT weight tiles) in a
+// One wave = one work item (group, column block of sk_nt weight tiles) in a
 // single pass over K through its LDS ring; waves past the class's list exit
-// at once.  Every class uses the same wide items: each activation block then
-// serves 8 weight tiles, which keeps the activation re-reads (one per item) a
-// small share of the loads even at 32 rows.  The ring (3 windows x 9..12.5 KB
-// per wave) takes 108..150 KB per workgroup: one workgroup per CU, one wave
-// per SIMD.
-constexpr int kRingDepth = 3;   // K windows in flight per wave
+// at once.  Every class uses the same items: an activation block then serves
+// 4 or 8 weight tiles, which keeps the activation re-reads (one per item) a
+// small share of the loads even at 32 rows.  The ring (3 windows x 9..12.5
+// KB per wave for 8-tile items, 4..6 windows x 5..8 KB for 4-tile ones)
+// takes 108..152 KB per workgroup: one workgroup per CU, one wave per SIMD.
+constexpr int kRingDepth = 3;   // K windows in flight per wave (8-tile items)
 constexpr size_t sk_ring_bytes(int wave_bytes) { return (size_t)4 * wave_bytes; }   // 4 waves
+// Windows in flight for class MT: 4-tile items have smaller windows and run
+// deeper rings, so a wave keeps about as many bytes in flight.
+constexpr int ring_depth(int nt, int mt) { return nt >= 8 ? kRingDepth : (mt == 1 ? 6 : mt == 2 ? 5 : 4); }
+// A wave's share of the LDS: the largest ring of the three classes.
+template <int DT, int NT> constexpr int ring_wave_bytes() {
+  constexpr int b1 = RingCfg<DT, 1, NT, ring_depth(NT, 1)>::WAVE_BYTES;
+  constexpr int b2 = RingCfg<DT, 2, NT, ring_depth(NT, 2)>::WAVE_BYTES;
+  constexpr int b4 = RingCfg<DT, 4, NT, ring_depth(NT, 4)>::WAVE_BYTES;
+  return b1 > b2 ? (b1 > b4 ? b1 : b4) : (b2 > b4 ? b2 : b4);
+}
 
-// One launch for the three row classes.  Workgroups reach the 8 XCDs
-// round-robin (blockIdx % 8).  Each class takes a contiguous band of
-// blockIdx, the 17..32-row class first (its items take longest, so they
-// start first), then 9..16, then 1..8 rows; inside a band XCD x takes the
-// contiguous range x * per_xcd ... of the class's items, so the items of a
-// group run on one or two XCDs and its activation rows, re-read by every
-// item, stay in that XCD's L2.  The 4 waves of a workgroup are independent
-// (each streams its own item through its own ring, sized for 32 rows), so a
-// workgroup may straddle two groups or classes.  Bands are sized from the
-// device-side list lengths; the host sizes the grid from upper bounds and
-// workgroups past the bands exit at once.
 template <int DT, int MODE>
 __global__ __launch_bounds__(256) void ffn_skinny_kernel(Args a) {
-  constexpr int NT = kSkNT;
+  constexpr int NT = sk_nt(DT, MODE);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cols_per_item = MODE == 1 ? 4 * NT : 8 * NT;
   const int items = (MODE == 1 ? a.I : a.H) / cols_per_item;
@@ -537,10 +540,10 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(Args a) {
   int g;
   const Group gr = group_of_entry(a, a.plan[kPlanHead + cls * 2 * a.G + gi], &g);
   extern __shared__ __attribute__((aligned(16))) uint8_t sk_ring[];
-  uint8_t* ring = sk_ring + wave * RingCfg<DT, 4, NT, kRingDepth>::WAVE_BYTES;
-  if (cls == 2) skinny_ring<DT, MODE, 4, NT, kRingDepth>(a, gr, g, it, lane, ring);
-  else if (cls == 1) skinny_ring<DT, MODE, 2, NT, kRingDepth>(a, gr, g, it, lane, ring);
-  else skinny_ring<DT, MODE, 1, NT, kRingDepth>(a, gr, g, it, lane, ring);
+  uint8_t* ring = sk_ring + wave * ring_wave_bytes<DT, NT>();
+  if (cls == 2) skinny_ring<DT, MODE, 4, NT, ring_depth(NT, 4)>(a, gr, g, it, lane, ring);
+  else if (cls == 1) skinny_ring<DT, MODE, 2, NT, ring_depth(NT, 2)>(a, gr, g, it, lane, ring);
+  else skinny_ring<DT, MODE, 1, NT, ring_depth(NT, 1)>(a, gr, g, it, lane, ring);
 }
 
 // The shared expert when T <= kSkinnyRows: its row count is known on the
@@ -558,7 +561,7 @@ __global__ __launch_bounds__(64 * kShKS) void ffn_shared_skinny_kernel(Args a) {
 
 template <int DT, int MODE>
 hipError_t launch_sk(unsigned grid, const Args& a, hipStream_t st) {
-  constexpr size_t lds = sk_ring_bytes(RingCfg<DT, 4, kSkNT, kRingDepth>::WAVE_BYTES);
+  constexpr size_t lds = sk_ring_bytes(ring_wave_bytes<DT, sk_nt(DT, MODE)>());
   static_assert(lds <= 160 * 1024, "LDS budget");
   hipError_t e = moe::ensure_dynamic_lds(reinterpret_cast<const void*>(&ffn_skinny_kernel<DT, MODE>), (int)lds);
   if (e != hipSuccess) return e;
