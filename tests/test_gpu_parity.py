@@ -151,6 +151,8 @@ MANY = {
                                              score="softmax"),
     "many_e32_split": _PF.with_(name="many_e32_split", T=1000, H=2048),
     "many_e32_one_range": _PF.with_(name="many_e32_one_range", T=700, H=512),
+    # K = 384: 6 slices of 64 (not a power of two), exactly 512 tokens (the threshold)
+    "many_e64_h384_t512": _D16.with_(name="many_e64_h384_t512", T=512, H=384, E=64, k=6),
     "many_e256_groups_split": _D16.with_(name="many_e256_groups_split", T=1030, H=1024, n_group=8, topk_group=4),
 }
 
