@@ -260,6 +260,31 @@ def test_dispatch_exact(T, E, k):
         np.testing.assert_array_equal(to_np(g), ref[name], err_msg=name)
 
 
+def test_dispatch_maximum_pairs():
+    """The largest call the library accepts, T * k = 2^24 pairs (E = 256,
+    k = 8), against the definitions the oracle's loops are pinned to (too
+    slow for its plain loops here): counts = bincount, offsets = exclusive
+    cumsum, sorted_pair = stable argsort of the expert ids, pair_slot = its
+    inverse."""
+    T, E, k = 1 << 21, 256, 8
+    rng = np.random.default_rng(24)
+    base = rng.integers(0, E, size=(T, 1))
+    step = 2 * rng.integers(0, E // 2, size=(T, 1)) + 1          # odd: k distinct experts per token
+    idx = ((base + step * np.arange(k)[None, :]) % E).astype(np.int32)
+    cfg = moe.make_cfg(T, 128, E, k, 64, 64)
+    got = moe.moe_dispatch(cfg, torch.from_numpy(idx).to(DEV))
+    torch.cuda.synchronize()
+    flat = idx.reshape(-1).astype(np.int64)
+    counts = np.bincount(flat, minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    sorted_pair = np.argsort(flat, kind="stable")
+    pair_slot = np.empty_like(sorted_pair)
+    pair_slot[sorted_pair] = np.arange(flat.shape[0])
+    for name, g, r in zip(("counts", "offsets", "sorted_pair", "pair_slot"), got,
+                          (counts, offsets, sorted_pair, pair_slot)):
+        np.testing.assert_array_equal(to_np(g), r, err_msg=name)
+
+
 @pytest.mark.parametrize("T", [4096, 65536])
 def test_dispatch_all_pairs_to_one_expert(T):
     E, k = 8, 1
