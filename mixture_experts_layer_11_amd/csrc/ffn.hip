@@ -135,9 +135,9 @@ hipError_t run_shared(const moe_cfg& c, const Args& a, hipStream_t st) {
 // The routed experts, on the stream it is given: plan, then per projection
 // the three skinny classes and the tiled groups.  Grids are sized on the
 // host from upper bounds; workgroups beyond the device-side lists exit.
-// run_routed calls hook(2 * mode - 2) before and hook(2 * mode - 1) after
-// the streaming launch of each GEMM (mode 1, 2); run_ffn forks the shared
-// expert there.
+// run_routed calls hook(2 * mode - 2) at the start of each GEMM's stage (mode
+// 1, 2; for fp8 before the quantisation of h) and hook(2 * mode - 1) after
+// its streaming launch; run_ffn forks the shared expert there.
 struct NoHook {
   hipError_t operator()(int) const { return hipSuccess; }
 };
@@ -159,6 +159,7 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st, const Hoo
   // halves mode: the shared expert's rows [P, P + T) of h are the routed lists' too
   const int qrows = P + (a.halves && a.has_shared ? c.T : 0);
   for (int mode = 1; mode <= 2; ++mode) {
+    if ((e = hook(2 * mode - 2)) != hipSuccess) return e;
     if (mode == 2 && DT == MOE_FP8_E4M3) {
       e = moe::launch_quant_fp8(qrows, c.I, a.qb, a.h, MOE_F32, const_cast<uint8_t*>(a.a2), const_cast<float*>(a.a2s),
                                 st);
@@ -179,7 +180,6 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st, const Hoo
       if (groups == 0 || min_rows > c.T) continue;
       bands += moe::ceil_div(moe::ceil_div(groups * items, 4LL), 8LL);   // 4 items per workgroup
     }
-    if ((e = hook(2 * mode - 2)) != hipSuccess) return e;
     // When both regimes are expected (a mean of 17..1023 rows per routed
     // expert), the tiled launches go on a second side stream, forked before
     // the streaming launch and joined after it, so the two share the device
@@ -224,7 +224,8 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st, const Hoo
 // st (an event records st's position, the side stream waits on it) and
 // joined back at the end (st waits on an event recorded after the shared
 // launches), so it overlaps the routed experts instead of running alone on
-// part of the device.  The fork comes right before the routed GEMM2 stage:
+// part of the device.  The fork comes at the start of the routed GEMM2 stage
+// (for fp8 before h is quantised, which the shared GEMM1 then overlaps):
 // the routed GEMM1, the longer of the two, keeps the whole device, and the
 // shared expert runs beside the routed GEMM2 (measured against forking at
 // the start: decode256 2.825 -> 2.766 ms, decode256_fp8 1.537 -> 1.522 ms,
