@@ -69,17 +69,6 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return v;
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, o, 64);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, 64);
-    uint64_t w = ((uint64_t)hi << 32) | lo;
-    v = w > v ? w : v;
-  }
-  return v;
-}
-
 // ------------------------------------------------------------------ MFMA fragments
 //
 // A "fragment" is 16 bytes per lane of one operand of a 16x16 MFMA tile:
