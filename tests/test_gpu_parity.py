@@ -477,10 +477,23 @@ def test_all_tokens_to_one_expert():
 
 FULL = ["decode16", "decode256", "prefill8192_ep8", "clustered2048_fp8", "decode16_fp8", "decode256_fp8"]
 
+# Mid-size layers that take every path at once: the three-kernel dispatch
+# (more than 4096 pairs), the LDS-staged router, streaming and tiled groups
+# on separate streams (a mean of 17..1023 rows per expert), the forked shared
+# expert, fp8 128-row rest tiles and both weight-scale layouts.
+MID = {
+    "mid_zipf_bf16": get_config("prefill8192_ep8").with_(name="mid_zipf_bf16", T=4097, H=512, E=64, I=512,
+                                                         I_shared=512),
+    "mid_clustered_fp8": get_config("clustered2048_fp8").with_(name="mid_clustered_fp8", T=3001, H=512, E=64,
+                                                               I=2048, I_shared=2048),
+    "mid_fp8_tiles": get_config("decode16_fp8").with_(name="mid_fp8_tiles", routing="zipf", T=1500, H=512, E=64,
+                                                      I=2048, I_shared=2048),
+}
 
-@pytest.mark.parametrize("name", FULL)
+
+@pytest.mark.parametrize("name", FULL + sorted(MID))
 def test_forward_full_size_sampled(name):
-    cfg = get_config(name)
+    cfg = MID[name] if name in MID else get_config(name)
     _log(f"[full {name}] drawing inputs on the GPU")
     gin = make_inputs(cfg, DEV)
     mc = moe.cfg_from(cfg)
