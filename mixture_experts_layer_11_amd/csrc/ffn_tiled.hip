@@ -5,6 +5,8 @@
 // deployment" (sections "GroupGEMM" and "Future work") finds the grouped
 // GEMM compute-bound once the rows per expert are many.
 
+#include <type_traits>
+
 #include "ffn.h"
 
 namespace {
@@ -49,7 +51,14 @@ template <int DT, int TM> struct TileCfg {
   // fp8 scale area: per-slice scales [NST][NSC] floats, or, when the slice
   // count is a multiple of 4, two blocks of [NSC][4 slices] floats
   static constexpr size_t SCB = (size_t)2 * NSC * 16;
-  static constexpr size_t LDS_BYTES = (size_t)NST * STAGE + (DT == MOE_FP8_E4M3 ? SCB : 0);
+  // Epilogue staging of the output tile (bf16 and fp8 layers): TM rows of at
+  // most 512 bytes (256 bf16 y columns, or 128 h columns of bf16 or fp32),
+  // padded by 16 bytes per row so that the 4 row groups of a wave's writes
+  // fall in different LDS banks.
+  static constexpr size_t EPI_STRIDE = 512 + 16;
+  static constexpr size_t EPI_BYTES = DT == MOE_F32 ? 0 : (size_t)TM * EPI_STRIDE;
+  static constexpr size_t MAIN_BYTES = (size_t)NST * STAGE + (DT == MOE_FP8_E4M3 ? SCB : 0);
+  static constexpr size_t LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   __device__ static __forceinline__ int off(int r, int c) { return r * SL + ((c ^ (r & 7)) << 4); }
 };
@@ -315,6 +324,56 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
   wait_vmcnt<0>();   // the full-tile loop's last reload is still in flight
 
   // ---- epilogue: lane holds rows wm*64 + i*16 + 4*grp + q, columns wn*WN + j*16 + row
+  if constexpr (DT != MOE_F32) {
+    // Through LDS: each lane writes its values (2-byte bf16, or fp32 h in
+    // the fp8 layer) into the row-major output tile, then the workgroup
+    // copies whole 16-byte chunks of each row out.  Stored straight from the
+    // accumulators, a lane's values are single 2-byte elements 16 columns
+    // apart: 64 to 128 scattered store instructions per lane (prefill GEMM2
+    // 1742 -> 1699 us staged).
+    using OT = typename std::conditional<MODE == 1 && FP8, float, uint16_t>::type;
+    constexpr int ES = sizeof(OT);
+    constexpr int OC = MODE == 1 ? kTN / 2 : kTN;       // output columns of the tile
+    constexpr int CPR = OC * ES / 16;                   // 16-byte chunks per row
+    constexpr int S = (int)C::EPI_STRIDE;
+    static_assert(OC * ES <= 512, "an output row of the tile fits a staging row");
+    __syncthreads();                                    // every wave is done with the stages
+    uint8_t* lt = smem;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i >= mval) break;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = wm * 64 + i * 16 + 4 * grp + q;
+        uint8_t* lrow = lt + r * S;
+        if (MODE == 1) {
+#pragma unroll
+          for (int jp = 0; jp < NTW / 2; ++jp) {
+            const float v = silu(acc[i][2 * jp][q]) * acc[i][2 * jp + 1][q];
+            const int lc = (wn * (NTW / 2) + jp) * 16 + row;
+            if constexpr (FP8) reinterpret_cast<float*>(lrow)[lc] = v;
+            else reinterpret_cast<uint16_t*>(lrow)[lc] = f32_to_bf16(v);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < NTW; ++j) reinterpret_cast<uint16_t*>(lrow)[wn * WN + j * 16 + row] = f32_to_bf16(acc[i][j][q]);
+        }
+      }
+    }
+    __syncthreads();
+    const int ncols = MODE == 1 ? a.I : a.H;            // row length of h or y (a multiple of 8)
+    const int col0 = nt * OC;
+    uint8_t* obase = MODE == 1 ? a.h + (size_t)(gr.slot0 + row0) * ncols * ES
+                               : (gr.routed ? a.y_sorted : a.y_shared) + (size_t)out_row(a, gr, row0) * ncols * ES;
+    for (int id = tid; id < rows * CPR; id += 512) {
+      const int r = id / CPR, ch = id - r * CPR;
+      const int col = col0 + ch * (16 / ES);
+      if (col < ncols)
+        *reinterpret_cast<i32x4*>(obase + ((size_t)r * ncols + col) * ES) =
+            *reinterpret_cast<const i32x4*>(lt + r * S + ch * 16);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (i >= mval) break;
