@@ -368,9 +368,13 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
     for (int id = tid; id < rows * CPR; id += 512) {
       const int r = id / CPR, ch = id - r * CPR;
       const int col = col0 + ch * (16 / ES);
+      // Streaming (nontemporal) stores: the tile is written once and the
+      // next reader is another launch, so it need not displace the weight
+      // and activation panels that neighbouring workgroups share in L2.
       if (col < ncols)
-        *reinterpret_cast<i32x4*>(obase + ((size_t)r * ncols + col) * ES) =
-            *reinterpret_cast<const i32x4*>(lt + r * S + ch * 16);
+        __builtin_nontemporal_store(
+            *reinterpret_cast<const i32x4*>(lt + r * S + ch * 16),
+            reinterpret_cast<i32x4*>(obase + ((size_t)r * ncols + col) * ES));
     }
     return;
   }
