@@ -158,9 +158,12 @@ hipError_t launch_shared_skinny(int mode, int T, const Args& a, hipStream_t st);
 // Tiled grouped GEMM with tm-row tiles (256 or 128): the plan's list of that
 // size (shared = false) or the shared expert's tiles of that size (shared =
 // true: floor(T / 256) full tiles, or ceil((T mod 256) / 128) tiles for the
-// rest); ntn column tiles each.
+// rest); ntn column tiles each.  stream_w (routed tiles only) loads the
+// weight slices nontemporally, for when each group's weights are read by
+// about one row tile.
 template <int DT>
-hipError_t launch_tiled(int mode, bool shared, int tm, unsigned grid, int ntn, const Args& a, hipStream_t st);
+hipError_t launch_tiled(int mode, bool shared, int tm, bool stream_w, unsigned grid, int ntn, const Args& a,
+                        hipStream_t st);
 
 }  // namespace ffn
 }  // namespace moe

@@ -124,8 +124,8 @@ hipError_t run_shared(const moe_cfg& c, const Args& a, hipStream_t st) {
       const int full = a.mid_rest ? c.T / kTileRows : moe::ceil_div(c.T, kTileRows);
       const int rest = a.mid_rest ? moe::ceil_div(c.T % kTileRows, kMidRows) : 0;
       e = hipSuccess;
-      if (full > 0) e = launch_tiled<DT>(mode, true, kTileRows, (unsigned)(full * ntn), ntn, a, st);
-      if (e == hipSuccess && rest > 0) e = launch_tiled<DT>(mode, true, kMidRows, (unsigned)(rest * ntn), ntn, a, st);
+      if (full > 0) e = launch_tiled<DT>(mode, true, kTileRows, false, (unsigned)(full * ntn), ntn, a, st);
+      if (e == hipSuccess && rest > 0) e = launch_tiled<DT>(mode, true, kMidRows, false, (unsigned)(rest * ntn), ntn, a, st);
     }
     if (e != hipSuccess) return e;
   }
@@ -189,6 +189,12 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st, const Hoo
     const int mean_rows = P / c.E;
     const bool both = bands > 0 && (max_fat > 0 || max_mid > 0) && mean_rows > kSkinnyRows / 2 &&
                       mean_rows < 4 * kTileRows;
+    // With a mean of at most one 256-row tile per routed expert, most groups'
+    // weights are read by one row tile, and nontemporal loads keep them from
+    // displacing the activation rows that the column tiles share
+    // (clustered2048_fp8: 2.54 -> 2.50 ms).  With more row tiles per group
+    // the weights must stay cached (prefill8192_ep8: 5.72 -> 6.37 ms).
+    const bool stream_w = mean_rows <= kTileRows;
     hipStream_t tst = st;
     moe::SideStream ts{};
     if (both) {
@@ -199,17 +205,17 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st, const Hoo
     }
     const int ntn = mode == 1 ? moe::ceil_div(c.I, kTN / 2) : moe::ceil_div(c.H, kTN);
     if (both) {   // tiles first, so their workgroups are queued before the streaming ones
-      if (max_fat > 0 && (e = launch_tiled<DT>(mode, false, kTileRows, (unsigned)(max_fat * ntn), ntn, a, tst)) != hipSuccess)
+      if (max_fat > 0 && (e = launch_tiled<DT>(mode, false, kTileRows, stream_w, (unsigned)(max_fat * ntn), ntn, a, tst)) != hipSuccess)
         return e;
-      if (max_mid > 0 && (e = launch_tiled<DT>(mode, false, kMidRows, (unsigned)(max_mid * ntn), ntn, a, tst)) != hipSuccess)
+      if (max_mid > 0 && (e = launch_tiled<DT>(mode, false, kMidRows, stream_w, (unsigned)(max_mid * ntn), ntn, a, tst)) != hipSuccess)
         return e;
     }
     if (bands > 0 && (e = launch_skinny<DT>(mode, (unsigned)(8 * bands), a, st)) != hipSuccess) return e;
     if ((e = hook(2 * mode - 1)) != hipSuccess) return e;
     if (!both) {
-      if (max_fat > 0 && (e = launch_tiled<DT>(mode, false, kTileRows, (unsigned)(max_fat * ntn), ntn, a, st)) != hipSuccess)
+      if (max_fat > 0 && (e = launch_tiled<DT>(mode, false, kTileRows, stream_w, (unsigned)(max_fat * ntn), ntn, a, st)) != hipSuccess)
         return e;
-      if (max_mid > 0 && (e = launch_tiled<DT>(mode, false, kMidRows, (unsigned)(max_mid * ntn), ntn, a, st)) != hipSuccess)
+      if (max_mid > 0 && (e = launch_tiled<DT>(mode, false, kMidRows, stream_w, (unsigned)(max_mid * ntn), ntn, a, st)) != hipSuccess)
         return e;
     } else {
       if ((e = hipEventRecord(ts.join, ts.stream)) != hipSuccess) return e;

@@ -76,7 +76,9 @@ __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::
 // fetches 4 slices' scales of the slot's row into block (kt / 4) % 2, so
 // each scale row's cache line is touched once per 4 slices (a slice's 512
 // scales lie in 512 different rows); else 4 bytes per slice into stage st.
-template <int DT, int TM, bool BLK>
+// With SW the weight slices are loaded nontemporally: each is read by about
+// one row tile, so it should not displace what other workgroups share.
+template <int DT, int TM, bool BLK, bool SW>
 __device__ __forceinline__ void tile_issue(uint8_t* smem, const uint8_t* const* ga, const uint8_t* const* gb,
                                            const float* gs, int kt, int st, int wave) {
   using C = TileCfg<DT, TM>;
@@ -86,7 +88,7 @@ __device__ __forceinline__ void tile_issue(uint8_t* smem, const uint8_t* const* 
 #pragma unroll
   for (int i = 0; i < C::LPA; ++i) __builtin_amdgcn_global_load_lds(ga[i] + off, la + i * 1024, 16, 0, 0);
 #pragma unroll
-  for (int i = 0; i < C::LPB; ++i) __builtin_amdgcn_global_load_lds(gb[i] + off, lb + i * 1024, 16, 0, 0);
+  for (int i = 0; i < C::LPB; ++i) __builtin_amdgcn_global_load_lds(gb[i] + off, lb + i * 1024, 16, 0, SW ? 2 : 0);   // 2: nontemporal
   if constexpr (DT == MOE_FP8_E4M3) {
     uint8_t* sc = smem + C::NST * C::STAGE;
     if constexpr (BLK) {
@@ -101,7 +103,7 @@ __device__ __forceinline__ void tile_issue(uint8_t* smem, const uint8_t* const* 
   }
 }
 
-template <int DT, int MODE, bool SHARED, int TM, bool BLK>
+template <int DT, int MODE, bool SHARED, int TM, bool BLK, bool SW>
 __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
   using F = Frag<DT>;
   using C = TileCfg<DT, TM>;
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
 
 #pragma unroll
   for (int p = 0; p < NST - 1; ++p)
-    if (p < nkt) tile_issue<DT, TM, BLK>(smem, ga, gb, gs, p, p, wave);
+    if (p < nkt) tile_issue<DT, TM, BLK, SW>(smem, ga, gb, gs, p, p, wave);
   bool full_tile = false;
   if constexpr (!FP8) full_tile = mval == 4;
   if (full_tile) {
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
         i32x4 fa[SL / 64][4], fb[SL / 64][NTW];
 #pragma unroll
         for (int fs = 0; fs < SL / 64; ++fs) {
-          if (fs == 1) tile_issue<DT, TM, false>(smem, ga, gb, gs, min(kt + 1, nkt - 1), (kt + 1) & 1, wave);
+          if (fs == 1) tile_issue<DT, TM, false, SW>(smem, ga, gb, gs, min(kt + 1, nkt - 1), (kt + 1) & 1, wave);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             fa[fs][i] = *reinterpret_cast<const i32x4*>(&la[C::off(wm * 64 + i * 16 + row, fs * 4 + grp)]);
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
         wait_vmcnt<0>();
       }
       barrier_no_fence();                          // everyone's slice kt is in LDS; stage (kt-1) % NST is free
-      if (kt + NST - 1 < nkt) tile_issue<DT, TM, BLK>(smem, ga, gb, gs, kt + NST - 1, (kt + NST - 1) % NST, wave);
+      if (kt + NST - 1 < nkt) tile_issue<DT, TM, BLK, SW>(smem, ga, gb, gs, kt + NST - 1, (kt + NST - 1) % NST, wave);
       const uint8_t* la = smem + st * C::STAGE;
       const uint8_t* lb = la + TM * SL;
       if constexpr (!FP8) {
@@ -406,13 +408,13 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
   }
 }
 
-template <int DT, int MODE, bool SHARED, int TM, bool BLK>
+template <int DT, int MODE, bool SHARED, int TM, bool BLK, bool SW>
 hipError_t launch_fat(const char* name, unsigned grid, int ntn, const Args& a, hipStream_t st) {
   using C = TileCfg<DT, TM>;
-  hipError_t e = moe::ensure_dynamic_lds(reinterpret_cast<const void*>(&ffn_fat_kernel<DT, MODE, SHARED, TM, BLK>),
+  hipError_t e = moe::ensure_dynamic_lds(reinterpret_cast<const void*>(&ffn_fat_kernel<DT, MODE, SHARED, TM, BLK, SW>),
                                           (int)C::LDS_BYTES);
   if (e != hipSuccess) return e;
-  MOE_LAUNCH(name, (ffn_fat_kernel<DT, MODE, SHARED, TM, BLK>), dim3(grid), dim3(512), C::LDS_BYTES, st, a, ntn);
+  MOE_LAUNCH(name, (ffn_fat_kernel<DT, MODE, SHARED, TM, BLK, SW>), dim3(grid), dim3(512), C::LDS_BYTES, st, a, ntn);
   return hipGetLastError();
 }
 
@@ -422,31 +424,31 @@ namespace moe {
 namespace ffn {
 
 template <int DT>
-hipError_t launch_tiled(int mode, bool shared, int tm, unsigned grid, int ntn, const Args& a, hipStream_t st) {
+hipError_t launch_tiled(int mode, bool shared, int tm, bool stream_w, unsigned grid, int ntn, const Args& a,
+                        hipStream_t st) {
   static const char* const kName[2][2][2] = {                  // [mode - 1][shared][tm == 128]
       {{"ffn_gemm1_tiled", "ffn_gemm1_tiled128"}, {"ffn_gemm1_shared_tiled", "ffn_gemm1_shared_tiled128"}},
       {{"ffn_gemm2_tiled", "ffn_gemm2_tiled128"}, {"ffn_gemm2_shared_tiled", "ffn_gemm2_shared_tiled128"}}};
   const char* name = kName[mode - 1][shared ? 1 : 0][tm == 128 ? 1 : 0];
   // fp8 scale blocks of 4 slices need the slice count K / 128 to be a multiple of 4
   const bool blk = DT == MOE_FP8_E4M3 && (((mode == 1 ? a.H : a.I) / 128) & 3) == 0;
-#define MOE_TL(M, S, TMV)                                                                      \
-  (DT == MOE_FP8_E4M3 && blk ? launch_fat<DT, M, S, TMV, DT == MOE_FP8_E4M3>(name, grid, ntn, a, st) \
-                             : launch_fat<DT, M, S, TMV, false>(name, grid, ntn, a, st))
-  if (tm == 256) {
-    if (mode == 1) return shared ? MOE_TL(1, true, 256) : MOE_TL(1, false, 256);
-    return shared ? MOE_TL(2, true, 256) : MOE_TL(2, false, 256);
-  }
-  if constexpr (DT == MOE_FP8_E4M3) {   // 128-row tiles serve fp8 weights only
-    if (mode == 1) return shared ? MOE_TL(1, true, 128) : MOE_TL(1, false, 128);
-    return shared ? MOE_TL(2, true, 128) : MOE_TL(2, false, 128);
-  }
+  constexpr bool FP8 = DT == MOE_FP8_E4M3;
+#define MOE_TLB(M, S, TMV, SWV) \
+  (FP8 && blk ? launch_fat<DT, M, S, TMV, FP8, SWV>(name, grid, ntn, a, st) \
+              : launch_fat<DT, M, S, TMV, false, SWV>(name, grid, ntn, a, st))
+  // the shared expert's weights are read by every row tile: always cached
+#define MOE_TL(M, TMV) \
+  (shared ? MOE_TLB(M, true, TMV, false) : stream_w ? MOE_TLB(M, false, TMV, true) : MOE_TLB(M, false, TMV, false))
+  if (tm == 256) return mode == 1 ? MOE_TL(1, 256) : MOE_TL(2, 256);
+  if constexpr (FP8) return mode == 1 ? MOE_TL(1, 128) : MOE_TL(2, 128);   // 128-row tiles serve fp8 weights only
   return hipErrorInvalidValue;
 #undef MOE_TL
+#undef MOE_TLB
 }
 
-template hipError_t launch_tiled<MOE_F32>(int, bool, int, unsigned, int, const Args&, hipStream_t);
-template hipError_t launch_tiled<MOE_BF16>(int, bool, int, unsigned, int, const Args&, hipStream_t);
-template hipError_t launch_tiled<MOE_FP8_E4M3>(int, bool, int, unsigned, int, const Args&, hipStream_t);
+template hipError_t launch_tiled<MOE_F32>(int, bool, int, bool, unsigned, int, const Args&, hipStream_t);
+template hipError_t launch_tiled<MOE_BF16>(int, bool, int, bool, unsigned, int, const Args&, hipStream_t);
+template hipError_t launch_tiled<MOE_FP8_E4M3>(int, bool, int, bool, unsigned, int, const Args&, hipStream_t);
 
 }  // namespace ffn
 }  // namespace moe

@@ -60,7 +60,7 @@ def rocprof_name(kernel: str, w_dtype: str) -> str:
     if kernel.startswith("ffn_gemm") and "_tiled" in kernel:
         shared = "true" if "_shared_" in kernel else "false"
         tm = 128 if kernel.endswith("128") else 256
-        return f"void (anonymous namespace)::ffn_fat_kernel<{dt}, {int(kernel[8])}, {shared}, {tm}, "   # then the fp8 scale-block flag
+        return f"void (anonymous namespace)::ffn_fat_kernel<{dt}, {int(kernel[8])}, {shared}, {tm}, "   # then the fp8 scale-block and streamed-weight flags
     if kernel.startswith("ffn_gemm") and kernel.endswith("_shared_skinny"):
         return f"void (anonymous namespace)::ffn_shared_skinny_kernel<{dt}, {int(kernel[8])}, "
     fixed = {"ffn_plan": "(anonymous namespace)::ffn_plan_kernel",
