@@ -154,7 +154,11 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st, const Hoo
   // group (256 rows, or with mid_rest 128 rows), of which there are at most
   // min(E, P / (kSkinnyRows + 1)).
   const int tiled_groups = c.T > kSkinnyRows ? (P / (kSkinnyRows + 1) < c.E ? P / (kSkinnyRows + 1) : c.E) : 0;
-  const int max_fat = tiled_groups > 0 ? P / kTileRows + tiled_groups : 0;
+  // With mid_rest every 256-row tile, full or partial, holds more than 128 of
+  // the P rows, so there are also at most P / 129 of them (clustered2048_fp8:
+  // 127 instead of 320 tiles in the grid, the rest exiting at once).
+  int max_fat = tiled_groups > 0 ? P / kTileRows + tiled_groups : 0;
+  if (a.mid_rest && P / (kMidRows + 1) < max_fat) max_fat = P / (kMidRows + 1);
   const int max_mid = a.mid_rest ? tiled_groups : 0;
   // halves mode: the shared expert's rows [P, P + T) of h are the routed lists' too
   const int qrows = P + (a.halves && a.has_shared ? c.T : 0);
