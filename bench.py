@@ -225,7 +225,22 @@ def main(argv=None):
         step()
     torch.cuda.synchronize()
     breakdown = moe.moe_profile_stop()
-    dom = max(breakdown, key=lambda n: breakdown[n][1])
+    # The dominant kernel is the one with the longest roofline time: its
+    # algorithmic bytes at the HBM peak or its FLOPs at the MFMA peak,
+    # whichever is longer, which the routing alone fixes.  Event spans would
+    # serve where kernels run one after another, but the streaming and tiled
+    # GEMMs that share the device (a mean of 17..1023 rows per expert) swap
+    # places from run to run.  Spans break ties and cover unmodelled kernels.
+    models, layer = kernel_models(cfg, counts_h)
+    wdt = "fp8" if cfg.w_dtype == "fp8" else cfg.act_dtype
+
+    def roof_s(n):
+        mm = models.get(n)
+        if not mm:
+            return -1.0
+        return max(mm["bytes"] / (HBM_PEAK_GBPS * 1e9), mm["flops"] / (MFMA_PEAK_TFLOPS[wdt] * 1e12))
+
+    dom = max(breakdown, key=lambda n: (roof_s(n), breakdown[n][1]))
 
     # timed region: K steps; the dominant kernel is bracketed by HIP events on its launch stream
     moe.moe_profile_start(dom)
@@ -245,10 +260,8 @@ def main(argv=None):
     ms_per_step = wall_ms / args.steps
     tokens_per_s = cfg.T * args.steps / (wall_ms / 1e3)
 
-    models, layer = kernel_models(cfg, counts_h)
     launches, tot_ms = prof[dom]
     avg_ms = tot_ms / max(launches, 1)
-    wdt = "fp8" if cfg.w_dtype == "fp8" else cfg.act_dtype
     if dom in models:
         mm = models[dom]
         # the kernel's own roofline: HBM-bound below the ridge point
