@@ -319,6 +319,30 @@ def test_expert_ffn_small(name):
     _log(f"[expert_ffn {name}] y_sorted err {e1} y_shared err {e2}")
 
 
+@pytest.mark.parametrize("sizes", [[129] * 4, [385, 129, 129, 129], [385, 129, 33, 5, 0]])
+def test_expert_ffn_fp8_tile_bound(sizes):
+    """Crafted group sizes at the 256-row tile grid's bound.  With 128-row rest
+    tiles (fp8) every 256-row tile, full or partial, holds at least 129 rows,
+    so a launch of P // 129 tiles covers them all; groups of 129 and 256 + 129
+    rows reach that bound exactly.  The last case adds a 128-row rest tile, a
+    streaming group and an empty group."""
+    E, T = len(sizes), sum(sizes)
+    cfg = get_config("clustered2048_fp8").with_(name="fp8_tile_bound", routing="random", T=T, H=512, E=E, k=1,
+                                                I=2048, I_shared=0)
+    inp, gin = _small_inputs(cfg)
+    # k = 1: pair p is token p; any order within a group is a valid dispatch
+    sorted_pair = np.random.default_rng(5).permutation(T).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    ow = oracle.OracleWeights.from_inputs(inp)
+    xa = oracle.prepare_activations(inp.x.double().numpy(), ow.fp8, ow.block)
+    ref_ys, _ = oracle.expert_ffn(xa, offsets, sorted_pair, 1, ow)
+    ys, _ = moe.moe_expert_ffn(moe.cfg_from(cfg), gin.x, torch.from_numpy(offsets).to(DEV),
+                               torch.from_numpy(sorted_pair).to(DEV), moe.Weights.from_inputs(gin))
+    torch.cuda.synchronize()
+    e = assert_outputs_close(ys, ref_ys, tol_key(cfg), "y_sorted")
+    _log(f"[expert_ffn tile bound {sizes}] y_sorted err {e}")
+
+
 @pytest.mark.parametrize("name", sorted(SMALL))
 def test_combine_small(name):
     cfg = SMALL[name]
