@@ -16,6 +16,7 @@
 
 #include "moe_common.h"
 #include "moe_launch.h"
+#include "plan.h"
 
 namespace {
 
@@ -143,11 +144,14 @@ __global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* __r
 // rank among equal experts of lower lane (the same 64-step register scan).
 constexpr int kSmallP = 4096;
 
+// With PLAN the workgroup then builds the expert FFN's work lists from the
+// histogram it holds (the FFN's plan launch is skipped).
+template <bool PLAN>
 __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __restrict__ idx, int P, int E,
                                                               int32_t* __restrict__ counts,
                                                               int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ sorted_pair,
-                                                              int32_t* __restrict__ pair_slot) {
+                                                              int32_t* __restrict__ pair_slot, moe::PlanArgs pa) {
   __shared__ int hist[256];
   __shared__ int run[256];
   __shared__ int wcnt[16][256];
@@ -205,6 +209,14 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __r
     }
     __syncthreads();
   }
+  if constexpr (PLAN) {
+    __shared__ int sk[3 * 512];
+    __shared__ int ft[512];
+    __shared__ int mt[512];
+    int m = 0;   // group tid's rows: the histogram, or all T tokens for the shared expert
+    if (tid < pa.G) m = tid < E ? hist[tid] : pa.T;
+    moe::ffn::build_plan(pa, m, sk, ft, mt);
+  }
 }
 
 }  // namespace
@@ -216,12 +228,21 @@ static int dispatch_nseg(const moe_cfg& c) { return ceil_div((long long)c.T * c.
 size_t dispatch_ws_bytes(const moe_cfg& c) { return 2 * (size_t)dispatch_nseg(c) * c.E * sizeof(int32_t); }
 
 hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, int32_t* counts, int32_t* offsets,
-                           int32_t* sorted_pair, int32_t* pair_slot, int32_t* seg_ws, hipStream_t st) {
+                           int32_t* sorted_pair, int32_t* pair_slot, int32_t* seg_ws, hipStream_t st,
+                           const PlanArgs* plan, bool* planned) {
   const int P = c.T * c.k;
+  if (planned) *planned = false;
   if (P <= kSmallP) {
-    MOE_LAUNCH("dispatch_small", dispatch_small_kernel, dim3(1), dim3(1024), 0, st, idx, P, c.E, counts, offsets,
-               sorted_pair, pair_slot);
-    return hipGetLastError();
+    if (plan) {
+      MOE_LAUNCH("dispatch_small", dispatch_small_kernel<true>, dim3(1), dim3(1024), 0, st, idx, P, c.E, counts,
+                 offsets, sorted_pair, pair_slot, *plan);
+    } else {
+      MOE_LAUNCH("dispatch_small", dispatch_small_kernel<false>, dim3(1), dim3(1024), 0, st, idx, P, c.E, counts,
+                 offsets, sorted_pair, pair_slot, PlanArgs{});
+    }
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess && plan && planned) *planned = true;
+    return e;
   }
   const int nseg = dispatch_nseg(c);
   int32_t* seg_counts = seg_ws;

@@ -35,6 +35,7 @@
 // with scale_a[row] * scale_w[col] and accumulated on the vector ALU.
 
 #include "ffn.h"
+#include "plan.h"
 
 namespace {
 
@@ -43,66 +44,13 @@ using namespace moe::ffn;
 // ------------------------------------------------------------------ plan
 
 __global__ __launch_bounds__(512) void ffn_plan_kernel(Args a) {
-  __shared__ int sk[3][512];
+  __shared__ int sk[3 * 512];
   __shared__ int ft[512];
   __shared__ int mt[512];
   const int g = threadIdx.x;
   int m = 0;
   if (g < a.G) m = g < a.E ? a.offsets[g + 1] - a.offsets[g] : a.T;
-  // skinny class: 0 for 1..8 rows, 1 for 9..16, 2 for 17..32; larger groups
-  // take floor(m / 256) full tiles, and their last m mod 256 rows one more
-  // 256-row tile, or with mid_rest one 128-row tile if they are at most 128
-  // (one 256-row tile above that, which reads the weights once).  The
-  // shared expert has launches of its own, except in halves mode (T <= 16):
-  // there every group, the shared expert included, enters the <= 8-row list
-  // as one or two 8-row halves, so the other lists stay empty.
-  const bool shared = g == a.E;
-  const bool listed = m > 0 && m <= kSkinnyRows && (!shared || a.halves);
-  const int cls = listed ? (a.halves || m <= 8 ? 0 : m <= 16 ? 1 : 2) : -1;
-  const int nent = cls < 0 ? 0 : (a.halves ? (m + 7) / 8 : 1);   // list entries of this group
-  const bool tiled = m > kSkinnyRows && !shared;
-  const int rest = m % kTileRows;
-  const bool rest_fat = a.mid_rest && rest > kMidRows;   // one partial 256-row tile reads the weights once
-  const int tiles = tiled ? (a.mid_rest ? m / kTileRows + (rest_fat ? 1 : 0) : (m + kTileRows - 1) / kTileRows) : 0;
-  const int mids = tiled && a.mid_rest && !rest_fat ? (rest + kMidRows - 1) / kMidRows : 0;
-#pragma unroll
-  for (int c = 0; c < 3; ++c) sk[c][g] = cls == c ? nent : 0;
-  ft[g] = tiles;
-  mt[g] = mids;
-  __syncthreads();
-  for (int d = 1; d < 512; d <<= 1) {
-    int v[3];
-#pragma unroll
-    for (int c = 0; c < 3; ++c) v[c] = g >= d ? sk[c][g - d] : 0;
-    const int v2 = g >= d ? ft[g - d] : 0;
-    const int v3 = g >= d ? mt[g - d] : 0;
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < 3; ++c) sk[c][g] += v[c];
-    ft[g] += v2;
-    mt[g] += v3;
-    __syncthreads();
-  }
-  int32_t* plan = const_cast<int32_t*>(a.plan);
-  if (g == 511) {
-#pragma unroll
-    for (int c = 0; c < 3; ++c) plan[c] = sk[c][511];
-    plan[3] = ft[511];
-    plan[4] = mt[511];
-  }
-  for (int h = 0; h < nent; ++h) plan[kPlanHead + cls * 2 * a.G + sk[cls][g] - nent + h] = g | (h << 16);
-  int32_t* fat = plan + kPlanHead + 6 * a.G;
-  const int t0 = ft[g] - tiles;
-  for (int i = 0; i < tiles; ++i) {
-    fat[2 * (t0 + i)] = g;
-    fat[2 * (t0 + i) + 1] = i * kTileRows;
-  }
-  int32_t* mid = fat + 2 * a.fat_cap;
-  const int m0 = mt[g] - mids;
-  for (int i = 0; i < mids; ++i) {
-    mid[2 * (m0 + i)] = g;
-    mid[2 * (m0 + i) + 1] = (m / kTileRows) * kTileRows + i * kMidRows;
-  }
+  build_plan(moe::PlanArgs{const_cast<int32_t*>(a.plan), a.G, a.E, a.T, a.fat_cap, a.halves, a.mid_rest}, m, sk, ft, mt);
 }
 
 // The shared expert: its own launches, on the stream it is given.
@@ -143,10 +91,12 @@ struct NoHook {
 };
 
 template <int DT, typename Hook = NoHook>
-hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st, const Hook& hook = Hook()) {
-  MOE_LAUNCH("ffn_plan", ffn_plan_kernel, dim3(1), dim3(512), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st, bool planned, const Hook& hook = Hook()) {
+  hipError_t e;
+  if (!planned) {   // else the dispatch built the plan already
+    MOE_LAUNCH("ffn_plan", ffn_plan_kernel, dim3(1), dim3(512), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int P = a.P;
   // Upper bounds of the tile lists: a token picks k distinct experts, so a
   // routed group has at most T rows and none is tiled when T <= kSkinnyRows.
@@ -245,8 +195,8 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st, const Hoo
 // compute-bound like the routed tiles: both stay on st, where running beside
 // the routed kernels would only add contention.
 template <int DT>
-hipError_t run_ffn(const moe_cfg& c, const Args& a, hipStream_t st) {
-  if (!a.has_shared || a.halves) return run_routed<DT>(c, a, st);
+hipError_t run_ffn(const moe_cfg& c, const Args& a, hipStream_t st, bool planned) {
+  if (!a.has_shared || a.halves) return run_routed<DT>(c, a, st, planned);
   moe::SideStream side;
   hipError_t e = moe::side_stream(&side);
   if (e != hipSuccess) return e;
@@ -255,7 +205,7 @@ hipError_t run_ffn(const moe_cfg& c, const Args& a, hipStream_t st) {
       moe::ceil_div(c.I, kTN / 2);
   if (c.T <= kSkinnyRows || shared_tiles1 >= side.cus) {
     e = run_shared<DT>(c, a, st);
-    return e != hipSuccess ? e : run_routed<DT>(c, a, st);
+    return e != hipSuccess ? e : run_routed<DT>(c, a, st, planned);
   }
   hipError_t es = hipSuccess;
   auto fork = [&](int at) -> hipError_t {   // at 2: the routed GEMM2 stage is next
@@ -266,7 +216,7 @@ hipError_t run_ffn(const moe_cfg& c, const Args& a, hipStream_t st) {
     es = run_shared<DT>(c, a, side.stream);
     return es;
   };
-  hipError_t er = run_routed<DT>(c, a, st, fork);
+  hipError_t er = run_routed<DT>(c, a, st, planned, fork);
   // join even after a failed launch, so that work queued later on st never
   // runs ahead of work already queued on the side stream
   if ((e = hipEventRecord(side.join, side.stream)) == hipSuccess) e = hipStreamWaitEvent(st, side.join, 0);
@@ -287,11 +237,23 @@ size_t ffn_plan_ints(const moe_cfg& c) {
   return kPlanHead + 6 * (size_t)G + 2 * (size_t)ffn_fat_cap(c) + 2 * (size_t)c.E;
 }
 
+PlanArgs ffn_plan_args(const moe_cfg& c, int32_t* plan) {
+  PlanArgs p;
+  p.plan = plan;
+  p.E = c.E;
+  p.G = c.E + (c.I_shared > 0 ? 1 : 0);
+  p.T = c.T;
+  p.fat_cap = ffn_fat_cap(c);
+  p.halves = c.T <= 16 ? 1 : 0;
+  p.mid_rest = c.w_dtype == MOE_FP8_E4M3 ? 1 : 0;   // HBM-bound medium groups: deeper pipeline on 128-row tiles
+  return p;
+}
+
 size_t ffn_h_elem_bytes(const moe_cfg& c) { return c.w_dtype == MOE_BF16 ? 2 : 4; }
 
 hipError_t launch_expert_ffn(const moe_cfg& c, const void* x, const int32_t* offsets,
                              const int32_t* sorted_pair, const moe_weights& w, void* y_sorted,
-                             void* y_shared, const FfnWs& ws, hipStream_t st) {
+                             void* y_shared, const FfnWs& ws, hipStream_t st, bool planned) {
   Args a{};
   a.T = c.T;
   a.H = c.H;
@@ -315,11 +277,12 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const void* x, const int32_t* off
   a.h = static_cast<uint8_t*>(ws.h);
   a.y_sorted = static_cast<uint8_t*>(y_sorted);
   a.y_shared = static_cast<uint8_t*>(y_shared);
-  a.plan = ws.plan;
-  a.G = c.E + (a.has_shared ? 1 : 0);
-  a.fat_cap = ffn_fat_cap(c);
-  a.halves = c.T <= 16;
-  a.mid_rest = c.w_dtype == MOE_FP8_E4M3;   // HBM-bound medium groups: deeper pipeline on 128-row tiles
+  const PlanArgs pa = ffn_plan_args(c, ws.plan);
+  a.plan = pa.plan;
+  a.G = pa.G;
+  a.fat_cap = pa.fat_cap;
+  a.halves = pa.halves;
+  a.mid_rest = pa.mid_rest;
   if (c.w_dtype == MOE_FP8_E4M3) {
     hipError_t e = launch_quant_fp8(c.T, c.H, c.quant_block, x, MOE_BF16, ws.xq, ws.xs, st);
     if (e != hipSuccess) return e;
@@ -327,12 +290,12 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const void* x, const int32_t* off
     a.a1s = ws.xs;
     a.a2 = ws.hq;
     a.a2s = ws.hs;
-    return run_ffn<MOE_FP8_E4M3>(c, a, st);
+    return run_ffn<MOE_FP8_E4M3>(c, a, st, planned);
   }
   a.a1 = static_cast<const uint8_t*>(x);
   a.a2 = a.h;
-  if (c.w_dtype == MOE_BF16) return run_ffn<MOE_BF16>(c, a, st);
-  return run_ffn<MOE_F32>(c, a, st);
+  if (c.w_dtype == MOE_BF16) return run_ffn<MOE_BF16>(c, a, st, planned);
+  return run_ffn<MOE_F32>(c, a, st, planned);
 }
 
 }  // namespace moe

@@ -329,9 +329,12 @@ int moe_forward(const moe_cfg* cfg, const void* x, const void* w_gate, const flo
   void* ysh = cfg->I_shared > 0 ? at<void>(ws, L.f_yshared) : nullptr;
   hipError_t e = moe::launch_route(*cfg, x, w_gate, sel_bias, idx, wt, at<float>(ws, L.route_part), st);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/route");
-  e = moe::launch_dispatch(*cfg, idx, counts, offsets, sorted, slot, at<int32_t>(ws, L.seg), st);
+  const moe::FfnWs fws = ffn_ws(ws, L);
+  const moe::PlanArgs pa = moe::ffn_plan_args(*cfg, fws.plan);
+  bool planned = false;   // the one-workgroup dispatch also builds the FFN plan
+  e = moe::launch_dispatch(*cfg, idx, counts, offsets, sorted, slot, at<int32_t>(ws, L.seg), st, &pa, &planned);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/dispatch");
-  e = moe::launch_expert_ffn(*cfg, x, offsets, sorted, *w, ys, ysh, ffn_ws(ws, L), st);
+  e = moe::launch_expert_ffn(*cfg, x, offsets, sorted, *w, ys, ysh, fws, st, planned);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/expert_ffn");
   e = moe::launch_combine(*cfg, ys, ysh, slot, wt, y, st);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/combine");

@@ -35,11 +35,23 @@ size_t route_ws_bytes(const moe_cfg& c);
 hipError_t launch_route(const moe_cfg& c, const void* x, const void* wg, const float* bias, int32_t* idx,
                         float* w, float* part, hipStream_t st);
 
+// ---- expert FFN work-list plan inputs besides the per-group row counts, so
+// that a kernel already holding the counts (the one-workgroup dispatch) can
+// build the plan and spare the FFN its own plan launch
+struct PlanArgs {
+  int32_t* plan;
+  int G, E, T, fat_cap, halves, mid_rest;
+};
+PlanArgs ffn_plan_args(const moe_cfg& c, int32_t* plan);
+
 // ---- dispatch
 constexpr int kDispatchSeg = 256;  // pairs per scatter segment (one wave each)
 size_t dispatch_ws_bytes(const moe_cfg& c);
+// With plan given, the one-workgroup path (up to 4096 pairs) also builds the
+// FFN plan from its counts and sets *planned.
 hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, int32_t* counts, int32_t* offsets,
-                           int32_t* sorted_pair, int32_t* pair_slot, int32_t* seg_ws, hipStream_t st);
+                           int32_t* sorted_pair, int32_t* pair_slot, int32_t* seg_ws, hipStream_t st,
+                           const PlanArgs* plan = nullptr, bool* planned = nullptr);
 
 // ---- fp8 block quantisation
 hipError_t launch_quant_fp8(int rows, int cols, int block, const void* in, int in_dtype, uint8_t* codes,
@@ -58,7 +70,7 @@ size_t ffn_plan_ints(const moe_cfg& c);
 size_t ffn_h_elem_bytes(const moe_cfg& c);
 hipError_t launch_expert_ffn(const moe_cfg& c, const void* x, const int32_t* offsets,
                              const int32_t* sorted_pair, const moe_weights& w, void* y_sorted,
-                             void* y_shared, const FfnWs& ws, hipStream_t st);
+                             void* y_shared, const FfnWs& ws, hipStream_t st, bool planned = false);
 
 // ---- side stream (streams.cpp): forked from and joined back to the caller's stream
 struct SideStream {
