@@ -44,13 +44,11 @@ using namespace moe::ffn;
 // ------------------------------------------------------------------ plan
 
 __global__ __launch_bounds__(512) void ffn_plan_kernel(Args a) {
-  __shared__ int sk[3 * 512];
-  __shared__ int ft[512];
-  __shared__ int mt[512];
+  __shared__ int wt[5 * 8];
   const int g = threadIdx.x;
   int m = 0;
   if (g < a.G) m = g < a.E ? a.offsets[g + 1] - a.offsets[g] : a.T;
-  build_plan(moe::PlanArgs{const_cast<int32_t*>(a.plan), a.G, a.E, a.T, a.fat_cap, a.halves, a.mid_rest}, m, sk, ft, mt);
+  build_plan(moe::PlanArgs{const_cast<int32_t*>(a.plan), a.G, a.E, a.T, a.fat_cap, a.halves, a.mid_rest}, m, wt);
 }
 
 // The shared expert: its own launches, on the stream it is given.
