@@ -384,6 +384,27 @@ def test_forward_small(name):
     _log(f"[forward {name}] near-ties={near} excluded={len(mism)} err={err}")
 
 
+@pytest.mark.parametrize("name", ["tiny_f32", "small_bf16", "small_fp8", "t16_e4_halves_bf16", "t600_e32_bf16"])
+def test_forward_matches_stages_bitwise(name):
+    """Up to 4096 pairs moe_forward builds the FFN work lists inside its
+    one-workgroup dispatch; the stage entry points build them in the FFN's own
+    plan kernel.  Both must give the same bits (t600_e32_bf16, 2400 pairs,
+    also takes the LDS-staged router)."""
+    cfg = SMALL[name]
+    assert cfg.T * cfg.k <= 4096
+    _, gin = _small_inputs(cfg)
+    mc = moe.cfg_from(cfg)
+    wts = moe.Weights.from_inputs(gin)
+    y, idx, w, counts = moe.moe_forward(mc, gin.x, gin.wg, gin.bias, wts, return_routing=True)
+    idx2, w2 = moe.moe_route(mc, gin.x, gin.wg, gin.bias)
+    counts2, off2, sp2, slot2 = moe.moe_dispatch(mc, idx2)
+    ys, ysh = moe.moe_expert_ffn(mc, gin.x, off2, sp2, wts)
+    y2 = moe.moe_combine(mc, ys, ysh, slot2, w2)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(w, w2) and torch.equal(counts, counts2)
+    assert torch.equal(y, y2)
+
+
 def test_forward_is_deterministic():
     cfg = SMALL["small_bf16"]
     _, gin = _small_inputs(cfg)
