@@ -15,7 +15,7 @@ representable value with ties to the even code and saturates at +-448.
 The block scale is ``fp32(amax / 448)`` (1 for an all-zero block) and a value
 v is encoded as ``e4m3(fp32(v / scale))``.
 
-Pins (tests/test_oracle_fp8.py): torch's ``float8_e4m3fn`` cast, a brute
+Pins (tests/test_oracle_pins.py, the fp8 section): torch's ``float8_e4m3fn`` cast, a brute
 force nearest-code search, and hand-derived values.
 """
 

@@ -365,6 +365,8 @@ def test_group_limited_worked_cases(golden_dir):
         assert plain["idx"][0].tolist() == case["plain_idx"], case["name"]
         s = [_sigmoid(case["logits"][e]) for e in case["idx"]]
         np.testing.assert_allclose(r["w"][0], np.array(s) / sum(s), rtol=1e-12)
+        # the group near-tie gap: last chosen group minus best unchosen group
+        assert abs(r["group_gap"][0] - case["group_gap"]) <= 1e-12, case["name"]
 
 
 def _brute_force_group_route(keys, n_group, topk_group, k):
@@ -388,7 +390,16 @@ def _brute_force_group_route(keys, n_group, topk_group, k):
         if total > best_total:
             best_set, best_total = subset, total
     elig = [e for e in range(E) if e // gs in best_set]
-    return sorted(elig, key=lambda e: (-keys[e], e))[:k]
+    return sorted(elig, key=lambda e: (-keys[e], e))[:k], _brute_force_group_gap(gscore, best_set)
+
+
+def _brute_force_group_gap(gscore, chosen):
+    """Smallest chosen group score minus the largest unchosen one (inf when
+    every group is chosen): how far the group choice is from a tie."""
+    unchosen = [g for g in range(len(gscore)) if g not in chosen]
+    if not unchosen:
+        return math.inf
+    return min(gscore[g] for g in chosen) - max(gscore[g] for g in unchosen)
 
 
 @pytest.mark.parametrize("E,n_group,topk_group,k", [(8, 4, 2, 3), (12, 3, 1, 2), (16, 4, 3, 5), (16, 8, 2, 4)])
@@ -401,7 +412,9 @@ def test_group_limited_matches_brute_force(E, n_group, topk_group, k):
     r = oracle.route(x, wg, bias, k, "sigmoid", n_group=n_group, topk_group=topk_group)
     keys = 1.0 / (1.0 + np.exp(-(x @ wg.T))) + bias
     for t in range(T):
-        assert r["idx"][t].tolist() == _brute_force_group_route(keys[t].tolist(), n_group, topk_group, k)
+        idx, gap = _brute_force_group_route(keys[t].tolist(), n_group, topk_group, k)
+        assert r["idx"][t].tolist() == idx
+        assert abs(r["group_gap"][t] - gap) <= 1e-12, (t, r["group_gap"][t], gap)
 
 
 def test_group_limited_all_groups_is_plain_topk():
