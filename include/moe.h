@@ -15,9 +15,12 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * - All tensor pointers are DEVICE pointers owned by the caller; the library
- *   never allocates, frees or synchronises, and keeps no state between calls
- *   apart from a thread-local error string.  Arrays are dense row-major.
+ * - All tensor pointers are DEVICE pointers owned by the caller; the layer's
+ *   calls never allocate device memory, free it or synchronise.  State kept
+ *   between calls: a thread-local error string; per host thread and device,
+ *   two side streams with their events and a capture stream, made on first
+ *   use; per (kernel, device), whether its LDS limit was raised; and the
+ *   measurement state of moe_profile_start/stop.  Arrays are dense row-major.
  * - Work is enqueued on `hip_stream` (a hipStream_t; NULL = default stream)
  *   and the call returns; faults inside kernels surface at the caller's next
  *   synchronisation.  No call reads device memory on the host.
@@ -103,8 +106,17 @@ const char* moe_status_str(int status);
 /* Detail of the last error returned on the calling thread ("" if none). */
 const char* moe_last_error(void);
 
-/* Bytes of device workspace that every call below needs for this layer
- * (an upper bound independent of the routing).  Returns a moe_status. */
+/* Bytes of device workspace that every call below needs for this layer: an
+ * upper bound independent of the routing, so that one allocation serves
+ * every batch of this shape (the graph-per-batch-size rule of Perplexity,
+ * "Lower latency and higher throughput with multi-node DeepSeek
+ * deployment", section "Quantization", MoE-router paragraph).  Returns 0
+ * when cfg is invalid (moe_last_error() says why); a valid layer always
+ * needs more than 0 bytes. */
+size_t moe_workspace_bytes(const moe_cfg* cfg);
+
+/* The same bound through an out-parameter, returning a moe_status (the form
+ * every other entry point uses). */
 int moe_workspace_size(const moe_cfg* cfg, size_t* bytes);
 
 /* Router (steps: gate GEMM, scoring, selection bias, top-k, weights).
@@ -119,12 +131,21 @@ int moe_route(const moe_cfg* cfg, const void* x, const void* w_gate, const float
               int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* hip_stream);
 
 /* Dispatch: per-expert aggregation of the routing (Perplexity, "MoE router").
- *   topk_idx    [T, k] int32 in, every value in [0, E)
+ *   topk_idx    [T, k] int32 in: each token's k experts, which must be
+ *               distinct (a token goes to k *different* experts, section
+ *               "Expert parallelism") and in [0, E).  An id outside [0, E)
+ *               is skipped: it is counted nowhere, its pair gets
+ *               pair_slot = -1 and moe_combine adds nothing for it.  With
+ *               repeated ids a group can exceed T rows; moe_expert_ffn
+ *               then leaves some y_sorted rows unwritten (no access goes
+ *               out of bounds, but the output is unspecified).
  *   counts      [E] int32 out: pairs routed to each expert
- *   offsets     [E+1] int32 out: exclusive running sum, offsets[E] = T*k
+ *   offsets     [E+1] int32 out: exclusive running sum, offsets[E] = number
+ *               of pairs with a valid id (T*k when all are valid)
  *   sorted_pair [T*k] int32 out: for each expert, its pair ids in ascending
  *               order, at positions offsets[e] .. offsets[e+1]-1
- *   pair_slot   [T*k] int32 out: inverse permutation (sorted_pair[pair_slot[p]] = p)
+ *   pair_slot   [T*k] int32 out: inverse permutation (sorted_pair[pair_slot[p]] = p),
+ *               -1 for a skipped pair
  * Bitwise deterministic. */
 int moe_dispatch(const moe_cfg* cfg, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
                  int32_t* sorted_pair, int32_t* pair_slot, void* ws, size_t ws_bytes,
@@ -152,14 +173,25 @@ int moe_expert_ffn(const moe_cfg* cfg, const void* x, const int32_t* offsets,
                    const int32_t* sorted_pair, const moe_weights* w, void* y_sorted,
                    void* y_shared, void* ws, size_t ws_bytes, void* hip_stream);
 
-/* Combine: y[t] = y_shared[t] + sum_j topk_w[t,j] * y_sorted[pair_slot[t*k+j]],
- * accumulated in fp32 in the order shared, j = 0..k-1 (deterministic).
+/* Combine (Perplexity, "Lower latency and higher throughput with multi-node
+ * DeepSeek deployment", section "Expert parallelism": the outputs of a
+ * token's k routed experts are summed with weights, and the shared expert's
+ * output, which every token also goes through, is added):
+ *   y[t] = y_shared[t] + sum_j topk_w[t,j] * y_sorted[pair_slot[t*k+j]],
+ * accumulated in fp32 in the order shared, j = 0..k-1 (deterministic);
+ * pairs with pair_slot < 0 (skipped by moe_dispatch) add nothing.
  *   y_sorted [T*k, H] and y_shared [T, H] (may be NULL: treated as 0) in
  *   act_dtype; y [T, H] act_dtype out. */
 int moe_combine(const moe_cfg* cfg, const void* y_sorted, const void* y_shared,
                 const int32_t* pair_slot, const float* topk_w, void* y, void* hip_stream);
 
-/* The whole layer: route -> dispatch -> expert FFN -> combine, on one stream.
+/* The whole layer (Perplexity, "Lower latency and higher throughput with
+ * multi-node DeepSeek deployment", section "Expert parallelism": k weighted
+ * routed experts plus the shared expert per token; the router's steps are
+ * those of the vLLM DeepSeek-V4.1-Flash article, section "Kernels", item
+ * "Mega-Gate"): route -> dispatch -> expert FFN -> combine, enqueued on
+ * hip_stream (the shared expert and, when both FFN regimes occur, the tiled
+ * groups may run on library side streams forked from and joined back to it).
  *   y [T, H] act_dtype out.  topk_idx_out [T,k], topk_w_out [T,k] and
  *   counts_out [E] are optional copies of the routing (NULL to skip). */
 int moe_forward(const moe_cfg* cfg, const void* x, const void* w_gate, const float* sel_bias,

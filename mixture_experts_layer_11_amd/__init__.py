@@ -29,6 +29,7 @@ from .binding import (  # noqa: F401
     moe_quantize_fp8,
     moe_route,
     moe_routing_stats,
+    moe_workspace_bytes,
     status_str,
     workspace_size,
 )

@@ -20,7 +20,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = range(2)
 
-EXPORTS = ("moe_status_str", "moe_last_error", "moe_workspace_size", "moe_route", "moe_dispatch",
+EXPORTS = ("moe_status_str", "moe_last_error", "moe_workspace_bytes", "moe_workspace_size", "moe_route", "moe_dispatch",
            "moe_quantize_fp8", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_graph_capture",
            "moe_graph_launch", "moe_graph_destroy", "moe_routing_stats", "moe_profile_start", "moe_profile_stop")
 
@@ -71,6 +71,8 @@ def load_library(path: str = LIB_PATH):
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_last_error.restype = ctypes.c_char_p
     lib.moe_last_error.argtypes = []
+    lib.moe_workspace_bytes.restype = SZ
+    lib.moe_workspace_bytes.argtypes = [cfgp]
     lib.moe_workspace_size.argtypes = [cfgp, ctypes.POINTER(SZ)]
     lib.moe_route.argtypes = [cfgp, P, P, P, P, P, P, SZ, P]
     lib.moe_dispatch.argtypes = [cfgp, P, P, P, P, P, P, SZ, P]
@@ -84,7 +86,7 @@ def load_library(path: str = LIB_PATH):
     lib.moe_graph_destroy.argtypes = [P]
     lib.moe_profile_start.argtypes = [ctypes.c_char_p]
     lib.moe_profile_stop.argtypes = [P, I32, ctypes.POINTER(I32)]
-    for name in EXPORTS[2:]:
+    for name in EXPORTS[3:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -128,6 +130,11 @@ def workspace_size(cfg: MoeCfg) -> int:
     n = ctypes.c_size_t(0)
     _check(load_library().moe_workspace_size(ctypes.byref(cfg), ctypes.byref(n)))
     return n.value
+
+
+def moe_workspace_bytes(cfg: MoeCfg) -> int:
+    """Workspace bytes for this layer (0 when cfg is invalid; see last_error())."""
+    return int(load_library().moe_workspace_bytes(ctypes.byref(cfg)))
 
 
 def alloc_workspace(cfg: MoeCfg, device="cuda") -> torch.Tensor:

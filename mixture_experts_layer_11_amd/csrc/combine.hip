@@ -3,8 +3,9 @@
 // multi-node DeepSeek deployment", section "Expert parallelism").
 //
 // y[t] = y_shared[t] + sum_j w[t,j] * y_sorted[pair_slot[t*k + j]], fp32
-// accumulation in the fixed order shared, j = 0..k-1.  Inputs and output are
-// in the activation dtype; every row is read once (nontemporal loads).
+// accumulation in the fixed order shared, j = 0..k-1; a pair whose slot is
+// negative (dispatch skipped its expert id) adds nothing.  Inputs and output
+// are in the activation dtype; every row is read once (nontemporal loads).
 
 #include "moe_common.h"
 #include "moe_launch.h"
@@ -62,13 +63,21 @@ __global__ __launch_bounds__(1024) void combine_kernel(const void* __restrict__ 
     if constexpr (KT > 0) {
       float v[KT][8];
 #pragma unroll
-      for (int j = 0; j < KT; ++j) load8<OUT_DT>(y_sorted, (size_t)slot[j] * H + c, v[j]);
+      for (int j = 0; j < KT; ++j) {
+        if (slot[j] >= 0) {
+          load8<OUT_DT>(y_sorted, (size_t)slot[j] * H + c, v[j]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[j][i] = 0.f;
+        }
+      }
 #pragma unroll
       for (int j = 0; j < KT; ++j)
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = fmaf(wt[j], v[j][i], acc[i]);
     } else {
       for (int j = 0; j < k; ++j) {
+        if (slot[j] < 0) continue;     // a pair that dispatch skipped (id outside [0, E))
         float v[8];
         load8<OUT_DT>(y_sorted, (size_t)slot[j] * H + c, v);
 #pragma unroll

@@ -12,7 +12,8 @@
 //               64-step register scan of the wave's expert ids, so the
 //               placement is stable (ascending pair id inside each expert).
 // Integer atomics only feed the histogram, so the result is deterministic.
-// Expert ids outside [0, E) are skipped (never used as an address).
+// Expert ids outside [0, E) are skipped: counted nowhere, never used as an
+// address, and their pairs get pair_slot = -1.
 
 #include "moe_common.h"
 #include "moe_launch.h"
@@ -130,6 +131,8 @@ __global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* __r
       const int slot = run[e] + rank;
       sorted_pair[slot] = p;
       pair_slot[p] = slot;
+    } else if (p < P) {
+      pair_slot[p] = -1;                 // skipped id: the combine adds nothing for it
     }
     __syncthreads();
     if (e >= 0 && rank == same - 1) run[e] += same;
@@ -200,6 +203,8 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __r
       for (int w = 0; w < wave; ++w) slot += wcnt[w][e];
       sorted_pair[slot] = p;
       pair_slot[p] = slot;
+    } else if (p < P) {
+      pair_slot[p] = -1;                 // skipped id: the combine adds nothing for it
     }
     __syncthreads();
     if (tid < E) {

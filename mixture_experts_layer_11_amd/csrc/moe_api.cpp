@@ -92,6 +92,7 @@ struct Layout {
 
 Layout layout(const moe_cfg& c) {
   Layout L{};
+  if (c.T == 0) return L;   // no tokens: no call touches the workspace
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -193,6 +194,13 @@ const char* moe_status_str(int status) {
 }
 
 const char* moe_last_error(void) { return g_err; }
+
+size_t moe_workspace_bytes(const moe_cfg* cfg) {
+  if (check_cfg(cfg)) return 0;
+  ok();
+  const size_t total = layout(*cfg).total;
+  return total > 0 ? total : 256;   // never 0 for a valid layer (0 means invalid)
+}
 
 int moe_workspace_size(const moe_cfg* cfg, size_t* bytes) {
   int s = check_cfg(cfg);

@@ -57,6 +57,7 @@ def _ws_status(cfg):
 def test_workspace_size_for_each_workload(name):
     st, n = _ws_status(B.cfg_from(CONFIGS[name]))
     assert st == B.MOE_OK and n > 0
+    assert moe.moe_workspace_bytes(B.cfg_from(CONFIGS[name])) == n
     bigger = B.cfg_from(CONFIGS[name].with_(T=CONFIGS[name].T * 2))
     assert _ws_status(bigger)[1] > n
 
@@ -87,6 +88,15 @@ def test_invalid_configs_rejected(kw, code):
     st, _ = _ws_status(_cfg(**kw))
     assert st == code, moe.last_error()
     assert moe.last_error()
+    assert moe.moe_workspace_bytes(_cfg(**kw)) == 0
+    assert moe.last_error()
+
+
+def test_workspace_bytes_null_cfg_and_tiny_layer():
+    lib = moe.load_library()
+    assert lib.moe_workspace_bytes(None) == 0 and "cfg" in moe.last_error()
+    n = moe.moe_workspace_bytes(_cfg(T=0))          # valid, nothing to hold: still nonzero
+    assert n > 0 and moe.last_error() == ""
 
 
 def test_argument_errors_before_any_launch():

@@ -285,6 +285,47 @@ def test_dispatch_maximum_pairs():
         np.testing.assert_array_equal(to_np(g), r, err_msg=name)
 
 
+@pytest.mark.parametrize("T,E,k", [(40, 16, 4), (1200, 32, 8)])
+def test_dispatch_and_combine_skip_out_of_range_ids(T, E, k):
+    """Ids outside [0, E) are the library's documented invalid input: the
+    dispatch counts them nowhere and gives their pairs pair_slot = -1, and
+    the combine adds nothing for them.  Both the one-workgroup dispatch
+    (160 pairs) and the three-kernel one (9600 pairs) are covered; the
+    expected values are the definitions restricted to the valid pairs."""
+    rng = np.random.default_rng(T + E)
+    idx = _distinct_topk(rng, T, E, k).astype(np.int64)
+    bad = rng.random(idx.shape) < 0.1
+    idx[bad] = rng.choice([-1, -7, E, E + 3], size=int(bad.sum()))
+    cfg = moe.make_cfg(T, 128, E, k, 64, 64)
+    counts, offsets, sorted_pair, pair_slot = moe.moe_dispatch(cfg, torch.from_numpy(idx.astype(np.int32)).to(DEV))
+    torch.cuda.synchronize()
+    flat = idx.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    ref_counts = np.bincount(flat[valid], minlength=E)
+    ref_off = np.concatenate([[0], np.cumsum(ref_counts)])
+    ref_sorted = np.nonzero(valid)[0][np.argsort(flat[valid], kind="stable")]
+    ref_slot = np.full(flat.shape[0], -1)
+    ref_slot[ref_sorted] = np.arange(len(ref_sorted))
+    np.testing.assert_array_equal(to_np(counts), ref_counts)
+    np.testing.assert_array_equal(to_np(offsets), ref_off)
+    np.testing.assert_array_equal(to_np(sorted_pair)[:len(ref_sorted)], ref_sorted)
+    np.testing.assert_array_equal(to_np(pair_slot), ref_slot)
+    # combine: rows of y_sorted in bf16, weights in fp32; skipped pairs add nothing
+    H = 128
+    ys = torch.from_numpy(rng.standard_normal((T * k, H))).to(torch.bfloat16)
+    ysh = torch.from_numpy(rng.standard_normal((T, H))).to(torch.bfloat16)
+    w = torch.from_numpy(rng.random((T, k)).astype(np.float32))
+    y = moe.moe_combine(cfg, ys.to(DEV), ysh.to(DEV), pair_slot, w.to(DEV))
+    torch.cuda.synchronize()
+    ys64, w64 = oracle.to_f64(ys), w.double().numpy()
+    expect = oracle.to_f64(ysh).copy()
+    for t in range(T):
+        for j in range(k):
+            if valid[t * k + j]:
+                expect[t] += w64[t, j] * ys64[ref_slot[t * k + j]]
+    assert_outputs_close(y, expect, "bf16", "combine with skipped pairs")
+
+
 @pytest.mark.parametrize("T", [4096, 65536])
 def test_dispatch_all_pairs_to_one_expert(T):
     E, k = 8, 1
