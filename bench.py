@@ -1,10 +1,13 @@
 """Benchmark of the MoE-layer forward on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode16]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill8192_ep8]
 
 One step = one moe_forward call (router, dispatch, expert FFNs with the
 shared expert, combine) over one batch of seeded synthetic input already
-resident in HBM.  Prints ONE JSON line:
+resident in HBM.  The default workload is the largest single-GPU one: one
+expert-parallel rank's share of an 8192-token prefill (32 local experts,
+Zipf-skewed routing, bf16), where the grouped GEMM is MFMA-bound.  Prints
+ONE JSON line:
 
 * value      whole-layer tokens/s = T * K / (wall time of the K timed steps)
 * roofline   for the kernel with the largest share of GPU time: algorithmic
@@ -24,6 +27,11 @@ resident in HBM.  Prints ONE JSON line:
 * cpu_baseline  the fp64 oracle timed on the host on a bounded sample of the
              same workload (first n tokens, single thread), as tokens/s,
              with the host's CPU model, logical CPUs and RAM.
+* workloads  the other six workloads measured in the same run (fewer steps,
+             no graph, no CPU baseline): tokens/s, the layer's fraction of
+             its roofline and the dominant kernel's.  Where the streaming and
+             tiled GEMMs share the device, the layer fraction is the figure
+             that means something; the per-kernel one is shown beside it.
 
 Only one GPU is used; --gpus above 1 exits with a message.
 """
@@ -41,6 +49,9 @@ METRIC = "MoE-layer tokens/s at 1 GPU + achieved HBM GB/s (decode) / MFMA % (pre
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 SKINNY_ROWS = 32          # groups with at most this many rows take the streaming (skinny) kernels
+HALVES_ROWS = 16          # up to this many tokens every group, the shared expert too, runs in 8-row halves
+DEFAULT_WORKLOAD = "prefill8192_ep8"
+OTHER_WORKLOADS = ("decode16", "decode256", "clustered2048_fp8", "decode16_fp8", "decode256_fp8", "tiny_f32")
 
 
 def kernel_models(cfg, counts):
@@ -82,7 +93,12 @@ def kernel_models(cfg, counts):
         else:
             items += tiled(mg, "")
     if cfg.I_shared:
-        items += [(T, "shared_skinny")] if T <= SKINNY_ROWS else tiled(T, "shared_")
+        # T <= 16: the shared expert runs as two 8-row halves inside the routed
+        # streaming launch; up to 32 tokens it has a streaming launch of its own
+        if T <= HALVES_ROWS:
+            items.append((T, "skinny"))
+        else:
+            items += [(T, "shared_skinny")] if T <= SKINNY_ROWS else tiled(T, "shared_")
     for mg, reg in items:
         if mg == 0:
             continue
@@ -118,7 +134,7 @@ def traffic_for(kernel, workload):
         d = json.load(open(p))
     except (OSError, ValueError):
         return None
-    from mixture_experts_layer_11_amd.profiling import kernel_source_hash
+    from moe_measure.profiling import kernel_source_hash
     if d.get("source_hash") != kernel_source_hash(kernel):
         return None
     return d.get("bytes_per_launch")
@@ -172,34 +188,19 @@ def cpu_baseline(inp_gpu, n_tokens, min_s=10.0, max_passes=4):
     return dt, passes
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode16")
-    ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the oracle's timed sample")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--quick", action="store_true", help="no CPU baseline (tuning sweeps)")
-    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay measurement (profiled runs)")
-    args = ap.parse_args(argv)
+def shares_device(cfg):
+    """Whether the streaming and tiled GEMMs of a step run at the same time:
+    the library forks the tiled launches onto a side stream when the mean
+    rows per routed expert lie in 17..1023 and the layer has more than 32
+    tokens; per-kernel spans then include the sharing."""
+    mean_rows = cfg.T * cfg.k // cfg.E
+    return cfg.T > SKINNY_ROWS and SKINNY_ROWS // 2 < mean_rows < 1024
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
-              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr, flush=True)
-        return 2
 
-    import torch
+def measure(moe, torch, cfg, steps, warmup, detail=True, graph=True):
+    """Time `steps` whole-layer steps of one workload; returns a dict."""
+    from moe_inputs import make_inputs
 
-    import mixture_experts_layer_11_amd as moe
-    from moe_inputs import get_config, make_inputs
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 1
-    moe.load_library()
-    cfg = get_config(args.workload)
     tg = time.perf_counter()
     inp = make_inputs(cfg, "cuda")
     torch.cuda.synchronize()
@@ -211,12 +212,12 @@ def main(argv=None):
                     device="cuda")
     step = lambda: moe.moe_forward(mc, inp.x, inp.wg, inp.bias, w, ws=ws, y=y)   # noqa: E731
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
     # untimed pass: routing of this batch (for the byte model) and the per-kernel
-    # breakdown of one instrumented step (every kernel bracketed by events)
+    # breakdown of instrumented steps (every kernel bracketed by events)
     _, idx, _, counts = moe.moe_forward(mc, inp.x, inp.wg, inp.bias, w, ws=ws, return_routing=True)
     torch.cuda.synchronize()
     counts_h = counts.cpu().tolist()
@@ -229,16 +230,17 @@ def main(argv=None):
     # algorithmic bytes at the HBM peak or its FLOPs at the MFMA peak,
     # whichever is longer, which the routing alone fixes.  Event spans would
     # serve where kernels run one after another, but the streaming and tiled
-    # GEMMs that share the device (a mean of 17..1023 rows per expert) swap
-    # places from run to run.  Spans break ties and cover unmodelled kernels.
+    # GEMMs that share the device swap places from run to run.  Spans break
+    # ties and cover unmodelled kernels.
     models, layer = kernel_models(cfg, counts_h)
     wdt = "fp8" if cfg.w_dtype == "fp8" else cfg.act_dtype
+    peak = MFMA_PEAK_TFLOPS[wdt]
 
     def roof_s(n):
         mm = models.get(n)
         if not mm:
             return -1.0
-        return max(mm["bytes"] / (HBM_PEAK_GBPS * 1e9), mm["flops"] / (MFMA_PEAK_TFLOPS[wdt] * 1e12))
+        return max(mm["bytes"] / (HBM_PEAK_GBPS * 1e9), mm["flops"] / (peak * 1e12))
 
     dom = max(breakdown, key=lambda n: (roof_s(n), breakdown[n][1]))
 
@@ -249,7 +251,7 @@ def main(argv=None):
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     ev1.record()
     torch.cuda.synchronize()
@@ -257,17 +259,16 @@ def main(argv=None):
     prof = moe.moe_profile_stop()
     gpu_ms = ev0.elapsed_time(ev1)
 
-    ms_per_step = wall_ms / args.steps
-    tokens_per_s = cfg.T * args.steps / (wall_ms / 1e3)
+    ms_per_step = wall_ms / steps
+    tokens_per_s = cfg.T * steps / (wall_ms / 1e3)
 
     launches, tot_ms = prof[dom]
     avg_ms = tot_ms / max(launches, 1)
+    ridge = peak * 1e12 / (HBM_PEAK_GBPS * 1e9)
     if dom in models:
         mm = models[dom]
         # the kernel's own roofline: HBM-bound below the ridge point
         # (peak FLOP/s / peak bytes/s), MFMA-bound above it
-        peak = MFMA_PEAK_TFLOPS[wdt]
-        ridge = peak * 1e12 / (HBM_PEAK_GBPS * 1e9)
         tflops = mm["flops"] / (avg_ms * 1e-3) / 1e12
         if mm["flops"] < ridge * mm["bytes"]:
             achieved = mm["bytes"] / (avg_ms * 1e-3) / 1e9
@@ -285,90 +286,160 @@ def main(argv=None):
     roof["kernel_avg_us"] = round(avg_ms * 1e3, 2)
     roof["algorithmic_per_launch"] = models.get(dom, {})
 
-    # per-step spread, in a pass of its own after the timed region: each step
-    # bracketed by events on the caller's stream (the side stream joins it)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a0, a1 in evs:
-        a0.record()
-        step()
-        a1.record()
-    torch.cuda.synchronize()
-    per_step = sorted(a0.elapsed_time(a1) for a0, a1 in evs)
-    pct = lambda q: per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]   # noqa: E731
-    step_spread = {"median_ms": round(pct(0.5), 4), "p10_ms": round(pct(0.1), 4), "p90_ms": round(pct(0.9), 4)}
-
     layer_gbps = layer["bytes"] / (ms_per_step * 1e-3) / 1e9
     layer_tflops = layer["flops"] / (ms_per_step * 1e-3) / 1e12
-
-    # beside the timed steps: the same step captured once as a HIP graph
-    # (moe_graph_capture) and replayed K times, which removes the host launch
-    # cost of the ~15-20 kernels per step
-    graph_line = None
-    if not args.no_graph:
-        graph = moe.MoEGraph(mc, inp.x, inp.wg, inp.bias, w, y, ws)
-        for _ in range(args.warmup):
-            graph.launch()
+    layer_bound = "mfma" if layer["flops"] >= ridge * layer["bytes"] else "hbm"
+    layer_frac = layer_tflops / peak if layer_bound == "mfma" else layer_gbps / HBM_PEAK_GBPS
+    out = {
+        "workload": cfg.name, "T": cfg.T, "dtype": wdt, "tokens_per_s": round(tokens_per_s, 1),
+        "ms_per_step": round(ms_per_step, 4), "steps": steps, "warmup": warmup,
+        "roofline": roof,
+        "layer": {"algorithmic_bytes": layer["bytes"], "flops": layer["flops"], "GBps": round(layer_gbps, 1),
+                  "hbm_frac": round(layer_gbps / HBM_PEAK_GBPS, 4), "TFLOPs": round(layer_tflops, 2),
+                  "mfma_frac": round(layer_tflops / peak, 4), "bound": layer_bound, "frac": round(layer_frac, 4),
+                  "gpu_event_ms_per_step": round(gpu_ms / steps, 4)},
+        "gemms_share_device": shares_device(cfg),
+        "touched_experts": layer["touched"],
+        "input_gen_s": round(gen_s, 2),
+    }
+    if detail:
+        out["kernels"] = {n: kernel_line(n, v, models) for n, v in sorted(breakdown.items())}
+        # per-step spread, in a pass of its own after the timed region: each step
+        # bracketed by events on the caller's stream (the side stream joins it)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a0, a1 in evs:
+            a0.record()
+            step()
+            a1.record()
         torch.cuda.synchronize()
-        g0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.launch()
+        per_step = sorted(a0.elapsed_time(a1) for a0, a1 in evs)
+        pct = lambda q: per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]   # noqa: E731
+        out["step_spread"] = {"median_ms": round(pct(0.5), 4), "p10_ms": round(pct(0.1), 4),
+                              "p90_ms": round(pct(0.9), 4)}
+        # beside the timed steps: the same step captured once as a HIP graph
+        # (moe_graph_capture) and replayed K times
+        out["graph"] = None
+        if graph:
+            g = moe.MoEGraph(mc, inp.x, inp.wg, inp.bias, w, y, ws)
+            for _ in range(warmup):
+                g.launch()
+            torch.cuda.synchronize()
+            g0 = time.perf_counter()
+            for _ in range(steps):
+                g.launch()
+            torch.cuda.synchronize()
+            graph_ms = (time.perf_counter() - g0) * 1e3 / steps
+            g.close()
+            out["graph"] = {"ms_per_step": round(graph_ms, 4), "tokens_per_s": round(cfg.T / (graph_ms * 1e-3), 1),
+                            "eager_minus_graph_us": round((ms_per_step - graph_ms) * 1e3, 2)}
+        # beside the layer, outside the timed steps: routing statistics of this
+        # batch (loads over 8 expert-parallel ranks when E allows, skews, affinity)
+        n_ranks = 8 if cfg.E % 8 == 0 else 1
+        moe.moe_routing_stats(mc, idx, n_ranks)
         torch.cuda.synchronize()
-        graph_ms = (time.perf_counter() - g0) * 1e3 / args.steps
-        graph.close()
-        graph_line = {"ms_per_step": round(graph_ms, 4), "tokens_per_s": round(cfg.T / (graph_ms * 1e-3), 1),
-                      "eager_minus_graph_us": round((ms_per_step - graph_ms) * 1e3, 2)}
+        moe.moe_profile_start()
+        for _ in range(5):
+            _, _, skew, _ = moe.moe_routing_stats(mc, idx, n_ranks)
+        torch.cuda.synchronize()
+        sp = moe.moe_profile_stop()
+        stat_us = {n: round(v[1] / max(v[0], 1) * 1e3, 2) for n, v in sorted(sp.items())}
+        skew_h = skew.cpu().tolist()
+        out["routing_stats"] = {"n_ranks": n_ranks, "rho_rank": round(skew_h[0], 4),
+                                "rho_expert": round(skew_h[1], 4), "us_per_call": round(sum(stat_us.values()), 2),
+                                "kernels_us": stat_us}
+        out["inputs"] = inp
+    return out
 
-    # beside the layer, outside the timed steps: routing statistics of this
-    # batch (loads over 8 expert-parallel ranks when E allows, skews, affinity)
-    n_ranks = 8 if cfg.E % 8 == 0 else 1
-    moe.moe_routing_stats(mc, idx, n_ranks)
-    torch.cuda.synchronize()
-    moe.moe_profile_start()
-    for _ in range(5):
-        _, _, skew, _ = moe.moe_routing_stats(mc, idx, n_ranks)
-    torch.cuda.synchronize()
-    sp = moe.moe_profile_stop()
-    stat_us = {n: round(v[1] / max(v[0], 1) * 1e3, 2) for n, v in sorted(sp.items())}
-    skew_h = skew.cpu().tolist()
-    routing_stats = {"n_ranks": n_ranks, "rho_rank": round(skew_h[0], 4), "rho_expert": round(skew_h[1], 4),
-                     "us_per_call": round(sum(stat_us.values()), 2), "kernels_us": stat_us}
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true", help="measure only --workload")
+    ap.add_argument("--other-steps", type=int, default=10, help="timed steps per other workload")
+    ap.add_argument("--quick", action="store_true", help="--workload only, no CPU baseline (tuning sweeps)")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay measurement (profiled runs)")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr, flush=True)
+        return 2
+
+    import torch
+
+    import mixture_experts_layer_11_amd as moe
+    from moe_inputs import get_config
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    moe.load_library()
+    cfg = get_config(args.workload)
+    print(f"[bench] {cfg.name}: {args.warmup} warmup + {args.steps} timed steps", file=sys.stderr, flush=True)
+    r = measure(moe, torch, cfg, args.steps, args.warmup, detail=True, graph=not args.no_graph)
+    inp = r.pop("inputs")
 
     cpu = None
     if not (args.no_cpu_baseline or args.quick):
         n = min(args.cpu_tokens, cfg.T)
+        print(f"[bench] cpu baseline: fp64 oracle on {n} tokens", file=sys.stderr, flush=True)
         dt, passes = cpu_baseline(inp, n)
         cpu = {"value": round(n * passes / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
                "host": host_info(),
                "sample": f"first {n} of {cfg.T} tokens of {cfg.name}, {passes} passes: fp64 numpy oracle, token "
                          f"by token (routing, fp64 upcast of each touched expert, SwiGLU, weighted sum), 1 thread, "
                          f"inputs already in host memory; {dt:.2f} s"}
+    del inp
+    torch.cuda.empty_cache()
+
+    others = None
+    if not (args.no_others or args.quick):
+        others = {}
+        for name in OTHER_WORKLOADS:
+            if name == cfg.name:
+                continue
+            print(f"[bench] {name}: 3 warmup + {args.other_steps} timed steps", file=sys.stderr, flush=True)
+            o = measure(moe, torch, get_config(name), args.other_steps, 3, detail=False)
+            rf = o["roofline"]
+            others[name] = {"tokens_per_s": o["tokens_per_s"], "ms_per_step": o["ms_per_step"],
+                            "layer_bound": o["layer"]["bound"], "layer_frac": o["layer"]["frac"],
+                            "layer_GBps": o["layer"]["GBps"], "layer_TFLOPs": o["layer"]["TFLOPs"],
+                            "gemms_share_device": o["gemms_share_device"],
+                            "dominant_kernel": rf["kernel"], "kernel_bound": rf["bound"],
+                            "kernel_frac": rf["frac"], "kernel_avg_us": rf["kernel_avg_us"]}
+            torch.cuda.empty_cache()
 
     out = {
         "metric": METRIC,
-        "value": round(tokens_per_s, 1),
+        "value": r["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wdt,
+        "dtype": r["dtype"],
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
-                   "I_shared": cfg.I_shared, "score": cfg.score, "weights": cfg.w_dtype,
-                   "touched_experts": layer["touched"], "parallelism": "none (1 GPU)"},
-        "roofline": roof,
-        "layer": {"algorithmic_bytes": layer["bytes"], "flops": layer["flops"], "GBps": round(layer_gbps, 1),
-                  "hbm_frac": round(layer_gbps / HBM_PEAK_GBPS, 4), "TFLOPs": round(layer_tflops, 2),
-                  "gpu_event_ms_per_step": round(gpu_ms / args.steps, 4)},
-        "kernels": {n: kernel_line(n, v, models) for n, v in sorted(breakdown.items())},
-        "step_spread": step_spread,
-        "input_gen_s": round(gen_s, 2),
-        "graph": graph_line,
-        "routing_stats": routing_stats,
+                   "I_shared": cfg.I_shared, "score": cfg.score, "weights": cfg.w_dtype, "routing": cfg.routing,
+                   "touched_experts": r["touched_experts"], "parallelism": "none (1 GPU)"},
+        "roofline": r["roofline"],
+        "layer": r["layer"],
+        "kernels": r["kernels"],
+        "step_spread": r["step_spread"],
+        "input_gen_s": r["input_gen_s"],
+        "graph": r["graph"],
+        "routing_stats": r["routing_stats"],
         "cpu_baseline": cpu,
+        "workloads": others,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -1,6 +1,6 @@
 """Plain device copy of a known size, for calibrating HBM traffic counters.
 
-python -m mixture_experts_layer_11_amd.hbm_copy_probe [--mib 1024] [--reps 3]
+python -m moe_measure.hbm_copy_probe [--mib 1024] [--reps 3]
 
 Copies a --mib MiB buffer into another with torch's copy kernel --reps
 times.  Under `rocprofv3 --pmc FETCH_SIZE` (then WRITE_SIZE) each copy

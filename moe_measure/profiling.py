@@ -9,7 +9,7 @@ stored counter reading is only used while the kernel is unchanged.
 CLI (writes profiles/<kernel>_<workload>.md and
 profiles/traffic_<kernel>_<workload>.json from rocprofv3 CSV output):
 
-  python -m mixture_experts_layer_11_amd.profiling --workload decode16 \\
+  python -m moe_measure.profiling --workload decode16 \\
       --kernel ffn_gemm1_skinny --stats RUN_kernel_stats.csv \\
       --fetch FETCH_counter_collection.csv --write WRITE_counter_collection.csv \\
       --copy-fetch COPYF.csv --copy-write COPYW.csv --copy-bytes 1073741824 \\
@@ -23,8 +23,8 @@ import json
 import os
 import statistics
 
-PKG = os.path.dirname(os.path.abspath(__file__))
-ROOT = os.path.dirname(PKG)
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "mixture_experts_layer_11_amd", "csrc")
 
 KERNEL_SOURCES = {
     "ffn_gemm1_skinny": "ffn_skinny.hip", "ffn_gemm2_skinny": "ffn_skinny.hip",
@@ -34,20 +34,31 @@ KERNEL_SOURCES = {
     "route_gate_fused": "route.hip", "route_gate_split": "route.hip", "route_gate_tiled": "route.hip",
     "route_reduce_select": "route.hip",
     "dispatch_count": "dispatch.hip", "dispatch_scan": "dispatch.hip", "dispatch_scatter": "dispatch.hip",
+    "dispatch_small": "dispatch.hip",
     "quant_fp8": "quant.hip", "combine": "combine.hip",
 }
 
 _DT = {"f32": 0, "bf16": 1, "fp8": 2}
 
 
+# Files that decide a kernel's launch geometry and what shares the device
+# with it, besides its own source: the expert FFN's launcher and work-list
+# builder (grids, tile lists, side streams), and the stream helpers.
+LAUNCH_SOURCES = {"ffn": ("ffn.hip", "plan.h", "streams.cpp"), "route": (), "dispatch": ("plan.h",),
+                  "quant": (), "combine": (), "stats": ()}
+
+
 def kernel_source_hash(kernel: str) -> str:
-    """sha256 prefix of the kernel's source file plus the device headers it includes."""
+    """sha256 prefix of every source a stored counter reading depends on: the
+    kernel's own file, its launcher, and all device and launch headers."""
     h = hashlib.sha256()
-    csrc = os.path.join(PKG, "csrc")
     src = KERNEL_SOURCES.get(kernel, "")
-    for f in (src, "ffn.h" if src.startswith("ffn") else "", "moe_common.h"):
-        p = os.path.join(csrc, f)
-        if os.path.isfile(p):
+    launch = LAUNCH_SOURCES.get(src.split(".")[0].split("_")[0], ())
+    headers = sorted(f for f in os.listdir(CSRC) if f.endswith(".h"))
+    for f in [src, *launch, *headers]:
+        p = os.path.join(CSRC, f)
+        if f and os.path.isfile(p):
+            h.update(f.encode())
             h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
 
