@@ -315,13 +315,16 @@ def forward(inp, weights: Optional[OracleWeights] = None):
     return dict(route=r, dispatch=d, xa=xa, y_sorted=y_sorted, y_shared=y_shared, y=y)
 
 
-def forward_tokens(inp, tokens, weights: Optional[OracleWeights] = None):
+def forward_tokens(inp, tokens, weights: Optional[OracleWeights] = None, workers: int = 1):
     """The layer's output for the listed tokens only, token by token.
 
     Routing, activation quantisation and the expert FFNs act on each token on
     its own, so y[t] = sum_j w[t,j] FFN_{idx[t,j]}(x[t]) + FFN_shared(x[t])
     ([PPLX] "Expert parallelism") is computed without any dispatch.  Each
     touched expert's weights are converted once for all listed tokens.
+    With ``workers`` > 1 the touched experts are evaluated on that many
+    threads; their outputs are still added in ascending expert order, so the
+    result is the same bits either way.
     Returns (y [n,H], route dict for the listed tokens).
     """
     cfg = inp.cfg
@@ -332,10 +335,20 @@ def forward_tokens(inp, tokens, weights: Optional[OracleWeights] = None):
               n_group=cfg.n_group, topk_group=cfg.topk_group)
     xa = prepare_activations(x, weights.fp8, weights.block)
     y = np.zeros_like(xa)
-    for e in np.unique(r["idx"]):
+
+    def one_expert(e):
         rows, js = np.nonzero(r["idx"] == e)
         w1, w3, w2 = weights.expert(int(e))
-        ye = swiglu_ffn(xa[rows], w1, w3, w2, weights.fp8, weights.block)
+        return rows, js, swiglu_ffn(xa[rows], w1, w3, w2, weights.fp8, weights.block)
+
+    experts = [int(e) for e in np.unique(r["idx"])]
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(workers) as ex:
+            outs = list(ex.map(one_expert, experts))
+    else:
+        outs = map(one_expert, experts)
+    for rows, js, ye in outs:                      # ascending expert order
         y[rows] += r["w"][rows, js][:, None] * ye
     if weights.shared is not None:
         w1, w3, w2 = weights.shared()

@@ -5,9 +5,13 @@ oracle/ alone; when a stage is tested on its own, its upstream inputs come
 from the oracle (or from the seeded generators), never from the GPU.
 
 Sizes: small layers the oracle finishes in seconds but that still span
-several tiles and ragged tails of both expert-FFN regimes, plus the five
-named workloads at full size, where the oracle checks every token's routing
-and a sample of tokens' outputs one by one.
+several tiles and ragged tails of both expert-FFN regimes; three mid-size
+layers whose whole output is checked; and the named workloads at full size:
+every token's routing, every token's output for the decode workloads, and
+for the prefill share and the clustered fp8 layer the tokens at each
+expert's first and last slot and at the tile boundaries, plus whole groups of
+every row class and the whole shared-expert output through the expert-FFN
+stage on the oracle's dispatch.
 """
 
 import os
@@ -559,9 +563,11 @@ def test_all_tokens_to_one_expert():
     assert_outputs_close(y, ref["y"], "bf16", "y")
 
 
-# ------------------------------------------------------------------ full-size workloads (sampled outputs)
+# ------------------------------------------------------------------ full-size workloads
 
-FULL = ["decode16", "decode256", "prefill8192_ep8", "clustered2048_fp8", "decode16_fp8", "decode256_fp8"]
+# Threads the oracle may use over experts in the full-size checks (its
+# results are the same bits for any count).
+ORACLE_WORKERS = 8
 
 # Mid-size layers that take every path at once: the three-kernel dispatch
 # (more than 4096 pairs), the LDS-staged router, streaming and tiled groups
@@ -577,27 +583,139 @@ MID = {
 }
 
 
-@pytest.mark.parametrize("name", FULL + sorted(MID))
-def test_forward_full_size_sampled(name):
-    cfg = MID[name] if name in MID else get_config(name)
-    _log(f"[full {name}] drawing inputs on the GPU")
+def _full_forward(cfg):
     gin = make_inputs(cfg, DEV)
     mc = moe.cfg_from(cfg)
     y, idx, w, counts = moe.moe_forward(mc, gin.x, gin.wg, gin.bias, moe.Weights.from_inputs(gin),
                                         return_routing=True)
     torch.cuda.synchronize()
-    _log(f"[full {name}] GPU forward done; oracle routing of all {cfg.T} tokens")
+    _log(f"[full {cfg.name}] GPU forward done; oracle routing of all {cfg.T} tokens")
     r = oracle.route(oracle.to_f64(gin.x), oracle.to_f64(gin.wg), oracle.to_f64(gin.bias), cfg.k, cfg.score)
     near, mism = compare_routing(idx, w, r, cfg.k)
     if len(mism) == 0:
         np.testing.assert_array_equal(to_np(counts), np.bincount(r["idx"].ravel(), minlength=cfg.E))
-    rng = np.random.default_rng(0)
-    cand = np.setdiff1d(np.arange(cfg.T), mism)
-    toks = np.unique(np.concatenate([[cand[0], cand[-1]], rng.choice(cand, size=min(4, len(cand)), replace=False)]))
-    _log(f"[full {name}] oracle outputs of tokens {toks.tolist()}")
-    yo, _ = oracle.forward_tokens(gin, toks)
+    return gin, y, r, counts, near, mism
+
+
+@pytest.mark.parametrize("name", ["decode16", "decode256", "decode16_fp8", "decode256_fp8"])
+def test_forward_full_size_every_token(name):
+    """The decode workloads at full size: every token's output, element by
+    element, against the oracle computed token by token (no dispatch)."""
+    cfg = get_config(name)
+    _log(f"[full {name}] drawing inputs on the GPU")
+    gin, y, r, counts, near, mism = _full_forward(cfg)
+    toks = np.setdiff1d(np.arange(cfg.T), mism)
+    _log(f"[full {name}] oracle outputs of all {len(toks)} tokens")
+    yo, _ = oracle.forward_tokens(gin, toks, workers=ORACLE_WORKERS)
     err = assert_outputs_close(to_np(y)[toks], yo, tol_key(cfg), "y")
     touched = int((to_np(counts) > 0).sum())
     _log(f"[full {name}] near-ties={near} excluded={len(mism)} touched experts={touched} err={err}")
+    del gin
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", sorted(MID))
+def test_forward_mid_whole_layer(name):
+    """The mid-size layers: the whole output against oracle.forward."""
+    cfg = MID[name]
+    inp, gin = _small_inputs(cfg)
+    ref = oracle.forward(inp)
+    y, idx, w, counts = moe.moe_forward(moe.cfg_from(cfg), gin.x, gin.wg, gin.bias, moe.Weights.from_inputs(gin),
+                                        return_routing=True)
+    torch.cuda.synchronize()
+    near, mism = compare_routing(idx, w, ref["route"], cfg.k)
+    if len(mism) == 0:
+        np.testing.assert_array_equal(to_np(counts), ref["dispatch"]["counts"])
+    keep = np.setdiff1d(np.arange(cfg.T), mism)
+    err = assert_outputs_close(to_np(y)[keep], ref["y"][keep], tol_key(cfg), "y")
+    _log(f"[mid {name}] near-ties={near} excluded={len(mism)} err={err}")
+
+
+def _boundary_tokens(cfg, idx, cap=800):
+    """Tokens whose rows sit where a row-position bug would show: each
+    touched expert's first and last sorted slot, and the rows on both sides
+    of every 256-row tile boundary and, for fp8 weights, of the 128-row rest
+    tile boundary.  Taken from the oracle's dispatch of the oracle's routing."""
+    d = oracle.dispatch(idx, cfg.E)
+    off, sp = d["offsets"], d["sorted_pair"]
+    rows = set()
+    for e in range(cfg.E):
+        m = int(off[e + 1] - off[e])
+        if m == 0:
+            continue
+        cand = {0, m - 1}
+        for b in range(256, m, 256):
+            cand |= {b - 1, b}
+        if cfg.w_dtype == "fp8" and m % 256 and m % 256 <= 128 and m > 256:
+            cand |= {m - m % 256 - 1, m - m % 256}
+        if m > 128:
+            cand |= {127, 128}
+        rows |= {int(off[e]) + r for r in cand if 0 <= r < m}
+    toks = np.unique(np.asarray(sorted(sp[r] for r in rows)) // cfg.k)
+    if len(toks) > cap:
+        toks = np.unique(np.random.default_rng(0).choice(toks, size=cap, replace=False))
+    return toks
+
+
+@pytest.mark.parametrize("name", ["prefill8192_ep8", "clustered2048_fp8"])
+def test_forward_full_size_boundary_tokens(name):
+    """Prefill share and clustered fp8 at full size through moe_forward: the
+    routing of every token, and the outputs of the tokens at every expert's
+    first and last slot and at the tile boundaries."""
+    cfg = get_config(name)
+    _log(f"[full {name}] drawing inputs on the GPU")
+    gin, y, r, counts, near, mism = _full_forward(cfg)
+    toks = np.setdiff1d(_boundary_tokens(cfg, r["idx"]), mism)
+    _log(f"[full {name}] oracle outputs of {len(toks)} boundary tokens")
+    yo, _ = oracle.forward_tokens(gin, toks, workers=ORACLE_WORKERS)
+    err = assert_outputs_close(to_np(y)[toks], yo, tol_key(cfg), "y")
+    _log(f"[full {name}] near-ties={near} excluded={len(mism)} tokens={len(toks)} err={err}")
+    del gin
+    torch.cuda.empty_cache()
+
+
+def _pick_groups(counts):
+    """The largest group and one of each row class: 129..255, 33..128, 1..32."""
+    counts = np.asarray(counts)
+    pick = [int(np.argmax(counts))]
+    for lo, hi in ((129, 255), (33, 128), (1, 32)):
+        cand = [e for e in np.nonzero((counts >= lo) & (counts <= hi))[0] if e not in pick]
+        if cand:
+            pick.append(int(cand[len(cand) // 2]))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("name", ["prefill8192_ep8", "clustered2048_fp8"])
+def test_expert_ffn_full_size_whole_groups(name):
+    """The expert FFN at full size on the oracle's dispatch: every row of the
+    largest group and of one group in each row class (129..255, 33..128 and
+    1..32 rows, where the workload has one), plus the whole shared-expert
+    output, element by element."""
+    cfg = get_config(name)
+    _log(f"[ffn {name}] drawing inputs on the GPU")
+    gin = make_inputs(cfg, DEV)
+    r = oracle.route(oracle.to_f64(gin.x), oracle.to_f64(gin.wg), oracle.to_f64(gin.bias), cfg.k, cfg.score)
+    d = oracle.dispatch(r["idx"], cfg.E)
+    off = torch.from_numpy(d["offsets"].astype(np.int32)).to(DEV)
+    sp = torch.from_numpy(d["sorted_pair"].astype(np.int32)).to(DEV)
+    ys, ysh = moe.moe_expert_ffn(moe.cfg_from(cfg), gin.x, off, sp, moe.Weights.from_inputs(gin))
+    torch.cuda.synchronize()
+    groups = _pick_groups(d["counts"])
+    sizes = [int(d["counts"][e]) for e in groups]
+    _log(f"[ffn {name}] oracle for groups {groups} of {sizes} rows and the shared expert")
+    # the picked groups as a smaller grouped problem: group i is expert groups[i]
+    full_w = oracle.OracleWeights.from_inputs(gin)
+    sub_w = oracle.OracleWeights(len(groups), lambda i: full_w.expert(groups[i]), full_w.shared, full_w.fp8,
+                                 full_w.block)
+    segs = [d["sorted_pair"][d["offsets"][e]:d["offsets"][e + 1]] for e in groups]
+    sub_off = np.concatenate([[0], np.cumsum([len(sg) for sg in segs])])
+    sub_sp = np.concatenate(segs)
+    xa = oracle.prepare_activations(oracle.to_f64(gin.x), full_w.fp8, full_w.block)
+    ref_ys, ref_ysh = oracle.expert_ffn(xa, sub_off, sub_sp, cfg.k, sub_w)
+    rows = np.concatenate([np.arange(d["offsets"][e], d["offsets"][e + 1]) for e in groups])
+    key = tol_key(cfg)
+    e1 = assert_outputs_close(to_np(ys)[rows], ref_ys, key, "y_sorted")
+    e2 = assert_outputs_close(ysh, ref_ysh, key, "y_shared")
+    _log(f"[ffn {name}] y_sorted err {e1} y_shared err {e2}")
     del gin
     torch.cuda.empty_cache()

@@ -297,6 +297,9 @@ def test_forward_and_forward_tokens_agree_on_tiny_workload():
     y, r = oracle.forward_tokens(inp, toks)
     np.testing.assert_allclose(y, full["y"][toks], rtol=1e-12, atol=1e-12)
     assert (r["idx"] == full["route"]["idx"][toks]).all()
+    # the thread pool over experts changes the scheduling only: same bits
+    y4, _ = oracle.forward_tokens(inp, toks, workers=4)
+    assert np.array_equal(y, y4)
 
 
 def test_fp8_activation_quantiser_is_exact_on_representable_blocks():
