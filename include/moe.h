@@ -198,6 +198,23 @@ int moe_forward(const moe_cfg* cfg, const void* x, const void* w_gate, const flo
                 const moe_weights* w, void* y, int32_t* topk_idx_out, float* topk_w_out,
                 int32_t* counts_out, void* ws, size_t ws_bytes, void* hip_stream);
 
+/* moe_forward for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * kernels as moe_forward, with the same arguments except the workspace:
+ * the intermediates live in a fixed device scratch array inside the library
+ * (64 MiB, one per GPU, held from the library's load until the process
+ * ends), so the call allocates nothing and calls no allocating routine.
+ * Every launch stays on hip_stream (no side stream).  Layers whose
+ * workspace exceeds the scratch (moe_workspace_bytes(cfg) > 64 MiB; e.g.
+ * the 8192-token prefill share) return MOE_ERR_WORKSPACE before anything
+ * is enqueued.  All calls on one GPU share its scratch: calls that overlap
+ * in time on one GPU (two host threads, or two streams not ordered by the
+ * caller) race and give undefined results.  No part of the scratch needs
+ * to start at zero; each call writes what it reads. */
+int moe_forward_noalloc(const moe_cfg* cfg, const void* x, const void* w_gate, const float* sel_bias,
+                        const moe_weights* w, void* y, int32_t* topk_idx_out, float* topk_w_out,
+                        int32_t* counts_out, void* hip_stream);
+
 /* Graph of one whole-layer call (Perplexity, "Lower latency and higher
  * throughput with multi-node DeepSeek deployment", section "Quantization",
  * MoE-router paragraph: one graph is captured per batch size, so the

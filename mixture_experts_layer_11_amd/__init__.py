@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     moe_dispatch,
     moe_expert_ffn,
     moe_forward,
+    moe_forward_noalloc,
     moe_profile_start,
     moe_profile_stop,
     moe_quantize_fp8,

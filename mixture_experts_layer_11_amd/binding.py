@@ -21,7 +21,7 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = range(2)
 
 EXPORTS = ("moe_status_str", "moe_last_error", "moe_workspace_bytes", "moe_workspace_size", "moe_route", "moe_dispatch",
-           "moe_quantize_fp8", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_graph_capture",
+           "moe_quantize_fp8", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_noalloc", "moe_graph_capture",
            "moe_graph_launch", "moe_graph_destroy", "moe_routing_stats", "moe_profile_start", "moe_profile_stop")
 
 
@@ -80,6 +80,7 @@ def load_library(path: str = LIB_PATH):
     lib.moe_expert_ffn.argtypes = [cfgp, P, P, P, wp, P, P, P, SZ, P]
     lib.moe_combine.argtypes = [cfgp, P, P, P, P, P, P]
     lib.moe_forward.argtypes = [cfgp, P, P, P, wp, P, P, P, P, P, SZ, P]
+    lib.moe_forward_noalloc.argtypes = [cfgp, P, P, P, wp, P, P, P, P, P]
     lib.moe_routing_stats.argtypes = [cfgp, P, I32, P, P, P, P, P]
     lib.moe_graph_capture.argtypes = [cfgp, P, P, P, wp, P, P, P, P, P, SZ, P, ctypes.POINTER(P)]
     lib.moe_graph_launch.argtypes = [P, P]
@@ -273,6 +274,17 @@ def moe_forward(cfg: MoeCfg, x, w_gate, sel_bias, weights: Weights, ws=None, y=N
     _check(lib.moe_forward(ctypes.byref(cfg), _ptr(x), _ptr(w_gate), _ptr(sel_bias), ctypes.byref(w), _ptr(y),
                            _ptr(idx), _ptr(wt), _ptr(counts), _ptr(ws), ws.numel(), _stream(stream)))
     return (y, idx, wt, counts) if return_routing else y
+
+
+def moe_forward_noalloc(cfg: MoeCfg, x, w_gate, sel_bias, weights: Weights, y, topk_idx=None, topk_w=None,
+                        counts=None, stream=None):
+    """The whole layer on the library's fixed device scratch (no workspace);
+    the caller passes every output.  Returns y."""
+    w = weights.c_struct()
+    _check(load_library().moe_forward_noalloc(ctypes.byref(cfg), _ptr(x), _ptr(w_gate), _ptr(sel_bias),
+                                              ctypes.byref(w), _ptr(y), _ptr(topk_idx), _ptr(topk_w), _ptr(counts),
+                                              _stream(stream)))
+    return y
 
 
 class MoEGraph:

@@ -89,7 +89,8 @@ struct NoHook {
 };
 
 template <int DT, typename Hook = NoHook>
-hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st, bool planned, const Hook& hook = Hook()) {
+hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st, bool planned, bool fork,
+                      const Hook& hook = Hook()) {
   hipError_t e;
   if (!planned) {   // else the dispatch built the plan already
     MOE_LAUNCH("ffn_plan", ffn_plan_kernel, dim3(1), dim3(512), 0, st, a);
@@ -139,7 +140,7 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st, bool plan
     // 2.62 ms).  Outside that range one regime is empty or nearly so and the
     // fork and join only add latency (prefill8192_ep8: +40 us).
     const int mean_rows = P / c.E;
-    const bool both = bands > 0 && (max_fat > 0 || max_mid > 0) && mean_rows > kSkinnyRows / 2 &&
+    const bool both = fork && bands > 0 && (max_fat > 0 || max_mid > 0) && mean_rows > kSkinnyRows / 2 &&
                       mean_rows < 4 * kTileRows;
     // With a mean of at most one 256-row tile per routed expert, most groups'
     // weights are read by one row tile, and nontemporal loads keep them from
@@ -193,8 +194,12 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st, bool plan
 // compute-bound like the routed tiles: both stay on st, where running beside
 // the routed kernels would only add contention.
 template <int DT>
-hipError_t run_ffn(const moe_cfg& c, const Args& a, hipStream_t st, bool planned) {
-  if (!a.has_shared || a.halves) return run_routed<DT>(c, a, st, planned);
+hipError_t run_ffn(const moe_cfg& c, const Args& a, hipStream_t st, bool planned, bool fork) {
+  if (!a.has_shared || a.halves) return run_routed<DT>(c, a, st, planned, fork);
+  if (!fork) {
+    hipError_t e = run_shared<DT>(c, a, st);
+    return e != hipSuccess ? e : run_routed<DT>(c, a, st, planned, false);
+  }
   moe::SideStream side;
   hipError_t e = moe::side_stream(&side);
   if (e != hipSuccess) return e;
@@ -203,10 +208,10 @@ hipError_t run_ffn(const moe_cfg& c, const Args& a, hipStream_t st, bool planned
       moe::ceil_div(c.I, kTN / 2);
   if (c.T <= kSkinnyRows || shared_tiles1 >= side.cus) {
     e = run_shared<DT>(c, a, st);
-    return e != hipSuccess ? e : run_routed<DT>(c, a, st, planned);
+    return e != hipSuccess ? e : run_routed<DT>(c, a, st, planned, true);
   }
   hipError_t es = hipSuccess;
-  auto fork = [&](int at) -> hipError_t {   // at 2: the routed GEMM2 stage is next
+  auto fork_at = [&](int at) -> hipError_t {   // at 2: the routed GEMM2 stage is next
     if (at != 2) return hipSuccess;
     hipError_t ef = hipEventRecord(side.fork, st);
     if (ef == hipSuccess) ef = hipStreamWaitEvent(side.stream, side.fork, 0);
@@ -214,7 +219,7 @@ hipError_t run_ffn(const moe_cfg& c, const Args& a, hipStream_t st, bool planned
     es = run_shared<DT>(c, a, side.stream);
     return es;
   };
-  hipError_t er = run_routed<DT>(c, a, st, planned, fork);
+  hipError_t er = run_routed<DT>(c, a, st, planned, true, fork_at);
   // join even after a failed launch, so that work queued later on st never
   // runs ahead of work already queued on the side stream
   if ((e = hipEventRecord(side.join, side.stream)) == hipSuccess) e = hipStreamWaitEvent(st, side.join, 0);
@@ -251,7 +256,7 @@ size_t ffn_h_elem_bytes(const moe_cfg& c) { return c.w_dtype == MOE_BF16 ? 2 : 4
 
 hipError_t launch_expert_ffn(const moe_cfg& c, const void* x, const int32_t* offsets,
                              const int32_t* sorted_pair, const moe_weights& w, void* y_sorted,
-                             void* y_shared, const FfnWs& ws, hipStream_t st, bool planned) {
+                             void* y_shared, const FfnWs& ws, hipStream_t st, bool planned, bool fork) {
   Args a{};
   a.T = c.T;
   a.H = c.H;
@@ -288,12 +293,12 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const void* x, const int32_t* off
     a.a1s = ws.xs;
     a.a2 = ws.hq;
     a.a2s = ws.hs;
-    return run_ffn<MOE_FP8_E4M3>(c, a, st, planned);
+    return run_ffn<MOE_FP8_E4M3>(c, a, st, planned, fork);
   }
   a.a1 = static_cast<const uint8_t*>(x);
   a.a2 = a.h;
-  if (c.w_dtype == MOE_BF16) return run_ffn<MOE_BF16>(c, a, st, planned);
-  return run_ffn<MOE_F32>(c, a, st, planned);
+  if (c.w_dtype == MOE_BF16) return run_ffn<MOE_BF16>(c, a, st, planned, fork);
+  return run_ffn<MOE_F32>(c, a, st, planned, fork);
 }
 
 }  // namespace moe

@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include "../../include/moe.h"
+#include <mutex>
 #include <new>
 
 #include "moe_launch.h"
@@ -310,12 +311,14 @@ int moe_combine(const moe_cfg* cfg, const void* y_sorted, const void* y_shared, 
   return e == hipSuccess ? ok() : hip_fail(e, "moe_combine");
 }
 
-int moe_forward(const moe_cfg* cfg, const void* x, const void* w_gate, const float* sel_bias, const moe_weights* w,
-                void* y, int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
-                void* hip_stream) {
-  int s = check_cfg(cfg);
-  if (s) return s;
-  if (cfg->T == 0) return ok();
+}  // extern "C"
+
+namespace {
+
+// Validation of moe_forward's arguments other than the workspace.
+int check_forward_args(const moe_cfg* cfg, const void* x, const void* w_gate, const float* sel_bias,
+                       const moe_weights* w, void* y, int32_t* topk_idx_out, float* topk_w_out,
+                       int32_t* counts_out) {
   NEED_PTR(x);
   NEED_PTR(w_gate);
   NEED_PTR(y);
@@ -323,9 +326,14 @@ int moe_forward(const moe_cfg* cfg, const void* x, const void* w_gate, const flo
   if ((topk_idx_out && !aligned16(topk_idx_out)) || (topk_w_out && !aligned16(topk_w_out)) ||
       (counts_out && !aligned16(counts_out)))
     return fail(MOE_ERR_INVALID_ARG, "routing output pointers must be 16-byte aligned");
-  if ((s = check_weights(*cfg, w))) return s;
-  Layout L;
-  if ((s = check_ws(*cfg, ws, ws_bytes, &L))) return s;
+  return check_weights(*cfg, w);
+}
+
+// The whole layer on a validated workspace laid out as L.  With fork = false
+// every launch stays on hip_stream (no side stream is created or used).
+int forward_on(const moe_cfg* cfg, const void* x, const void* w_gate, const float* sel_bias, const moe_weights* w,
+               void* y, int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out, void* ws, const Layout& L,
+               void* hip_stream, bool fork) {
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   int32_t* idx = topk_idx_out ? topk_idx_out : at<int32_t>(ws, L.f_idx);
   float* wt = topk_w_out ? topk_w_out : at<float>(ws, L.f_w);
@@ -342,11 +350,72 @@ int moe_forward(const moe_cfg* cfg, const void* x, const void* w_gate, const flo
   bool planned = false;   // the one-workgroup dispatch also builds the FFN plan
   e = moe::launch_dispatch(*cfg, idx, counts, offsets, sorted, slot, at<int32_t>(ws, L.seg), st, &pa, &planned);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/dispatch");
-  e = moe::launch_expert_ffn(*cfg, x, offsets, sorted, *w, ys, ysh, fws, st, planned);
+  e = moe::launch_expert_ffn(*cfg, x, offsets, sorted, *w, ys, ysh, fws, st, planned, fork);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/expert_ffn");
   e = moe::launch_combine(*cfg, ys, ysh, slot, wt, y, st);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/combine");
   return ok();
+}
+
+// Device scratch of moe_forward_noalloc: one copy per GPU, held from the
+// module's load until the process ends, zero at load.  In host code
+// `scratch` is only a host-side stand-in for the symbol; its device address
+// comes from hipGetSymbolAddress, once per device, and only that address is
+// ever handed to kernels.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "moe_forward_noalloc/device");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "moe_forward_noalloc/hipGetSymbolAddress");
+    if (!p) return fail(MOE_ERR_HIP, "moe_forward_noalloc: no device address for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward(const moe_cfg* cfg, const void* x, const void* w_gate, const float* sel_bias, const moe_weights* w,
+                void* y, int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out, void* ws, size_t ws_bytes,
+                void* hip_stream) {
+  int s = check_cfg(cfg);
+  if (s) return s;
+  if (cfg->T == 0) return ok();
+  if ((s = check_forward_args(cfg, x, w_gate, sel_bias, w, y, topk_idx_out, topk_w_out, counts_out))) return s;
+  Layout L;
+  if ((s = check_ws(*cfg, ws, ws_bytes, &L))) return s;
+  return forward_on(cfg, x, w_gate, sel_bias, w, y, topk_idx_out, topk_w_out, counts_out, ws, L, hip_stream, true);
+}
+
+int moe_forward_noalloc(const moe_cfg* cfg, const void* x, const void* w_gate, const float* sel_bias,
+                        const moe_weights* w, void* y, int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out,
+                        void* hip_stream) {
+  int s = check_cfg(cfg);
+  if (s) return s;
+  if (cfg->T == 0) return ok();
+  if ((s = check_forward_args(cfg, x, w_gate, sel_bias, w, y, topk_idx_out, topk_w_out, counts_out))) return s;
+  const Layout L = layout(*cfg);
+  if (L.total > kScratchBytes)
+    return fail(MOE_ERR_WORKSPACE, "moe_forward_noalloc: this layer needs %zu bytes of scratch, above the fixed %zu",
+                L.total, kScratchBytes);
+  void* ws = nullptr;
+  if ((s = scratch_on_current_device(&ws))) return s;
+  return forward_on(cfg, x, w_gate, sel_bias, w, y, topk_idx_out, topk_w_out, counts_out, ws, L, hip_stream, false);
 }
 
 struct moe_graph {

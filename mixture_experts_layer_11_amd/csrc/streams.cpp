@@ -10,7 +10,6 @@
 // threads from sharing the events.
 
 #include <mutex>
-#include <set>
 #include <utility>
 #include <vector>
 
@@ -54,16 +53,22 @@ hipError_t capture_stream(hipStream_t* out) {
   return hipSuccess;
 }
 
+// (kernel, device) pairs whose limit is raised, in a fixed table so that no
+// call allocates host memory either; past its capacity the attribute is
+// simply set again on every launch (correct, only slower).
 hipError_t ensure_dynamic_lds(const void* kernel, int bytes) {
+  constexpr int kCap = 512;
   static std::mutex mu;
-  static std::set<std::pair<const void*, int>> done;   // (kernel, device)
+  static std::pair<const void*, int> done[kCap];
+  static int n_done = 0;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   std::lock_guard<std::mutex> lock(mu);
-  if (done.count({kernel, dev})) return hipSuccess;
+  for (int i = 0; i < n_done; ++i)
+    if (done[i].first == kernel && done[i].second == dev) return hipSuccess;
   if ((e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes)) != hipSuccess) return e;
-  done.insert({kernel, dev});
+  if (n_done < kCap) done[n_done++] = {kernel, dev};
   return hipSuccess;
 }
 
