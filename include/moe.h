@@ -112,14 +112,24 @@ const char* moe_last_error(void);
  * "Lower latency and higher throughput with multi-node DeepSeek
  * deployment", section "Quantization", MoE-router paragraph).  Returns 0
  * when cfg is invalid (moe_last_error() says why); a valid layer always
- * needs more than 0 bytes. */
+ * needs more than 0 bytes.
+ * The workspace's first 256 bytes hold the router's completion counters:
+ * they must be zero before a workspace is first used (zero-fill it once
+ * after allocating it), and every call leaves them zero again.  The rest
+ * needs no initialisation. */
 size_t moe_workspace_bytes(const moe_cfg* cfg);
 
 /* The same bound through an out-parameter, returning a moe_status (the form
  * every other entry point uses). */
 int moe_workspace_size(const moe_cfg* cfg, size_t* bytes);
 
-/* Router (steps: gate GEMM, scoring, selection bias, top-k, weights).
+/* Router (steps: gate GEMM, scoring, selection bias, top-k, weights; the
+ * vLLM DeepSeek-V4.1-Flash article, section "Kernels", item "Mega-Gate").
+ * Below 512 bf16 tokens (up to 1024 fp32 tokens) it is one launch:
+ * the last workgroup to finish a 16-token tile's partial gate GEMM sums the
+ * partials and selects, using the workspace's counters (see
+ * moe_workspace_bytes). */
+/* Router arguments:
  *   x        [T, H] act_dtype          w_gate [E, H] act_dtype
  *   sel_bias [E] fp32 or NULL: added to the scores for choosing experts only
  *   topk_idx [T, k] int32 out: chosen experts, descending biased score,
@@ -209,8 +219,9 @@ int moe_forward(const moe_cfg* cfg, const void* x, const void* w_gate, const flo
  * the 8192-token prefill share) return MOE_ERR_WORKSPACE before anything
  * is enqueued.  All calls on one GPU share its scratch: calls that overlap
  * in time on one GPU (two host threads, or two streams not ordered by the
- * caller) race and give undefined results.  No part of the scratch needs
- * to start at zero; each call writes what it reads. */
+ * caller) race and give undefined results.  The router's counters at the
+ * start of the scratch are zero when the library loads and every call
+ * leaves them zero; the rest of the scratch needs no initialisation. */
 int moe_forward_noalloc(const moe_cfg* cfg, const void* x, const void* w_gate, const float* sel_bias,
                         const moe_weights* w, void* y, int32_t* topk_idx_out, float* topk_w_out,
                         int32_t* counts_out, void* hip_stream);

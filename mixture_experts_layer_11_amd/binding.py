@@ -139,7 +139,10 @@ def moe_workspace_bytes(cfg: MoeCfg) -> int:
 
 
 def alloc_workspace(cfg: MoeCfg, device="cuda") -> torch.Tensor:
-    return torch.empty(max(workspace_size(cfg), 16), dtype=torch.uint8, device=device)
+    """A workspace for this layer, zero-filled: its first 256 bytes hold the
+    router's counters, which must be zero before the first call (each call
+    leaves them zero)."""
+    return torch.zeros(max(workspace_size(cfg), 256), dtype=torch.uint8, device=device)
 
 
 # --------------------------------------------------------------------------- tensors

@@ -86,7 +86,7 @@ int check_cfg(const moe_cfg* c) {
 }
 
 struct Layout {
-  size_t route_part, seg, plan, h, hq, hs, xq, xs;
+  size_t ctr, route_part, seg, plan, h, hq, hs, xq, xs;
   size_t f_idx, f_w, f_counts, f_offsets, f_sorted, f_slot, f_ysorted, f_yshared;
   size_t total;
 };
@@ -104,6 +104,7 @@ Layout layout(const moe_cfg& c) {
   const size_t Ts = c.I_shared > 0 ? T : 0;
   const bool fp8 = c.w_dtype == MOE_FP8_E4M3;
   const size_t qb = fp8 ? (size_t)c.quant_block : 1;
+  L.ctr = take(moe::kRouteCounters * sizeof(int32_t));   // offset 0: must start zeroed
   L.route_part = take(moe::route_ws_bytes(c));
   L.seg = take(moe::dispatch_ws_bytes(c));
   L.plan = take(moe::ffn_plan_ints(c) * sizeof(int32_t));
@@ -224,7 +225,7 @@ int moe_route(const moe_cfg* cfg, const void* x, const void* w_gate, const float
   Layout L;
   if ((s = check_ws(*cfg, ws, ws_bytes, &L))) return s;
   hipError_t e = moe::launch_route(*cfg, x, w_gate, sel_bias, topk_idx, topk_w, at<float>(ws, L.route_part),
-                                   static_cast<hipStream_t>(hip_stream));
+                                   at<int32_t>(ws, L.ctr), static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? ok() : hip_fail(e, "moe_route");
 }
 
@@ -343,7 +344,8 @@ int forward_on(const moe_cfg* cfg, const void* x, const void* w_gate, const floa
   int32_t* slot = at<int32_t>(ws, L.f_slot);
   void* ys = at<void>(ws, L.f_ysorted);
   void* ysh = cfg->I_shared > 0 ? at<void>(ws, L.f_yshared) : nullptr;
-  hipError_t e = moe::launch_route(*cfg, x, w_gate, sel_bias, idx, wt, at<float>(ws, L.route_part), st);
+  hipError_t e = moe::launch_route(*cfg, x, w_gate, sel_bias, idx, wt, at<float>(ws, L.route_part),
+                                   at<int32_t>(ws, L.ctr), st);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/route");
   const moe::FfnWs fws = ffn_ws(ws, L);
   const moe::PlanArgs pa = moe::ffn_plan_args(*cfg, fws.plan);

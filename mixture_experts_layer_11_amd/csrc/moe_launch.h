@@ -32,8 +32,11 @@ class ProfScope {
 // ---- router
 int route_splits(const moe_cfg& c);
 size_t route_ws_bytes(const moe_cfg& c);
+// ctr: the router's counters, kRouteCounters ints at the workspace start,
+// zero before a call and zero after it.
+constexpr int kRouteCounters = 64;
 hipError_t launch_route(const moe_cfg& c, const void* x, const void* wg, const float* bias, int32_t* idx,
-                        float* w, float* part, hipStream_t st);
+                        float* w, float* part, int32_t* ctr, hipStream_t st);
 
 // ---- expert FFN work-list plan inputs besides the per-group row counts, so
 // that a kernel already holding the counts (the one-workgroup dispatch) can

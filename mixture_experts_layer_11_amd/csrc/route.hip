@@ -9,15 +9,17 @@
 // order-preserving uint32 keys (DPP row reductions), then the lowest expert
 // holding it (a ballot), so equal keys go to the lower expert.
 //
-// Below 512 tokens (and for fp32 activations) one workgroup (4 waves) owns a
-// tile of 16 tokens and all E <= 256 experts; wave w accumulates expert
-// tiles w, w+4, w+8, w+12 of 16 experts with 16x16 MFMAs straight from
-// global memory.  From 512 bf16 tokens on, an LDS-staged kernel owns 64 or
-// 128 tokens per workgroup, so the gate weights are re-read far less often
-// (see gate_tile_kernel).  When the token tiles are too few to fill the
-// GPU, the K range is split over workgroups; each writes fp32 partial logits
-// and a second kernel sums them in split order (fixed order: bitwise
-// reproducible) before the same selection.
+// Below 512 bf16 tokens (up to 1024 fp32 tokens) the whole router is one
+// launch (gate_last_kernel): workgroups split the 16-token tiles' gate GEMM
+// by expert groups and K ranges, and the last one to finish a tile sums its
+// partials in split order and selects.  From 512 bf16 tokens on, an
+// LDS-staged kernel owns 64 or 128 tokens per workgroup, so the gate weights
+// are re-read far less often (see gate_tile_kernel); beyond 1024 fp32 tokens
+// a workgroup (4 waves) owns a 16-token tile and all E <= 256 experts with
+// 16x16 MFMAs straight from global memory (gate_kernel).  When those tiles
+// are too few to fill the GPU, the K range is split over workgroups; each
+// writes fp32 partial logits and a second kernel sums them in split order
+// (fixed order: bitwise reproducible) before the same selection.
 
 #include "moe_common.h"
 #include "moe_launch.h"
@@ -252,6 +254,166 @@ __global__ __launch_bounds__(256) void gate_kernel(const uint8_t* __restrict__ x
   }
 }
 
+// ---- few tokens: the whole router in one launch
+//
+// The decode shapes (a few to a few hundred tokens) read the 3.7 MB gate
+// weight with little reuse, so the work is spread over many workgroups:
+// workgroup (token tile, expert group, K split) computes the partial logits
+// of 16 tokens x 64 experts over its K range (8 waves split the range
+// further; their partials are added in wave order through LDS) and stores
+// them.  It then counts itself done on its token tile's counter; the last
+// workgroup to arrive sums the tile's partials over the splits in split order
+// (bitwise reproducible) and runs scoring, bias, top-k and weights for the
+// tile's 16 tokens, two per wave, and clears the counter for the next call.
+// So gate GEMM, scoring, bias and top-k are one launch with no round trip of
+// the scores through a second kernel.  Nothing waits on another workgroup:
+// each either returns or is the last.  The counters must be zero when a call
+// starts; every call leaves them zero.
+constexpr int kLastEG = 64;        // experts per workgroup
+constexpr int kLastWaves = 8;
+constexpr int kLastMaxTiles = 64;  // token tiles (counters) of one call
+
+template <int DT>
+__global__ __launch_bounds__(512) void gate_last_kernel(const uint8_t* __restrict__ x, const uint8_t* __restrict__ wg,
+                                                        int T, int H, int nsplit, float* __restrict__ part,
+                                                        int* __restrict__ ctr, RouteOut o) {
+  using F = Frag<DT>;
+  __shared__ float red[kLastWaves][16][kLastEG + 4];
+  __shared__ float lg_s[16][kMaxE + 4];
+  __shared__ int last;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = lane & 15, grp = lane >> 4;
+  const int E = o.E;
+  const int ng = (E + kLastEG - 1) / kLastEG;
+  const int eg = blockIdx.y % ng, s = blockIdx.y / ng;
+  const int t0 = blockIdx.x * kTokTile;
+  const int e0 = eg * kLastEG;
+  const int nt = min(4, (E - e0 + 15) >> 4);          // 16-expert tiles of this group
+  const int nfrag = H / F::KF;
+  const int f0 = (int)((long long)nfrag * s / nsplit), f1 = (int)((long long)nfrag * (s + 1) / nsplit);
+  const int wf0 = f0 + (int)((long long)(f1 - f0) * wave / kLastWaves);
+  const int wf1 = f0 + (int)((long long)(f1 - f0) * (wave + 1) / kLastWaves);
+  const size_t rowbytes = (size_t)H * F::ESZ;
+  const uint8_t* pa = x + (size_t)min(t0 + row, T - 1) * rowbytes + grp * 16;   // rows past T: never stored
+  const uint8_t* pb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pb[j] = wg + (size_t)min(e0 + j * 16 + row, E - 1) * rowbytes + grp * 16;
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int f = wf0; f < wf1; ++f) {
+    const size_t off = (size_t)f * 64;
+    const i32x4 av = ld16(pa + off);
+    i32x4 bv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < nt) bv[j] = ld16(pb[j] + off);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < nt) F::mma(acc[j], av, bv[j]);
+  }
+  // acc[j][i] = partial logit of token t0 + 4 grp + i, expert e0 + 16 j + row
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][4 * grp + i][16 * j + row] = acc[j][i];
+  __syncthreads();
+  for (int idx = tid; idx < 16 * kLastEG; idx += 512) {
+    const int r = idx / kLastEG, e = idx % kLastEG;
+    float v = red[0][r][e];
+#pragma unroll
+    for (int w = 1; w < kLastWaves; ++w) v += red[w][r][e];   // wave order
+    // device-scope stores: written through to where every XCD reads them
+    if (t0 + r < T && e0 + e < E)
+      __hip_atomic_store(&part[((size_t)s * T + t0 + r) * E + e0 + e], v, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // Every thread's stores have completed before the workgroup counts itself
+  // done (the barrier waits for them and orders them before the count).  A
+  // device-scope release fence would instead write back this XCD's whole L2
+  // (512 such fences made the 256-token router 4x slower).
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    last = __hip_atomic_fetch_add(&ctr[blockIdx.x], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           (int)gridDim.y - 1;
+  __syncthreads();
+  if (!last) return;
+  // logits of the tile's tokens: the partials summed over the splits in split order
+  if ((E & 3) == 0) {
+    // 16-byte device-scope loads (through a buffer resource, whose cache
+    // policy can carry the scope bit), every split's load of two positions
+    // issued before the first add
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(part, 0, (int)((size_t)nsplit * T * E * sizeof(float)), 0x00020000);
+    const int E4 = E >> 2;
+    for (int q0 = tid; q0 < 16 * E4; q0 += 1024) {
+      f32x4 u[2][8];
+      int qr[2], qe[2];
+      bool ok[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int q = q0 + 512 * p;
+        qr[p] = q / E4;
+        qe[p] = q - qr[p] * E4;
+        ok[p] = q < 16 * E4 && t0 + qr[p] < T;
+#pragma unroll
+        for (int sp = 0; sp < 8; ++sp) {
+          u[p][sp] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (ok[p] && sp < nsplit) {
+            const int off = (int)((((size_t)sp * T + t0 + qr[p]) * E + 4 * qe[p]) * sizeof(float));
+            u[p][sp] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 16));   // 16: sc1
+          }
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        if (!ok[p]) continue;
+        f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sp = 0; sp < 8; ++sp)
+          if (sp < nsplit) v += u[p][sp];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) lg_s[qr[p]][4 * qe[p] + c] = v[c];
+      }
+    }
+  } else {
+  for (int idx = tid; idx < 16 * E; idx += 512) {
+    const int r = idx / E, e = idx % E;
+    const int t = t0 + r;
+    if (t >= T) continue;
+    float* p = part + (size_t)t * E + e;
+    const size_t stride = (size_t)T * E;
+    float v = 0.f;
+    int sp = 0;
+    for (; sp + 8 <= nsplit; sp += 8) {
+      float q[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)   // device-scope loads: not served from a stale cache line
+        q[u] = __hip_atomic_load(p + (size_t)(sp + u) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v += q[u];
+    }
+    for (; sp < nsplit; ++sp)
+      v += __hip_atomic_load(p + (size_t)sp * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    lg_s[r][e] = v;
+  }
+  }
+  __syncthreads();
+  for (int r = wave; r < 16; r += kLastWaves) {
+    const int t = t0 + r;
+    if (t >= T) break;
+    float lg[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int e = lane + 64 * c;
+      lg[c] = e < E ? lg_s[r][e] : 0.f;
+    }
+    route_token(lg, t, o);
+  }
+  if (tid == 0) __hip_atomic_store(&ctr[blockIdx.x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // next call
+}
+
 // ---- many tokens: LDS-staged gate GEMM
 //
 // For hundreds of tokens and more the gate GEMM is a plain [T, H] x [H, E]
@@ -475,7 +637,25 @@ GateShape gate_shape(const moe_cfg& c) {
 
 }  // namespace
 
+// The one-launch router for up to kLastMaxTiles token tiles (see
+// gate_last_kernel): K splits so that each wave keeps at least two
+// fragments, at most 8 (the last workgroup reads 8 partials per logit).
+// Measured at H = 7168, E = 256 (router us, split + reduce launches before):
+// 16 tokens 8 splits 21.3-22.3 (25.5 before), 4 splits 24.3-24.6;
+// 256 tokens 8 splits 26.8, 4 splits 24.9-25.5 (28.3-30.0 before).
+static int last_splits(const moe_cfg& c) {
+  const int kf = c.act_dtype == MOE_F32 ? Frag<MOE_F32>::KF : Frag<MOE_BF16>::KF;
+  const int cap = ceil_div(c.T, kTokTile) <= 4 ? 8 : 4;   // at most 8: the last workgroup's loads
+  const int s = c.H / kf / (2 * kLastWaves);
+  return s < 1 ? 1 : (s > cap ? cap : s);
+}
+
+static bool use_last(const moe_cfg& c) {
+  return gate_shape(c).ep == 0 && ceil_div(c.T, kTokTile) <= kLastMaxTiles;
+}
+
 int route_splits(const moe_cfg& c) {
+  if (use_last(c)) return last_splits(c);
   const GateShape gs = gate_shape(c);
   if (gs.ep > 0) {   // fill the device with (token tile, K range) workgroups, >= 2 NST slices per range
     const int tiles = ceil_div(c.T, gs.tt);
@@ -495,6 +675,7 @@ int route_splits(const moe_cfg& c) {
 
 size_t route_ws_bytes(const moe_cfg& c) {
   const int s = route_splits(c);
+  if (use_last(c)) return (size_t)s * c.T * c.E * sizeof(float);   // partials of every expert group
   return s > 1 ? (size_t)s * c.T * c.E * sizeof(float) : 0;
 }
 
@@ -543,8 +724,19 @@ static hipError_t launch_gate_tile_shape(const moe_cfg& c, const GateShape& gs, 
 }
 
 hipError_t launch_route(const moe_cfg& c, const void* x, const void* wg, const float* bias, int32_t* idx,
-                        float* w, float* part, hipStream_t st) {
+                        float* w, float* part, int32_t* ctr, hipStream_t st) {
   RouteOut o{bias, idx, w, c.E, c.k, c.score, c.routed_scale, c.n_group, c.topk_group};
+  if (use_last(c)) {
+    const int s = last_splits(c);
+    const dim3 grid(ceil_div(c.T, kTokTile), ceil_div(c.E, kLastEG) * s);
+    const uint8_t* xb = static_cast<const uint8_t*>(x);
+    const uint8_t* wb = static_cast<const uint8_t*>(wg);
+    if (c.act_dtype == MOE_F32)
+      MOE_LAUNCH("route_gate_last", gate_last_kernel<MOE_F32>, grid, dim3(512), 0, st, xb, wb, c.T, c.H, s, part, ctr, o);
+    else
+      MOE_LAUNCH("route_gate_last", gate_last_kernel<MOE_BF16>, grid, dim3(512), 0, st, xb, wb, c.T, c.H, s, part, ctr, o);
+    return hipGetLastError();
+  }
   const GateShape gs = gate_shape(c);
   if (gs.ep > 0) {
     const int s = route_splits(c);

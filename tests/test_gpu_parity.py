@@ -158,6 +158,10 @@ MANY = {
     # K = 384: 6 slices of 64 (not a power of two), exactly 512 tokens (the threshold)
     "many_e64_h384_t512": _D16.with_(name="many_e64_h384_t512", T=512, H=384, E=64, k=6),
     "many_e256_groups_split": _D16.with_(name="many_e256_groups_split", T=1030, H=1024, n_group=8, topk_group=4),
+    # fp32 beyond the one-launch router's 64 token tiles: the 16-token split-K
+    # kernel with the reduce (69 tiles) and, from 256 tiles, in one K range
+    "many_f32_split_reduce": get_config("tiny_f32").with_(name="many_f32_split_reduce", T=1100, H=512),
+    "many_f32_one_range": get_config("tiny_f32").with_(name="many_f32_one_range", T=4200, H=256, E=64, k=6),
 }
 
 
@@ -166,6 +170,24 @@ def test_route_many_tokens(name):
     cfg = MANY[name]
     x, wg, bias = make_router_inputs(cfg, "cpu")
     _route_check(cfg, x, wg, bias)
+
+
+@pytest.mark.parametrize("name", ["decode16", "decode256"])
+def test_route_one_launch_leaves_counters_zero(name):
+    """The one-launch router counts finished workgroups per token tile in the
+    workspace's first 256 bytes: after each call they are zero again, and a
+    second call on the same workspace gives the same bits."""
+    cfg = get_config(name)
+    x, wg, bias = make_router_inputs(cfg, DEV)
+    mc = moe.cfg_from(cfg)
+    ws = moe.alloc_workspace(mc)
+    idx1, w1 = moe.moe_route(mc, x, wg, bias, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ws[:256]) == 0
+    idx2, w2 = moe.moe_route(mc, x, wg, bias, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ws[:256]) == 0
+    assert torch.equal(idx1, idx2) and torch.equal(w1, w2)
 
 
 # Group-limited routing: DeepSeek-V3-like groups (256 experts in 8 groups,
