@@ -58,7 +58,7 @@ __device__ __forceinline__ void skinny_epilogue(const Args& a, const Group& gr, 
 #pragma unroll
         for (int j = 0; j < NTP / 2; ++j) {
           const float gv = acc[mt][j][i], uv = acc[mt][j + NTP / 2][i];
-          store_h<DT>(a.h, hrow + it * cols_per_item + 8 * (p * (NTP / 2) + j) + r8, silu(gv) * uv);
+          store_h<DT>(a.h, hrow + it * cols_per_item + 8 * (p * (NTP / 2) + j) + r8, silu_for<DT>(gv) * uv);
         }
       } else {
         uint8_t* ybase = gr.routed ? a.y_sorted : a.y_shared;
@@ -478,7 +478,7 @@ __device__ __forceinline__ void skinny_ring(const Args& a, const Group& gr, int 
 #pragma unroll
         for (int np = 0; np < NP / 2; ++np)   // gate pair np, up pair np + NP / 2
           store_h<DT>(a.h, hrow + it * cols_per_item + 16 * np + n16,
-                      silu(acc[mp][np][i]) * acc[mp][np + NP / 2][i]);
+                      silu_for<DT>(acc[mp][np][i]) * acc[mp][np + NP / 2][i]);
       } else {
         uint8_t* ybase = gr.routed ? a.y_sorted : a.y_shared;
         const size_t yrow = (size_t)out_row(a, gr, r) * a.H;

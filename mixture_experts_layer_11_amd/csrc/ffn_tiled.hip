@@ -351,7 +351,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
         if (MODE == 1) {
 #pragma unroll
           for (int jp = 0; jp < NTW / 2; ++jp) {
-            const float v = silu(acc[i][2 * jp][q]) * acc[i][2 * jp + 1][q];
+            const float v = silu_for<DT>(acc[i][2 * jp][q]) * acc[i][2 * jp + 1][q];
             const int lc = (wn * (NTW / 2) + jp) * 16 + row;
             if constexpr (FP8) reinterpret_cast<float*>(lrow)[lc] = v;
             else reinterpret_cast<uint16_t*>(lrow)[lc] = f32_to_bf16(v);
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
         for (int jp = 0; jp < NTW / 2; ++jp) {
           const float gv = acc[i][2 * jp][q], uv = acc[i][2 * jp + 1][q];
           const int col = nt * (kTN / 2) + (wn * (NTW / 2) + jp) * 16 + row;
-          if (col < a.I) store_h<DT>(a.h, hrow + col, silu(gv) * uv);
+          if (col < a.I) store_h<DT>(a.h, hrow + col, silu_for<DT>(gv) * uv);
         }
       } else {
         uint8_t* ybase = gr.routed ? a.y_sorted : a.y_shared;
