@@ -116,6 +116,8 @@ def main(argv=None):
     ap.add_argument("--copy-fetch")
     ap.add_argument("--copy-write")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--counters", action="append", default=[],
+                    help="counter_collection.csv of another --pmc pass (SQ_*, GRBM_* counters), repeatable")
     ap.add_argument("--bench-log", help="output of the bench run profiled with --kernel-trace")
     ap.add_argument("--command", action="append", default=[], help="command lines that produced the inputs")
     ap.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
@@ -181,6 +183,36 @@ def main(argv=None):
                "fetch_scale": ff, "write_scale": wf, "commands": args.command}
         with open(os.path.join(args.out_dir, f"traffic_{args.kernel}_{args.workload}.json"), "w") as f:
             json.dump(rec, f, indent=1)
+    if args.counters:
+        med = {}
+        for path in args.counters:
+            names = sorted({r["Counter_Name"] for r in csv.DictReader(open(path))})
+            for c in names:
+                v = _counter_values(path, prefix, c)
+                if v:
+                    med[c] = (statistics.median(v), len(v))
+        lines += ["", "## Shader counters (rocprofv3 --pmc, medians over dispatches)", "",
+                  "| counter | median per dispatch | dispatches |", "|---|---|---|"]
+        lines += [f"| {c} | {v:.4e} | {n} |" for c, (v, n) in sorted(med.items())]
+        if "GRBM_GUI_ACTIVE" in med:
+            raw = med["GRBM_GUI_ACTIVE"][0] / avg_us          # cycles per us = MHz
+            # the counter is summed over the 8 XCDs' graphics blocks when it reads above any clock
+            per = 8 if raw > 4000 else 1
+            mhz = raw / per
+            lines += ["", f"Clock while the kernel runs: GRBM_GUI_ACTIVE {med['GRBM_GUI_ACTIVE'][0]:.4e} / "
+                          f"{avg_us:.1f} us{' / 8 XCDs' if per == 8 else ''} = **{mhz:.0f} MHz** "
+                          f"(2400 MHz is the clock of the published peaks)."]
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in med:
+                simd_cycles = mhz * avg_us * 1024          # 256 CUs x 4 SIMDs
+                busy = med["SQ_VALU_MFMA_BUSY_CYCLES"][0] / simd_cycles
+                lines.append(f"MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (kernel cycles x 1024 SIMDs) = **{busy:.3f}**.")
+                if "SQ_INSTS_MFMA" in med:
+                    lines.append(f"Busy cycles per MFMA instruction: "
+                                 f"{med['SQ_VALU_MFMA_BUSY_CYCLES'][0] / med['SQ_INSTS_MFMA'][0]:.1f}.")
+            if bench and bench["roofline"]["unit"] == "TFLOP/s":
+                at_clock = bench["roofline"]["peak"] * mhz / 2400.0
+                lines.append(f"Peak at that clock {at_clock:.0f} TFLOP/s: the kernel runs at "
+                             f"{bench['roofline']['achieved'] / at_clock:.3f} of it.")
     with open(os.path.join(args.out_dir, f"{args.kernel}_{args.workload}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
