@@ -82,7 +82,7 @@ def rocprof_name(kernel: str, w_dtype: str) -> str:
              "route_gate_fused": "void (anonymous namespace)::gate_kernel<",
              "route_gate_split": "void (anonymous namespace)::gate_kernel<",
              "route_gate_tiled": "void (anonymous namespace)::gate_tile_kernel<",
-             "combine": "void (anonymous namespace)::combine_kernel<",
+             "combine": "void (anonymous namespace)::combine",
              "quant_fp8": "void (anonymous namespace)::quant_fp8_kernel<"}
     return fixed[kernel]
 
