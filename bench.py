@@ -157,7 +157,7 @@ def host_info():
     return {"cpu": model, "nproc": os.cpu_count(), "ram_gib": ram_gb}
 
 
-def cpu_baseline(inp_gpu, n_tokens, min_s=10.0, max_passes=4):
+def cpu_baseline(inp_gpu, n_tokens, min_s=10.0, max_passes=8):
     """Time the fp64 oracle, single-threaded, on the first n tokens, repeating
     the pass until at least min_s seconds of CPU work (at most max_passes).
     Returns (seconds, passes)."""
@@ -197,8 +197,10 @@ def shares_device(cfg):
     return cfg.T > SKINNY_ROWS and SKINNY_ROWS // 2 < mean_rows < 1024
 
 
-def measure(moe, torch, cfg, steps, warmup, detail=True, graph=True):
-    """Time `steps` whole-layer steps of one workload; returns a dict."""
+def measure(moe, torch, cfg, steps, warmup, detail=True, graph=True, warm_s=0.0):
+    """Time `steps` whole-layer steps of one workload; returns a dict.
+    Warm-up is `warmup` steps, continued until at least `warm_s` seconds of
+    steps have run (the GPU's clocks drop while the host works alone)."""
     from moe_inputs import make_inputs
 
     tg = time.perf_counter()
@@ -212,8 +214,13 @@ def measure(moe, torch, cfg, steps, warmup, detail=True, graph=True):
                     device="cuda")
     step = lambda: moe.moe_forward(mc, inp.x, inp.wg, inp.bias, w, ws=ws, y=y)   # noqa: E731
 
-    for _ in range(warmup):
+    tw = time.perf_counter()
+    n_warm = 0
+    while n_warm < warmup or time.perf_counter() - tw < warm_s:
         step()
+        n_warm += 1
+        if n_warm % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     # untimed pass: routing of this batch (for the byte model) and the per-kernel
@@ -292,7 +299,7 @@ def measure(moe, torch, cfg, steps, warmup, detail=True, graph=True):
     layer_frac = layer_tflops / peak if layer_bound == "mfma" else layer_gbps / HBM_PEAK_GBPS
     out = {
         "workload": cfg.name, "T": cfg.T, "dtype": wdt, "tokens_per_s": round(tokens_per_s, 1),
-        "ms_per_step": round(ms_per_step, 4), "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 4), "steps": steps, "warmup": n_warm,
         "roofline": roof,
         "layer": {"algorithmic_bytes": layer["bytes"], "flops": layer["flops"], "GBps": round(layer_gbps, 1),
                   "hbm_frac": round(layer_gbps / HBM_PEAK_GBPS, 4), "TFLOPs": round(layer_tflops, 2),
@@ -404,10 +411,12 @@ def main(argv=None):
         for name in OTHER_WORKLOADS:
             if name == cfg.name:
                 continue
-            print(f"[bench] {name}: 3 warmup + {args.other_steps} timed steps", file=sys.stderr, flush=True)
-            o = measure(moe, torch, get_config(name), args.other_steps, 3, detail=False)
+            print(f"[bench] {name}: >= 3 warmup steps over >= 0.5 s + {args.other_steps} timed steps", file=sys.stderr,
+                  flush=True)
+            o = measure(moe, torch, get_config(name), args.other_steps, 3, detail=False, warm_s=0.5)
             rf = o["roofline"]
             others[name] = {"tokens_per_s": o["tokens_per_s"], "ms_per_step": o["ms_per_step"],
+                            "steps": o["steps"], "warmup_steps": o["warmup"],
                             "layer_bound": o["layer"]["bound"], "layer_frac": o["layer"]["frac"],
                             "layer_GBps": o["layer"]["GBps"], "layer_TFLOPs": o["layer"]["TFLOPs"],
                             "gemms_share_device": o["gemms_share_device"],
