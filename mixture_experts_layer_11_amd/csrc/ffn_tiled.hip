@@ -33,6 +33,12 @@ using namespace moe::ffn;
 // way: 16 bytes per lane every 4th slice into one of two 4-slice blocks when
 // the slice count is a multiple of 4, else 4 bytes per lane per slice.
 // Waves whose 64 rows lie beyond the tile's valid rows skip their MFMAs.
+// bf16 GEMM1 on 256-row tiles keeps the weight slices three deep and the
+// activation slices two deep (160 KB).  For bf16 256-row tiles the direct
+// loads go through buffer resources when the offsets fit 32 bits: with the
+// global form of the LDS-direct load outstanding, the compiler's wait
+// counting waits for every LDS fragment read before each first use, with
+// the buffer form it waits for exactly the reads each MFMA needs.
 
 template <int DT, int TM> struct TileCfg {
   static constexpr int SL = 128;                              // bytes of K per slice and row
@@ -57,7 +63,15 @@ template <int DT, int TM> struct TileCfg {
   // fall in different LDS banks.
   static constexpr size_t EPI_STRIDE = 512 + 16;
   static constexpr size_t EPI_BYTES = DT == MOE_F32 ? 0 : (size_t)TM * EPI_STRIDE;
-  static constexpr size_t MAIN_BYTES = (size_t)NST * STAGE + (DT == MOE_FP8_E4M3 ? SCB : 0);
+  // bf16 256-row tiles: the A rows (gathered activations, mostly fetched
+  // from beyond the XCD's L2) in 3 slots and the B rows in 2, so the A loads
+  // run two slices ahead of the MFMAs and the B loads one.  160 KB in all.
+  // bf16 256-row tiles of GEMM1 keep the weight slices 3 deep and the
+  // activation slices 2 deep (the ring below): 5 slots of 32 KB
+  static constexpr bool RING_OK = DT == MOE_BF16 && TM == 256;
+  static constexpr int SLOT = TM * SL;                        // one operand's slice (TM == kTN)
+  static constexpr size_t MAIN_BYTES =
+      RING_OK ? (size_t)5 * SLOT : (size_t)NST * STAGE + (DT == MOE_FP8_E4M3 ? SCB : 0);
   static constexpr size_t LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   __device__ static __forceinline__ int off(int r, int c) { return r * SL + ((c ^ (r & 7)) << 4); }
@@ -103,7 +117,29 @@ __device__ __forceinline__ void tile_issue(uint8_t* smem, const uint8_t* const* 
   }
 }
 
-template <int DT, int MODE, bool SHARED, int TM, bool BLK, bool SW>
+// One operand's direct loads of a slice (LP per thread) into an LDS slot.
+template <int LP, bool NT>
+__device__ __forceinline__ void issue_rows(uint8_t* slot, const uint8_t* const* g, size_t off, int wave) {
+  uint8_t* d = slot + wave * LP * 1024;
+#pragma unroll
+  for (int i = 0; i < LP; ++i) __builtin_amdgcn_global_load_lds(g[i] + off, d + i * 1024, 16, 0, NT ? 2 : 0);
+}
+
+// The same through a buffer resource (32-bit offsets from the resource's
+// base; the slice offset in soff).  Same LDS effect; the compiler's wait
+// counting then keeps exact LDS-read counts, where with the global form
+// pending it waits for every outstanding LDS read before each use.
+template <int LP, bool NT>
+__device__ __forceinline__ void issue_rows_buf(uint8_t* slot, __amdgpu_buffer_rsrc_t rs, const uint32_t* voff,
+                                               int soff, int wave) {
+  uint8_t* d = slot + wave * LP * 1024;
+#pragma unroll
+  for (int i = 0; i < LP; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(d + i * 1024), 16,
+                                             (int)voff[i], soff, 0, NT ? 2 : 0);
+}
+
+template <int DT, int MODE, bool SHARED, int TM, bool BLK, bool SW, bool BUF>
 __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
   using F = Frag<DT>;
   using C = TileCfg<DT, TM>;
@@ -178,6 +214,22 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
     const int lc = (C::off(r, lane % C::CPR) - r * SL) >> 4;
     gb[i] = wbase + (size_t)b_wrow(r) * krow + lc * 16;
   }
+  // With BUF (bf16 256-row tiles, when the host finds the activation
+  // matrix and one expert's weights below 4 GB) the direct loads go through
+  // buffer resources instead: the A base is the activation matrix, the B
+  // base this group's weights, with per-lane 32-bit offsets.
+  static_assert(!BUF || (DT == MOE_BF16 && TM == 256), "buffer loads: bf16 256-row tiles");
+  const __amdgpu_buffer_rsrc_t rsa =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(asrc), 0, (int)0xffffffffu, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsb =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(wbase), 0, (int)0xffffffffu, 0x00020000);
+  uint32_t va[C::LPA], vb[C::LPB];
+  if constexpr (BUF) {
+#pragma unroll
+    for (int i = 0; i < C::LPA; ++i) va[i] = (uint32_t)(ga[i] - asrc);
+#pragma unroll
+    for (int i = 0; i < C::LPB; ++i) vb[i] = (uint32_t)(gb[i] - wbase);
+  }
   // fp8 scales: scale slot s = 64 * wave + lane of each stage holds the
   // slice's scale of A row s (s < TM), of B row s - TM (s < TM + kTN), or a
   // copy of B row 0's (the remaining slots, never read).
@@ -195,32 +247,51 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
     for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int mval = min(4, max(0, (rows - wm * 64 + 15) >> 4));   // this wave's M tiles holding valid rows
 
-#pragma unroll
-  for (int p = 0; p < NST - 1; ++p)
-    if (p < nkt) tile_issue<DT, TM, BLK, SW>(smem, ga, gb, gs, p, p, wave);
   bool full_tile = false;
   if constexpr (!FP8) full_tile = mval == 4;
-  if (full_tile) {
-    // Full tiles (all 64 rows of every M tile valid; bf16 and fp32 weights,
-    // two stages): one straight-line block per slice, so the scheduling
-    // hints below can order the fragment reads, the next slice's direct
-    // loads and the MFMAs.  The first half's reads go first; the next slice's
-    // loads are issued while they are in flight, spread over the first
-    // MFMAs, so a wave never stalls on a full load queue while it has MFMAs
-    // ready; the second half's reads are interleaved with the rest of the
-    // first half's MFMAs.  The last slice reloads itself into the free stage,
-    // which keeps the block free of branches.
-    if constexpr (!FP8) {
-      static_assert(NST == 2, "the full-tile loop assumes two stages");
+  constexpr bool RING = C::RING_OK && MODE == 1;
+  if constexpr (RING) {
+    // GEMM1 on bf16 256-row tiles: the weight (B) slices in 3 LDS slots and
+    // the activation (A) slices in 2, 160 KB in all, so the B loads run two
+    // slices ahead of the MFMAs and the A loads one.  Slots: B slice kt in
+    // slot kt % 3 (at 0, 32, 64 KB), A slice kt in slot kt % 2 (at 96 and
+    // 128 KB).  At iteration kt the slots of slice kt - 1 are free after the
+    // barrier; A slice kt + 1 is issued first, then B slice kt + 2, so that
+    // waiting until only the last LPB loads (B slice kt + 1) are outstanding
+    // finds both operands of slice kt landed.  Past the last slice the loads
+    // repeat it into a slot nobody reads, which keeps the loop free of
+    // branches.  Against two stages of both: prefill8192_ep8 GEMM1 -1%, and
+    // -3.5% with the buffer-resource loads.
+    auto a_at = [&](int kt) -> uint8_t* { return smem + (3 + (kt & 1)) * C::SLOT; };
+    auto b_at = [&](int sd) -> uint8_t* { return smem + sd * C::SLOT; };
+    auto issue_a = [&](int kt) {
+      const int kk = min(kt, nkt - 1);
+      if constexpr (BUF) issue_rows_buf<C::LPA, false>(a_at(kt), rsa, va, kk * SL, wave);
+      else issue_rows<C::LPA, false>(a_at(kt), ga, (size_t)kk * SL, wave);
+    };
+    auto issue_b = [&](int kt, int sd) {
+      const int kk = min(kt, nkt - 1);
+      if constexpr (BUF) issue_rows_buf<C::LPB, SW>(b_at(sd), rsb, vb, kk * SL, wave);
+      else issue_rows<C::LPB, SW>(b_at(sd), gb, (size_t)kk * SL, wave);
+    };
+    issue_a(0);
+    issue_b(0, 0);
+    issue_b(1, 1);
+    int sd = 0;                                    // kt % 3
+    if (full_tile) {
       for (int kt = 0; kt < nkt; ++kt) {
-        wait_vmcnt<0>();                           // this thread's loads of slice kt have landed
-        barrier_no_fence();                        // everyone's have, and the other stage is free
-        const uint8_t* la = smem + (kt & 1) * C::STAGE;
-        const uint8_t* lb = la + TM * SL;
+        wait_vmcnt<C::LPB>();                      // this thread's slice kt of both operands has landed
+        barrier_no_fence();                        // everyone's has, and slice kt - 1's slots are free
+        const uint8_t* la = a_at(kt);
+        const uint8_t* lb = b_at(sd);
+        const int sd2 = sd == 0 ? 2 : sd - 1;      // (kt + 2) % 3
         i32x4 fa[SL / 64][4], fb[SL / 64][NTW];
 #pragma unroll
         for (int fs = 0; fs < SL / 64; ++fs) {
-          if (fs == 1) tile_issue<DT, TM, false, SW>(smem, ga, gb, gs, min(kt + 1, nkt - 1), (kt + 1) & 1, wave);
+          if (fs == 1) {
+            issue_a(kt + 1);
+            issue_b(kt + 2, sd2);
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             fa[fs][i] = *reinterpret_cast<const i32x4*>(&la[C::off(wm * 64 + i * 16 + row, fs * 4 + grp)]);
@@ -234,40 +305,32 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
           for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < NTW; ++j) F::mma(acc[i][j], fa[fs][i], fb[fs][j]);
-        if constexpr (DT == MOE_BF16) {
-          constexpr int R = 4 + NTW;                 // fragment reads per half
-          constexpr int L = C::LPA + C::LPB;         // direct loads per slice
-          __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+        // the same order as the two-stage loop below
+        constexpr int R = 4 + NTW;                 // fragment reads per half
+        constexpr int L = C::LPA + C::LPB;         // direct loads per slice
+        __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
 #pragma unroll
-          for (int q = 0; q < L; ++q) {              // 1 load : 2 MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          }
-#pragma unroll
-          for (int q = 0; q < R; ++q) {              // 1 read : 2 MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 8 * NTW - 2 * R - 2 * L, 0);
+        for (int q = 0; q < L; ++q) {              // 1 load : 2 MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }
+#pragma unroll
+        for (int q = 0; q < R; ++q) {              // 1 read : 2 MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8 * NTW - 2 * R - 2 * L, 0);
+        sd = sd == 2 ? 0 : sd + 1;
       }
-    }
-  } else {
-    for (int kt = 0; kt < nkt; ++kt) {
-      const int st = kt % NST;
-      // wait until this thread's loads of slice kt have landed; later slices may stay in flight
-      if (NST > 2 && kt + 1 < nkt) {
-        if (FP8 && BLK) wait_vmcnt_dyn(C::LPA + C::LPB + (((kt + 1) & 3) == 0 ? 1 : 0));
-        else wait_vmcnt<C::PER_SLICE>();
-      } else {
-        wait_vmcnt<0>();
-      }
-      barrier_no_fence();                          // everyone's slice kt is in LDS; stage (kt-1) % NST is free
-      if (kt + NST - 1 < nkt) tile_issue<DT, TM, BLK, SW>(smem, ga, gb, gs, kt + NST - 1, (kt + NST - 1) % NST, wave);
-      const uint8_t* la = smem + st * C::STAGE;
-      const uint8_t* lb = la + TM * SL;
-      if constexpr (!FP8) {
-        // a group's last, partial tile: skip the M tiles without valid rows
+    } else {
+      // a group's last, partial tile: the same ring, skipping the M tiles without valid rows
+      for (int kt = 0; kt < nkt; ++kt) {
+        wait_vmcnt<C::LPB>();
+        barrier_no_fence();
+        const uint8_t* la = a_at(kt);
+        const uint8_t* lb = b_at(sd);
+        issue_a(kt + 1);
+        issue_b(kt + 2, sd == 0 ? 2 : sd - 1);
         if (mval > 0) {
 #pragma unroll
           for (int fs = 0; fs < SL / 64; ++fs) {
@@ -284,38 +347,139 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
               }
           }
         }
+        sd = sd == 2 ? 0 : sd + 1;
+      }
+    }
+  } else {
+    // slice kt into stage st: A rows, then B rows (and fp8 scales)
+    auto tissue = [&](int kt, int st) {
+      if constexpr (BUF) {
+        issue_rows_buf<C::LPA, false>(smem + st * C::STAGE, rsa, va, kt * SL, wave);
+        issue_rows_buf<C::LPB, SW>(smem + st * C::STAGE + TM * SL, rsb, vb, kt * SL, wave);
       } else {
-        // scales of slot s (A row s, then B row s - TM) for slice kt
-        constexpr int SS = BLK ? 4 : 1;   // floats between consecutive slots
-        const float* sp = BLK ? lds_s + (size_t)((kt >> 2) & 1) * C::NSC * 4 + (kt & 3) : lds_s + st * C::NSC;
-        auto scale = [&](int slot) -> float { return sp[slot * SS]; };
-        // groups of 4 column tiles keep the B fragments within the register budget
+        tile_issue<DT, TM, BLK, SW>(smem, ga, gb, gs, kt, st, wave);
+      }
+    };
 #pragma unroll
-        for (int jh = 0; jh < NTW / 4; ++jh) {
-          i32x4 fb0[4], fb1[4];
-          float sb[4];
+    for (int p = 0; p < NST - 1; ++p)
+      if (p < nkt) tissue(p, p);
+    if (full_tile) {
+      // Full tiles (all 64 rows of every M tile valid; bf16 and fp32 weights,
+      // two stages): one straight-line block per slice, so the scheduling
+      // hints below can order the fragment reads, the next slice's direct
+      // loads and the MFMAs.  The first half's reads go first; the next slice's
+      // loads are issued while they are in flight, spread over the first
+      // MFMAs, so a wave never stalls on a full load queue while it has MFMAs
+      // ready; the second half's reads are interleaved with the rest of the
+      // first half's MFMAs.  The last slice reloads itself into the free stage,
+      // which keeps the block free of branches.
+      if constexpr (!FP8) {
+        static_assert(NST == 2, "the full-tile loop assumes two stages");
+        for (int kt = 0; kt < nkt; ++kt) {
+          wait_vmcnt<0>();                           // this thread's loads of slice kt have landed
+          barrier_no_fence();                        // everyone's have, and the other stage is free
+          const uint8_t* la = smem + (kt & 1) * C::STAGE;
+          const uint8_t* lb = la + TM * SL;
+          i32x4 fa[SL / 64][4], fb[SL / 64][NTW];
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int n = wn * WN + (4 * jh + jj) * 16 + row;
-            fb0[jj] = *reinterpret_cast<const i32x4*>(&lb[C::off(n, grp)]);
-            fb1[jj] = *reinterpret_cast<const i32x4*>(&lb[C::off(n, 4 + grp)]);
-            sb[jj] = scale(TM + n);
+          for (int fs = 0; fs < SL / 64; ++fs) {
+            if (fs == 1) tissue(min(kt + 1, nkt - 1), (kt + 1) & 1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              fa[fs][i] = *reinterpret_cast<const i32x4*>(&la[C::off(wm * 64 + i * 16 + row, fs * 4 + grp)]);
+#pragma unroll
+            for (int j = 0; j < NTW; ++j)
+              fb[fs][j] = *reinterpret_cast<const i32x4*>(&lb[C::off(wn * WN + j * 16 + row, fs * 4 + grp)]);
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (i < mval) {
-              const int r = wm * 64 + i * 16 + row;
-              const i32x4 fa0 = *reinterpret_cast<const i32x4*>(&la[C::off(r, grp)]);
-              const i32x4 fa1 = *reinterpret_cast<const i32x4*>(&la[C::off(r, 4 + grp)]);
-              float sa[4];
+          for (int fs = 0; fs < SL / 64; ++fs)
 #pragma unroll
-              for (int q = 0; q < 4; ++q) sa[q] = scale(wm * 64 + i * 16 + 4 * grp + q);
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-              for (int jj = 0; jj < 4; ++jj) {
-                const f32x4 p = F::mma128(fa0, fa1, fb0[jj], fb1[jj]);
+              for (int j = 0; j < NTW; ++j) F::mma(acc[i][j], fa[fs][i], fb[fs][j]);
+          if constexpr (DT == MOE_BF16) {
+            constexpr int R = 4 + NTW;                 // fragment reads per half
+            constexpr int L = C::LPA + C::LPB;         // direct loads per slice
+            __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                  acc[i][4 * jh + jj][q] = fmaf(p[q], sa[q] * sb[jj], acc[i][4 * jh + jj][q]);
+            for (int q = 0; q < L; ++q) {              // 1 load : 2 MFMAs
+              __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < R; ++q) {              // 1 read : 2 MFMAs
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 8 * NTW - 2 * R - 2 * L, 0);
+          }
+        }
+      }
+    } else {
+      for (int kt = 0; kt < nkt; ++kt) {
+        const int st = kt % NST;
+        // wait until this thread's loads of slice kt have landed; later slices may stay in flight
+        if (NST > 2 && kt + 1 < nkt) {
+          if (FP8 && BLK) wait_vmcnt_dyn(C::LPA + C::LPB + (((kt + 1) & 3) == 0 ? 1 : 0));
+          else wait_vmcnt<C::PER_SLICE>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        barrier_no_fence();                          // everyone's slice kt is in LDS; stage (kt-1) % NST is free
+        if (kt + NST - 1 < nkt) tissue(kt + NST - 1, (kt + NST - 1) % NST);
+        const uint8_t* la = smem + st * C::STAGE;
+        const uint8_t* lb = la + TM * SL;
+        if constexpr (!FP8) {
+          // a group's last, partial tile: skip the M tiles without valid rows
+          if (mval > 0) {
+#pragma unroll
+            for (int fs = 0; fs < SL / 64; ++fs) {
+              i32x4 fb[NTW];
+#pragma unroll
+              for (int j = 0; j < NTW; ++j)
+                fb[j] = *reinterpret_cast<const i32x4*>(&lb[C::off(wn * WN + j * 16 + row, fs * 4 + grp)]);
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (i < mval) {
+                  const i32x4 fa = *reinterpret_cast<const i32x4*>(&la[C::off(wm * 64 + i * 16 + row, fs * 4 + grp)]);
+#pragma unroll
+                  for (int j = 0; j < NTW; ++j) F::mma(acc[i][j], fa, fb[j]);
+                }
+            }
+          }
+        } else {
+          // scales of slot s (A row s, then B row s - TM) for slice kt
+          constexpr int SS = BLK ? 4 : 1;   // floats between consecutive slots
+          const float* sp = BLK ? lds_s + (size_t)((kt >> 2) & 1) * C::NSC * 4 + (kt & 3) : lds_s + st * C::NSC;
+          auto scale = [&](int slot) -> float { return sp[slot * SS]; };
+          // groups of 4 column tiles keep the B fragments within the register budget
+#pragma unroll
+          for (int jh = 0; jh < NTW / 4; ++jh) {
+            i32x4 fb0[4], fb1[4];
+            float sb[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int n = wn * WN + (4 * jh + jj) * 16 + row;
+              fb0[jj] = *reinterpret_cast<const i32x4*>(&lb[C::off(n, grp)]);
+              fb1[jj] = *reinterpret_cast<const i32x4*>(&lb[C::off(n, 4 + grp)]);
+              sb[jj] = scale(TM + n);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (i < mval) {
+                const int r = wm * 64 + i * 16 + row;
+                const i32x4 fa0 = *reinterpret_cast<const i32x4*>(&la[C::off(r, grp)]);
+                const i32x4 fa1 = *reinterpret_cast<const i32x4*>(&la[C::off(r, 4 + grp)]);
+                float sa[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) sa[q] = scale(wm * 64 + i * 16 + 4 * grp + q);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                  const f32x4 p = F::mma128(fa0, fa1, fb0[jj], fb1[jj]);
+#pragma unroll
+                  for (int q = 0; q < 4; ++q)
+                    acc[i][4 * jh + jj][q] = fmaf(p[q], sa[q] * sb[jj], acc[i][4 * jh + jj][q]);
+                }
               }
             }
           }
@@ -323,7 +487,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
       }
     }
   }
-  wait_vmcnt<0>();   // the full-tile loop's last reload is still in flight
+  wait_vmcnt<0>();   // the loops' last reloads are still in flight
 
   // ---- epilogue: lane holds rows wm*64 + i*16 + 4*grp + q, columns wn*WN + j*16 + row
   if constexpr (DT != MOE_F32) {
@@ -408,13 +572,14 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
   }
 }
 
-template <int DT, int MODE, bool SHARED, int TM, bool BLK, bool SW>
+template <int DT, int MODE, bool SHARED, int TM, bool BLK, bool SW, bool BUF = false>
 hipError_t launch_fat(const char* name, unsigned grid, int ntn, const Args& a, hipStream_t st) {
   using C = TileCfg<DT, TM>;
-  hipError_t e = moe::ensure_dynamic_lds(reinterpret_cast<const void*>(&ffn_fat_kernel<DT, MODE, SHARED, TM, BLK, SW>),
-                                          (int)C::LDS_BYTES);
+  hipError_t e = moe::ensure_dynamic_lds(
+      reinterpret_cast<const void*>(&ffn_fat_kernel<DT, MODE, SHARED, TM, BLK, SW, BUF>), (int)C::LDS_BYTES);
   if (e != hipSuccess) return e;
-  MOE_LAUNCH(name, (ffn_fat_kernel<DT, MODE, SHARED, TM, BLK, SW>), dim3(grid), dim3(512), C::LDS_BYTES, st, a, ntn);
+  MOE_LAUNCH(name, (ffn_fat_kernel<DT, MODE, SHARED, TM, BLK, SW, BUF>), dim3(grid), dim3(512), C::LDS_BYTES, st, a,
+             ntn);
   return hipGetLastError();
 }
 
@@ -433,8 +598,14 @@ hipError_t launch_tiled(int mode, bool shared, int tm, bool stream_w, unsigned g
   // fp8 scale blocks of 4 slices need the slice count K / 128 to be a multiple of 4
   const bool blk = DT == MOE_FP8_E4M3 && (((mode == 1 ? a.H : a.I) / 128) & 3) == 0;
   constexpr bool FP8 = DT == MOE_FP8_E4M3;
+  // buffer-resource loads (bf16 GEMM1 256-row tiles) need 32-bit offsets
+  // into the activations and into one expert's weights
+  const size_t act_bytes = mode == 1 ? (size_t)a.T * a.H * 2 : (size_t)(a.P + a.T) * a.I * 2;   // x, or h
+  const bool buf = DT == MOE_BF16 && tm == 256 && act_bytes <= 0xffffffffu &&
+                   (size_t)2 * a.I * a.H * 2 <= 0xffffffffu;
 #define MOE_TLB(M, S, TMV, SWV) \
   (FP8 && blk ? launch_fat<DT, M, S, TMV, FP8, SWV>(name, grid, ntn, a, st) \
+   : buf      ? launch_fat<DT, M, S, TMV, false, SWV, DT == MOE_BF16 && TMV == 256>(name, grid, ntn, a, st) \
               : launch_fat<DT, M, S, TMV, false, SWV>(name, grid, ntn, a, st))
   // the shared expert's weights are read by every row tile: always cached
 #define MOE_TL(M, TMV) \
