@@ -118,6 +118,8 @@ __device__ __forceinline__ void tile_issue(uint8_t* smem, const uint8_t* const* 
 }
 
 // One operand's direct loads of a slice (LP per thread) into an LDS slot.
+template <bool V> struct BoolC { static constexpr bool value = V; };
+
 template <int LP, bool NT>
 __device__ __forceinline__ void issue_rows(uint8_t* slot, const uint8_t* const* g, size_t off, int wave) {
   uint8_t* d = slot + wave * LP * 1024;
@@ -218,7 +220,8 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
   // matrix and one expert's weights below 4 GB) the direct loads go through
   // buffer resources instead: the A base is the activation matrix, the B
   // base this group's weights, with per-lane 32-bit offsets.
-  static_assert(!BUF || (DT == MOE_BF16 && TM == 256), "buffer loads: bf16 256-row tiles");
+  static_assert(!BUF || (DT == MOE_BF16 && TM == 256) || (FP8 && TM == 128),
+                "buffer loads: bf16 256-row tiles and fp8 128-row tiles");
   const __amdgpu_buffer_rsrc_t rsa =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(asrc), 0, (int)0xffffffffu, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsb =
@@ -232,12 +235,23 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
   }
   // fp8 scales: scale slot s = 64 * wave + lane of each stage holds the
   // slice's scale of A row s (s < TM), of B row s - TM (s < TM + kTN), or a
-  // copy of B row 0's (the remaining slots, never read).
+  // copy of B row 0's (the remaining slots, never read).  A wave's slots are
+  // all A rows or all B rows, so with BUF its scale resource is one array.
   const float* gs = nullptr;
+  const float* sbase = nullptr;
+  uint32_t vs = 0;
   if constexpr (FP8) {
     const int sidx = 64 * wave + lane;
-    if (sidx < TM) gs = (MODE == 1 ? a.a1s : a.a2s) + (size_t)a_src(sidx) * nkb;
+    const float* as = MODE == 1 ? a.a1s : a.a2s;
+    if (sidx < TM) gs = as + (size_t)a_src(sidx) * nkb;
     else gs = wsbase + (size_t)(b_wrow(sidx < TM + kTN ? sidx - TM : 0) >> a.wsr_shift) * nkb;
+    if constexpr (BUF) {
+      const uint64_t sb = reinterpret_cast<uint64_t>(64 * wave < TM ? as : wsbase);
+      sbase = reinterpret_cast<const float*>(
+          ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(sb >> 32)) << 32) |
+          (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sb));
+      vs = (uint32_t)((gs - sbase) * sizeof(float));
+    }
   }
 
   f32x4 acc[4][NTW];
@@ -356,6 +370,21 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
       if constexpr (BUF) {
         issue_rows_buf<C::LPA, false>(smem + st * C::STAGE, rsa, va, kt * SL, wave);
         issue_rows_buf<C::LPB, SW>(smem + st * C::STAGE + TM * SL, rsb, vb, kt * SL, wave);
+        if constexpr (FP8) {   // the scale loads of tile_issue, from the wave's scale resource
+          const __amdgpu_buffer_rsrc_t rss =
+              __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sbase), 0, (int)0xffffffffu, 0x00020000);
+          uint8_t* sc = smem + C::NST * C::STAGE;
+          if constexpr (BLK) {
+            if ((kt & 3) == 0)
+              __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                  rss, (__attribute__((address_space(3))) void*)(sc + (((kt >> 2) & 1) * C::NSC + wave * 64) * 16), 16,
+                  (int)vs, kt * 4, 0, 0);
+          } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rss, (__attribute__((address_space(3))) void*)(sc + (st * C::NSC + wave * 64) * 4), 4, (int)vs, kt * 4,
+                0, 0);
+          }
+        }
       } else {
         tile_issue<DT, TM, BLK, SW>(smem, ga, gb, gs, kt, st, wave);
       }
@@ -452,37 +481,48 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
           constexpr int SS = BLK ? 4 : 1;   // floats between consecutive slots
           const float* sp = BLK ? lds_s + (size_t)((kt >> 2) & 1) * C::NSC * 4 + (kt & 3) : lds_s + st * C::NSC;
           auto scale = [&](int slot) -> float { return sp[slot * SS]; };
-          // groups of 4 column tiles keep the B fragments within the register budget
-#pragma unroll
-          for (int jh = 0; jh < NTW / 4; ++jh) {
-            i32x4 fb0[4], fb1[4];
-            float sb[4];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const int n = wn * WN + (4 * jh + jj) * 16 + row;
-              fb0[jj] = *reinterpret_cast<const i32x4*>(&lb[C::off(n, grp)]);
-              fb1[jj] = *reinterpret_cast<const i32x4*>(&lb[C::off(n, 4 + grp)]);
-              sb[jj] = scale(TM + n);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              if (i < mval) {
-                const int r = wm * 64 + i * 16 + row;
-                const i32x4 fa0 = *reinterpret_cast<const i32x4*>(&la[C::off(r, grp)]);
-                const i32x4 fa1 = *reinterpret_cast<const i32x4*>(&la[C::off(r, 4 + grp)]);
-                float sa[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) sa[q] = scale(wm * 64 + i * 16 + 4 * grp + q);
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                  const f32x4 p = F::mma128(fa0, fa1, fb0[jj], fb1[jj]);
-#pragma unroll
-                  for (int q = 0; q < 4; ++q)
-                    acc[i][4 * jh + jj][q] = fmaf(p[q], sa[q] * sb[jj], acc[i][4 * jh + jj][q]);
-                }
-              }
-            }
+          // groups of 4 column tiles keep the B fragments within the register
+          // budget; on 128-row tiles a wave whose 4 M tiles all hold valid rows
+          // takes a copy without the per-tile guards, which the compiler can
+          // software-pipeline (256-row tiles, with 8 column tiles per wave, sit
+          // at the register limit and keep only the guarded copy)
+#define MOE_FP8_MTILES(GUARD) \
+          _Pragma("unroll") \
+          for (int jh = 0; jh < NTW / 4; ++jh) { \
+            i32x4 fb0[4], fb1[4]; \
+            float sb[4]; \
+            _Pragma("unroll") \
+            for (int jj = 0; jj < 4; ++jj) { \
+              const int n = wn * WN + (4 * jh + jj) * 16 + row; \
+              fb0[jj] = *reinterpret_cast<const i32x4*>(&lb[C::off(n, grp)]); \
+              fb1[jj] = *reinterpret_cast<const i32x4*>(&lb[C::off(n, 4 + grp)]); \
+              sb[jj] = scale(TM + n); \
+            } \
+            _Pragma("unroll") \
+            for (int i = 0; i < 4; ++i) { \
+              if (GUARD) { \
+                const int r = wm * 64 + i * 16 + row; \
+                const i32x4 fa0 = *reinterpret_cast<const i32x4*>(&la[C::off(r, grp)]); \
+                const i32x4 fa1 = *reinterpret_cast<const i32x4*>(&la[C::off(r, 4 + grp)]); \
+                float sa[4]; \
+                _Pragma("unroll") \
+                for (int q = 0; q < 4; ++q) sa[q] = scale(wm * 64 + i * 16 + 4 * grp + q); \
+                _Pragma("unroll") \
+                for (int jj = 0; jj < 4; ++jj) { \
+                  const f32x4 p = F::mma128(fa0, fa1, fb0[jj], fb1[jj]); \
+                  _Pragma("unroll") \
+                  for (int q = 0; q < 4; ++q) \
+                    acc[i][4 * jh + jj][q] = fmaf(p[q], sa[q] * sb[jj], acc[i][4 * jh + jj][q]); \
+                } \
+              } \
+            } \
           }
+          if (TM == 128 && mval == 4) {
+            MOE_FP8_MTILES(true)
+          } else {
+            MOE_FP8_MTILES(i < mval)
+          }
+#undef MOE_FP8_MTILES
         }
       }
     }
@@ -598,15 +638,20 @@ hipError_t launch_tiled(int mode, bool shared, int tm, bool stream_w, unsigned g
   // fp8 scale blocks of 4 slices need the slice count K / 128 to be a multiple of 4
   const bool blk = DT == MOE_FP8_E4M3 && (((mode == 1 ? a.H : a.I) / 128) & 3) == 0;
   constexpr bool FP8 = DT == MOE_FP8_E4M3;
-  // buffer-resource loads (bf16 GEMM1 256-row tiles) need 32-bit offsets
-  // into the activations and into one expert's weights
-  const size_t act_bytes = mode == 1 ? (size_t)a.T * a.H * 2 : (size_t)(a.P + a.T) * a.I * 2;   // x, or h
-  const bool buf = DT == MOE_BF16 && tm == 256 && act_bytes <= 0xffffffffu &&
-                   (size_t)2 * a.I * a.H * 2 <= 0xffffffffu;
+  // buffer-resource loads (bf16 256-row tiles, fp8 tiles) need 32-bit
+  // offsets into the activations (x, or h; fp8: their codes and scales) and
+  // into one expert's weights
+  const size_t esz = DT == MOE_BF16 ? 2 : 1;
+  const size_t act_bytes = mode == 1 ? (size_t)a.T * a.H * esz : (size_t)(a.P + a.T) * a.I * esz;
+  // (fp8 256-row tiles sit at the register limit: the buffer form spills there)
+  const bool buf = (DT == MOE_BF16 ? tm == 256 : FP8 && tm == 128) && act_bytes <= 0xffffffffu &&
+                   (size_t)2 * a.I * a.H * esz <= 0xffffffffu;
+#define MOE_BUFV(TMV) ((DT == MOE_BF16 && TMV == 256) || (FP8 && TMV == 128))
 #define MOE_TLB(M, S, TMV, SWV) \
-  (FP8 && blk ? launch_fat<DT, M, S, TMV, FP8, SWV>(name, grid, ntn, a, st) \
-   : buf      ? launch_fat<DT, M, S, TMV, false, SWV, DT == MOE_BF16 && TMV == 256>(name, grid, ntn, a, st) \
-              : launch_fat<DT, M, S, TMV, false, SWV>(name, grid, ntn, a, st))
+  (buf ? (FP8 && blk ? launch_fat<DT, M, S, TMV, FP8, SWV, MOE_BUFV(TMV)>(name, grid, ntn, a, st) \
+                     : launch_fat<DT, M, S, TMV, false, SWV, MOE_BUFV(TMV)>(name, grid, ntn, a, st)) \
+       : (FP8 && blk ? launch_fat<DT, M, S, TMV, FP8, SWV>(name, grid, ntn, a, st) \
+                     : launch_fat<DT, M, S, TMV, false, SWV>(name, grid, ntn, a, st)))
   // the shared expert's weights are read by every row tile: always cached
 #define MOE_TL(M, TMV) \
   (shared ? MOE_TLB(M, true, TMV, false) : stream_w ? MOE_TLB(M, false, TMV, true) : MOE_TLB(M, false, TMV, false))
@@ -615,6 +660,7 @@ hipError_t launch_tiled(int mode, bool shared, int tm, bool stream_w, unsigned g
   return hipErrorInvalidValue;
 #undef MOE_TL
 #undef MOE_TLB
+#undef MOE_BUFV
 }
 
 template hipError_t launch_tiled<MOE_F32>(int, bool, int, bool, unsigned, int, const Args&, hipStream_t);
