@@ -215,7 +215,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int32_t* __r
     __syncthreads();
   }
   if constexpr (PLAN) {
-    __shared__ int wt[5 * 8];
+    __shared__ int wt[moe::ffn::kPlanLds];
     int m = 0;   // group tid's rows: the histogram, or all T tokens for the shared expert
     if (tid < pa.G) m = tid < E ? hist[tid] : pa.T;
     moe::ffn::build_plan(pa, m, wt);

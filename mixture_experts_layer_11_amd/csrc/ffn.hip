@@ -44,7 +44,7 @@ using namespace moe::ffn;
 // ------------------------------------------------------------------ plan
 
 __global__ __launch_bounds__(512) void ffn_plan_kernel(Args a) {
-  __shared__ int wt[5 * 8];
+  __shared__ int wt[moe::ffn::kPlanLds];
   const int g = threadIdx.x;
   int m = 0;
   if (g < a.G) m = g < a.E ? a.offsets[g + 1] - a.offsets[g] : a.T;

@@ -10,8 +10,11 @@
 namespace moe {
 namespace ffn {
 
+// LDS ints build_plan needs from its caller.
+constexpr int kPlanLds = 5 * 8 + 2 * 8 + 3 * 512;
+
 // Thread g (any block of at least 512 threads; all threads must call it)
-// owns group g with m rows (0 for g >= G).  wt holds 5 x 8 ints of LDS.
+// owns group g with m rows (0 for g >= G).  wt holds kPlanLds ints of LDS.
 // Skinny class: 0 for 1..8 rows, 1 for 9..16, 2 for 17..32; larger groups
 // take floor(m / 256) full tiles, and their last m mod 256 rows one more
 // 256-row tile, or with mid_rest one 128-row tile if they are at most 128
@@ -20,7 +23,10 @@ namespace ffn {
 // there every group, the shared expert included, enters the <= 8-row list
 // as one or two 8-row halves, so the other lists stay empty.  The five
 // per-group counts are prefix-summed over groups 0..g in each wave with
-// shuffles, then across the 8 waves through wt (one barrier).
+// shuffles, then across the 8 waves through wt (one barrier).  The two tile
+// lists run in order of decreasing group size (equal sizes by group), so a
+// launch ends with the smallest groups' tiles and its last workgroups are
+// short ones; a group's row tiles stay consecutive.
 __device__ inline void build_plan(const PlanArgs& a, int m, int* wt) {
   const int g = threadIdx.x, lane = g & 63, wave = g >> 6;
   const bool act = g < 512;
@@ -48,27 +54,77 @@ __device__ inline void build_plan(const PlanArgs& a, int m, int* wt) {
     for (int c = 0; c < 5; ++c) wt[c * 8 + wave] = v[c];
   }
   __syncthreads();
-  if (!act) return;
-  for (int w = 0; w < wave; ++w) {
-#pragma unroll
-    for (int c = 0; c < 5; ++c) v[c] += wt[c * 8 + w];
-  }
-  // v[c] now sums groups 0..g
   int32_t* plan = a.plan;
-  if (g == 511) {
+  if (act) {   // every thread of the block reaches the barriers below
+    for (int w = 0; w < wave; ++w) {
 #pragma unroll
-    for (int c = 0; c < 5; ++c) plan[c] = v[c];
+      for (int c = 0; c < 5; ++c) v[c] += wt[c * 8 + w];
+    }
+    // v[c] now sums groups 0..g
+    if (g == 511) {
+#pragma unroll
+      for (int c = 0; c < 5; ++c) plan[c] = v[c];
+    }
+    const int send = cls == 0 ? v[0] : cls == 1 ? v[1] : v[2];   // end of this group's entries in its list
+    for (int h = 0; h < nent; ++h) plan[kPlanHead + cls * 2 * a.G + send - nent + h] = g | (h << 16);
   }
-  const int send = cls == 0 ? v[0] : cls == 1 ? v[1] : v[2];   // end of this group's entries in its list
-  for (int h = 0; h < nent; ++h) plan[kPlanHead + cls * 2 * a.G + send - nent + h] = g | (h << 16);
+
+  // Tile lists by decreasing group size: rank r of each tiled group, its
+  // tile counts at position r, a prefix sum over positions, and back.
+  int* wp = wt + 5 * 8;        // [2][8] cross-wave sums
+  int* ms = wp + 2 * 8;        // [512] rows of tiled groups (-1: not tiled)
+  int* ct = ms + 512;          // [512] 256-row tiles at position r, then their start
+  int* cm = ct + 512;          // [512] 128-row tiles at position r, then their start
+  const bool ranked = act && (tiles > 0 || mids > 0);
+  if (act) {
+    ms[g] = ranked ? m : -1;
+    ct[g] = 0;
+    cm[g] = 0;
+  }
+  __syncthreads();
+  int r = 0;
+  if (ranked) {
+    for (int h = 0; h < a.G; ++h) {
+      const int mh = ms[h];
+      r += mh > m || (mh == m && h < g);
+    }
+    ct[r] = tiles;
+    cm[r] = mids;
+  }
+  __syncthreads();
+  int u[2] = {act ? ct[g] : 0, act ? cm[g] : 0};   // thread g now stands for position g
+  const int own[2] = {u[0], u[1]};
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int w = __shfl_up(u[c], d, 64);
+      if (lane >= d) u[c] += w;
+    }
+  }
+  if (act && lane == 63) {
+    wp[wave] = u[0];
+    wp[8 + wave] = u[1];
+  }
+  __syncthreads();
+  if (act) {
+    for (int w = 0; w < wave; ++w) {
+      u[0] += wp[w];
+      u[1] += wp[8 + w];
+    }
+    ct[g] = u[0] - own[0];     // start of position g's tiles (position g read its own count above)
+    cm[g] = u[1] - own[1];
+  }
+  __syncthreads();
+  if (!ranked) return;
   int32_t* fat = plan + kPlanHead + 6 * a.G;
-  const int t0 = v[3] - tiles;
+  const int t0 = ct[r];
   for (int i = 0; i < tiles; ++i) {
     fat[2 * (t0 + i)] = g;
     fat[2 * (t0 + i) + 1] = i * kTileRows;
   }
   int32_t* mid = fat + 2 * a.fat_cap;
-  const int m0 = v[4] - mids;
+  const int m0 = cm[r];
   for (int i = 0; i < mids; ++i) {
     mid[2 * (m0 + i)] = g;
     mid[2 * (m0 + i) + 1] = (m / kTileRows) * kTileRows + i * kMidRows;
