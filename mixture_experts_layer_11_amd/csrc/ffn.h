@@ -147,6 +147,24 @@ constexpr int kShKS = 4;   // waves splitting K in the skinny shared expert's wo
 constexpr int kTM = 256;   // tiled GEMM: tile rows (tokens)
 constexpr int kTN = 256;   // tiled GEMM: tile columns (weight rows; GEMM1: 128 gate + 128 up)
 
+// Tile columns of the tiled GEMM with TM-row tiles: kTN, except for the fp8
+// shared expert's 256-row GEMM1 tiles, which take 128 columns (64 gate + 64
+// up): three LDS stages and 64 accumulators per wave then fit, which suits
+// its full, compute-bound tiles over K = H (clustered2048_fp8, alone: 173 ->
+// 107 us).  Its GEMM2 (K = I, 16 slices) measured 60 -> 65 us that way and
+// keeps kTN.  The routed fp8 256-row tiles are partial (129..255 rows left
+// of a group) and bound by their loads, which the narrower tiles' twice
+// re-read activation rows make slower (GEMM1 439 -> 461 us): they keep kTN.
+__host__ __device__ constexpr int tile_cols(int dt, int mode, int tm, bool shared) {
+  return dt == MOE_FP8_E4M3 && mode == 1 && tm == 256 && shared ? 128 : kTN;
+}
+// Column tiles per row tile: GEMM1 covers I h-columns (half of a tile's
+// weight rows are gate rows), GEMM2 the H output columns.
+inline int tile_ntn(int dt, int mode, int tm, bool shared, int I, int H) {
+  const int tn = tile_cols(dt, mode, tm, shared);
+  return mode == 1 ? (I + tn / 2 - 1) / (tn / 2) : (H + tn - 1) / tn;
+}
+
 // Launchers (explicitly instantiated for MOE_F32, MOE_BF16, MOE_FP8_E4M3).
 // mode 1 = gate/up GEMM with SwiGLU, mode 2 = down GEMM.
 // The routed skinny classes (1..8, 9..16, 17..32 rows) in one launch of `grid` workgroups.
@@ -158,12 +176,12 @@ hipError_t launch_shared_skinny(int mode, int T, const Args& a, hipStream_t st);
 // Tiled grouped GEMM with tm-row tiles (256 or 128): the plan's list of that
 // size (shared = false) or the shared expert's tiles of that size (shared =
 // true: floor(T / 256) full tiles, or ceil((T mod 256) / 128) tiles for the
-// rest); ntn column tiles each.  stream_w (routed tiles only) loads the
-// weight slices nontemporally, for when each group's weights are read by
-// about one row tile.
+// rest), for `tiles` row tiles of tile_ntn column tiles each (the routed
+// lists' row tiles beyond the plan's count exit at once).  stream_w (routed
+// tiles only) loads the weight slices nontemporally, for when each group's
+// weights are read by about one row tile.
 template <int DT>
-hipError_t launch_tiled(int mode, bool shared, int tm, bool stream_w, unsigned grid, int ntn, const Args& a,
-                        hipStream_t st);
+hipError_t launch_tiled(int mode, bool shared, int tm, bool stream_w, int tiles, const Args& a, hipStream_t st);
 
 }  // namespace ffn
 }  // namespace moe

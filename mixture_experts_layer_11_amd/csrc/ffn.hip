@@ -66,12 +66,11 @@ hipError_t run_shared(const moe_cfg& c, const Args& a, hipStream_t st) {
     if (c.T <= kSkinnyRows) {
       e = launch_shared_skinny<DT>(mode, c.T, a, st);
     } else {
-      const int ntn = mode == 1 ? moe::ceil_div(c.I, kTN / 2) : moe::ceil_div(c.H, kTN);
       const int full = a.mid_rest ? c.T / kTileRows : moe::ceil_div(c.T, kTileRows);
       const int rest = a.mid_rest ? moe::ceil_div(c.T % kTileRows, kMidRows) : 0;
       e = hipSuccess;
-      if (full > 0) e = launch_tiled<DT>(mode, true, kTileRows, false, (unsigned)(full * ntn), ntn, a, st);
-      if (e == hipSuccess && rest > 0) e = launch_tiled<DT>(mode, true, kMidRows, false, (unsigned)(rest * ntn), ntn, a, st);
+      if (full > 0) e = launch_tiled<DT>(mode, true, kTileRows, false, full, a, st);
+      if (e == hipSuccess && rest > 0) e = launch_tiled<DT>(mode, true, kMidRows, false, rest, a, st);
     }
     if (e != hipSuccess) return e;
   }
@@ -156,19 +155,18 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st, bool plan
       if ((e = hipStreamWaitEvent(ts.stream, ts.fork, 0)) != hipSuccess) return e;
       tst = ts.stream;
     }
-    const int ntn = mode == 1 ? moe::ceil_div(c.I, kTN / 2) : moe::ceil_div(c.H, kTN);
     if (both) {   // tiles first, so their workgroups are queued before the streaming ones
-      if (max_fat > 0 && (e = launch_tiled<DT>(mode, false, kTileRows, stream_w, (unsigned)(max_fat * ntn), ntn, a, tst)) != hipSuccess)
+      if (max_fat > 0 && (e = launch_tiled<DT>(mode, false, kTileRows, stream_w, max_fat, a, tst)) != hipSuccess)
         return e;
-      if (max_mid > 0 && (e = launch_tiled<DT>(mode, false, kMidRows, stream_w, (unsigned)(max_mid * ntn), ntn, a, tst)) != hipSuccess)
+      if (max_mid > 0 && (e = launch_tiled<DT>(mode, false, kMidRows, stream_w, max_mid, a, tst)) != hipSuccess)
         return e;
     }
     if (bands > 0 && (e = launch_skinny<DT>(mode, (unsigned)(8 * bands), a, st)) != hipSuccess) return e;
     if ((e = hook(2 * mode - 1)) != hipSuccess) return e;
     if (!both) {
-      if (max_fat > 0 && (e = launch_tiled<DT>(mode, false, kTileRows, stream_w, (unsigned)(max_fat * ntn), ntn, a, st)) != hipSuccess)
+      if (max_fat > 0 && (e = launch_tiled<DT>(mode, false, kTileRows, stream_w, max_fat, a, st)) != hipSuccess)
         return e;
-      if (max_mid > 0 && (e = launch_tiled<DT>(mode, false, kMidRows, stream_w, (unsigned)(max_mid * ntn), ntn, a, st)) != hipSuccess)
+      if (max_mid > 0 && (e = launch_tiled<DT>(mode, false, kMidRows, stream_w, max_mid, a, st)) != hipSuccess)
         return e;
     } else {
       if ((e = hipEventRecord(ts.join, ts.stream)) != hipSuccess) return e;
@@ -203,6 +201,7 @@ hipError_t run_ffn(const moe_cfg& c, const Args& a, hipStream_t st, bool planned
   moe::SideStream side;
   hipError_t e = moe::side_stream(&side);
   if (e != hipSuccess) return e;
+  // (in units of 256 x 256 output tiles, whatever the kernels' tile widths)
   const long long shared_tiles1 =
       (long long)(a.mid_rest ? c.T / kTileRows + moe::ceil_div(c.T % kTileRows, kMidRows) : moe::ceil_div(c.T, kTileRows)) *
       moe::ceil_div(c.I, kTN / 2);

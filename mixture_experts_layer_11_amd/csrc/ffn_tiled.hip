@@ -13,13 +13,17 @@ namespace {
 
 using namespace moe::ffn;
 
-// Output tiles of TM x kTN per workgroup of 8 waves, with 16x16 MFMAs:
+// Output tiles of TM x TN per workgroup of 8 waves, with 16x16 MFMAs:
 //   TM = 256: 4 waves along M x 2 along N, 64 x 128 each, 2 LDS stages
-//             (groups of 256 rows and more: the prefill regime);
+//             (groups of 256 rows and more: the prefill regime; fp8: the
+//             last 129..255 rows of a group);
+//   TM = 256, TN = 128 (the fp8 shared expert's GEMM1): 64 x 64 per wave,
+//             3 LDS stages;
 //   TM = 128: 2 waves along M x 4 along N, 64 x 64 each, 3 LDS stages
-//             (fp8 weights: the last 1..255 rows of a group, and groups of
-//             33..255 rows).
-// K advances in 128-byte slices: each slice of the TM A rows and the kTN B
+//             (fp8 weights: the last 1..128 rows of a group).
+// fp8 256-row tiles give wave wm the 16-row M tiles wm, wm + 4, ...: the
+// SIMDs then share a partial tile's valid rows evenly.
+// K advances in 128-byte slices: each slice of the TM A rows and the TN B
 // rows goes global -> LDS directly (16 bytes per lane per instruction) into
 // a ring of NST stages, so the loads run NST - 1 slices ahead of the MFMAs
 // and there is one barrier per slice.  With 128-row tiles a stage is 48 KB,
@@ -40,19 +44,31 @@ using namespace moe::ffn;
 // counting waits for every LDS fragment read before each first use, with
 // the buffer form it waits for exactly the reads each MFMA needs.
 
-template <int DT, int TM> struct TileCfg {
+template <int DT, int TM, int TN_ = kTN> struct TileCfg {
+  static constexpr int TN = TN_;                              // tile columns
   static constexpr int SL = 128;                              // bytes of K per slice and row
-  static constexpr int NST = TM == 256 ? 2 : 3;               // LDS stages
+  static constexpr int NST = TM == 256 && TN == 256 ? 2 : 3;  // LDS stages
   static constexpr int CPR = SL / 16;                         // 16-byte chunks per row
   static constexpr int RPI = 1024 / SL;                       // rows one wave instruction fills
   static constexpr int WAVES_M = TM / 64;                     // waves along M (64 rows each)
   static constexpr int WAVES_N = 8 / WAVES_M;                 // waves along N
-  static constexpr int WN = kTN / WAVES_N;                    // columns per wave
+  static constexpr int WN = TN / WAVES_N;                     // columns per wave
   static constexpr int NTW = WN / 16;                         // 16-column MFMA tiles per wave
   static constexpr int LPA = TM * SL / 1024 / 8;              // A loads per thread per slice
-  static constexpr int LPB = kTN * SL / 1024 / 8;             // B loads per thread per slice
+  static constexpr int LPB = TN * SL / 1024 / 8;              // B loads per thread per slice
   static constexpr int NSC = 512;                             // fp8 scale slots per stage: 8 waves x 64
-  static constexpr int STAGE = (TM + kTN) * SL;               // tile bytes per stage (A then B)
+  static constexpr int STAGE = (TM + TN) * SL;                // tile bytes per stage (A then B)
+  // fp8 256-row tiles: wave wm takes the 16-row M tiles wm, wm + 4, wm + 8,
+  // wm + 12 instead of 64 consecutive rows, so that the 4 SIMDs (SIMD s runs
+  // waves s and s + 4) share a partial tile's valid rows evenly.
+  static constexpr bool ILV = DT == MOE_FP8_E4M3 && TM == 256;
+  // first row of the wave's i-th M tile
+  __device__ static __forceinline__ int mrow(int wm, int i) { return ILV ? (i * WAVES_M + wm) * 16 : wm * 64 + i * 16; }
+  // the wave's M tiles holding any of the tile's valid rows (they come first in i)
+  __device__ static __forceinline__ int mvalid(int wm, int rows) {
+    if constexpr (ILV) return min(4, max(0, (((rows + 15) >> 4) - wm + WAVES_M - 1) / WAVES_M));
+    else return min(4, max(0, (rows - wm * 64 + 15) >> 4));
+  }
   static constexpr int PER_SLICE = LPA + LPB + (DT == MOE_FP8_E4M3 ? 1 : 0);   // loads per thread per slice
   // fp8 scale area: per-slice scales [NST][NSC] floats, or, when the slice
   // count is a multiple of 4, two blocks of [NSC][4 slices] floats
@@ -69,7 +85,7 @@ template <int DT, int TM> struct TileCfg {
   // bf16 256-row tiles of GEMM1 keep the weight slices 3 deep and the
   // activation slices 2 deep (the ring below): 5 slots of 32 KB
   static constexpr bool RING_OK = DT == MOE_BF16 && TM == 256;
-  static constexpr int SLOT = TM * SL;                        // one operand's slice (TM == kTN)
+  static constexpr int SLOT = TM * SL;                        // one operand's slice (TM == TN)
   static constexpr size_t MAIN_BYTES =
       RING_OK ? (size_t)5 * SLOT : (size_t)NST * STAGE + (DT == MOE_FP8_E4M3 ? SCB : 0);
   static constexpr size_t LDS_BYTES = MAIN_BYTES > EPI_BYTES ? MAIN_BYTES : EPI_BYTES;
@@ -92,15 +108,18 @@ __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::
 // scales lie in 512 different rows); else 4 bytes per slice into stage st.
 // With SW the weight slices are loaded nontemporally: each is read by about
 // one row tile, so it should not displace what other workgroups share.
-template <int DT, int TM, bool BLK, bool SW>
+// Only the wave's first na A-row loads are issued (the others would fetch
+// the clamped copies of a partial tile's last row).
+template <int DT, int TM, int TN, bool BLK, bool SW>
 __device__ __forceinline__ void tile_issue(uint8_t* smem, const uint8_t* const* ga, const uint8_t* const* gb,
-                                           const float* gs, int kt, int st, int wave) {
-  using C = TileCfg<DT, TM>;
+                                           const float* gs, int kt, int st, int wave, int na) {
+  using C = TileCfg<DT, TM, TN>;
   const size_t off = (size_t)kt * C::SL;
   uint8_t* la = smem + st * C::STAGE + wave * C::LPA * 1024;
   uint8_t* lb = smem + st * C::STAGE + TM * C::SL + wave * C::LPB * 1024;
 #pragma unroll
-  for (int i = 0; i < C::LPA; ++i) __builtin_amdgcn_global_load_lds(ga[i] + off, la + i * 1024, 16, 0, 0);
+  for (int i = 0; i < C::LPA; ++i)
+    if (i < na) __builtin_amdgcn_global_load_lds(ga[i] + off, la + i * 1024, 16, 0, 0);
 #pragma unroll
   for (int i = 0; i < C::LPB; ++i) __builtin_amdgcn_global_load_lds(gb[i] + off, lb + i * 1024, 16, 0, SW ? 2 : 0);   // 2: nontemporal
   if constexpr (DT == MOE_FP8_E4M3) {
@@ -133,18 +152,19 @@ __device__ __forceinline__ void issue_rows(uint8_t* slot, const uint8_t* const* 
 // pending it waits for every outstanding LDS read before each use.
 template <int LP, bool NT>
 __device__ __forceinline__ void issue_rows_buf(uint8_t* slot, __amdgpu_buffer_rsrc_t rs, const uint32_t* voff,
-                                               int soff, int wave) {
+                                               int soff, int wave, int n = LP) {
   uint8_t* d = slot + wave * LP * 1024;
 #pragma unroll
   for (int i = 0; i < LP; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(d + i * 1024), 16,
-                                             (int)voff[i], soff, 0, NT ? 2 : 0);
+    if (i < n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(d + i * 1024), 16,
+                                               (int)voff[i], soff, 0, NT ? 2 : 0);
 }
 
 template <int DT, int MODE, bool SHARED, int TM, bool BLK, bool SW, bool BUF>
 __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
   using F = Frag<DT>;
-  using C = TileCfg<DT, TM>;
+  using C = TileCfg<DT, TM, tile_cols(DT, MODE, TM, SHARED)>;
   constexpr bool FP8 = DT == MOE_FP8_E4M3;
   constexpr int SL = C::SL, NST = C::NST, RPI = C::RPI, NTW = C::NTW, WN = C::WN;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -190,10 +210,10 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
   auto b_wrow = [&](int n) -> int {
     if (MODE == 1) {
       const int blk = n >> 4;          // 16-row blocks alternate gate, up
-      const int hc = min(nt * (kTN / 2) + (blk >> 1) * 16 + (n & 15), a.I - 1);
+      const int hc = min(nt * (C::TN / 2) + (blk >> 1) * 16 + (n & 15), a.I - 1);
       return ((blk & 1) ? a.I : 0) + hc;
     }
-    return min(nt * kTN + n, a.H - 1);
+    return min(nt * C::TN + n, a.H - 1);
   };
   // Source row of A row r (clamped: padded rows recompute a valid row, never stored).
   auto a_src = [&](int r) -> int {
@@ -220,8 +240,8 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
   // matrix and one expert's weights below 4 GB) the direct loads go through
   // buffer resources instead: the A base is the activation matrix, the B
   // base this group's weights, with per-lane 32-bit offsets.
-  static_assert(!BUF || (DT == MOE_BF16 && TM == 256) || (FP8 && TM == 128),
-                "buffer loads: bf16 256-row tiles and fp8 128-row tiles");
+  static_assert(!BUF || (DT == MOE_BF16 && TM == 256) || (FP8 && (TM == 128 || C::TN == 128)),
+                "buffer loads: bf16 256-row tiles and fp8 tiles 128 rows or 128 columns wide");
   const __amdgpu_buffer_rsrc_t rsa =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(asrc), 0, (int)0xffffffffu, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsb =
@@ -234,7 +254,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
     for (int i = 0; i < C::LPB; ++i) vb[i] = (uint32_t)(gb[i] - wbase);
   }
   // fp8 scales: scale slot s = 64 * wave + lane of each stage holds the
-  // slice's scale of A row s (s < TM), of B row s - TM (s < TM + kTN), or a
+  // slice's scale of A row s (s < TM), of B row s - TM (s < TM + TN), or a
   // copy of B row 0's (the remaining slots, never read).  A wave's slots are
   // all A rows or all B rows, so with BUF its scale resource is one array.
   const float* gs = nullptr;
@@ -244,7 +264,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
     const int sidx = 64 * wave + lane;
     const float* as = MODE == 1 ? a.a1s : a.a2s;
     if (sidx < TM) gs = as + (size_t)a_src(sidx) * nkb;
-    else gs = wsbase + (size_t)(b_wrow(sidx < TM + kTN ? sidx - TM : 0) >> a.wsr_shift) * nkb;
+    else gs = wsbase + (size_t)(b_wrow(sidx < TM + C::TN ? sidx - TM : 0) >> a.wsr_shift) * nkb;
     if constexpr (BUF) {
       const uint64_t sb = reinterpret_cast<uint64_t>(64 * wave < TM ? as : wsbase);
       sbase = reinterpret_cast<const float*>(
@@ -259,7 +279,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < NTW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int mval = min(4, max(0, (rows - wm * 64 + 15) >> 4));   // this wave's M tiles holding valid rows
+  const int mval = C::mvalid(wm, rows);   // this wave's M tiles holding valid rows
 
   bool full_tile = false;
   if constexpr (!FP8) full_tile = mval == 4;
@@ -308,7 +328,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            fa[fs][i] = *reinterpret_cast<const i32x4*>(&la[C::off(wm * 64 + i * 16 + row, fs * 4 + grp)]);
+            fa[fs][i] = *reinterpret_cast<const i32x4*>(&la[C::off(C::mrow(wm, i) + row, fs * 4 + grp)]);
 #pragma unroll
           for (int j = 0; j < NTW; ++j)
             fb[fs][j] = *reinterpret_cast<const i32x4*>(&lb[C::off(wn * WN + j * 16 + row, fs * 4 + grp)]);
@@ -355,7 +375,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
               if (i < mval) {
-                const i32x4 fa = *reinterpret_cast<const i32x4*>(&la[C::off(wm * 64 + i * 16 + row, fs * 4 + grp)]);
+                const i32x4 fa = *reinterpret_cast<const i32x4*>(&la[C::off(C::mrow(wm, i) + row, fs * 4 + grp)]);
 #pragma unroll
                 for (int j = 0; j < NTW; ++j) F::mma(acc[i][j], fa, fb[j]);
               }
@@ -365,10 +385,19 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
       }
     }
   } else {
+    // A-row loads this wave issues.  fp8 tiles with two stages (the routed
+    // 256-row tiles, whose tiles are partial: a group's last 129..255 rows)
+    // wait for all of a slice's loads (vmcnt 0), so the loads of 8-row blocks
+    // wholly past the valid rows are skipped; their LDS rows feed only C rows
+    // that are never stored (serial clustered2048_fp8 256-row GEMM1 -4%).
+    // With deeper rings the waits count loads and every load is issued; the
+    // bf16 tiles keep a branch-free issue (their GEMM2 measured 4% slower
+    // with the test in the full-tile loop).
+    const int na = FP8 && NST == 2 ? min(C::LPA, max(0, (rows - wave * C::LPA * RPI + RPI - 1) / RPI)) : C::LPA;
     // slice kt into stage st: A rows, then B rows (and fp8 scales)
     auto tissue = [&](int kt, int st) {
       if constexpr (BUF) {
-        issue_rows_buf<C::LPA, false>(smem + st * C::STAGE, rsa, va, kt * SL, wave);
+        issue_rows_buf<C::LPA, false>(smem + st * C::STAGE, rsa, va, kt * SL, wave, na);
         issue_rows_buf<C::LPB, SW>(smem + st * C::STAGE + TM * SL, rsb, vb, kt * SL, wave);
         if constexpr (FP8) {   // the scale loads of tile_issue, from the wave's scale resource
           const __amdgpu_buffer_rsrc_t rss =
@@ -386,7 +415,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
           }
         }
       } else {
-        tile_issue<DT, TM, BLK, SW>(smem, ga, gb, gs, kt, st, wave);
+        tile_issue<DT, TM, C::TN, BLK, SW>(smem, ga, gb, gs, kt, st, wave, na);
       }
     };
 #pragma unroll
@@ -415,7 +444,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
             if (fs == 1) tissue(min(kt + 1, nkt - 1), (kt + 1) & 1);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              fa[fs][i] = *reinterpret_cast<const i32x4*>(&la[C::off(wm * 64 + i * 16 + row, fs * 4 + grp)]);
+              fa[fs][i] = *reinterpret_cast<const i32x4*>(&la[C::off(C::mrow(wm, i) + row, fs * 4 + grp)]);
 #pragma unroll
             for (int j = 0; j < NTW; ++j)
               fb[fs][j] = *reinterpret_cast<const i32x4*>(&lb[C::off(wn * WN + j * 16 + row, fs * 4 + grp)]);
@@ -470,7 +499,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
 #pragma unroll
               for (int i = 0; i < 4; ++i)
                 if (i < mval) {
-                  const i32x4 fa = *reinterpret_cast<const i32x4*>(&la[C::off(wm * 64 + i * 16 + row, fs * 4 + grp)]);
+                  const i32x4 fa = *reinterpret_cast<const i32x4*>(&la[C::off(C::mrow(wm, i) + row, fs * 4 + grp)]);
 #pragma unroll
                   for (int j = 0; j < NTW; ++j) F::mma(acc[i][j], fa, fb[j]);
                 }
@@ -501,12 +530,12 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
             _Pragma("unroll") \
             for (int i = 0; i < 4; ++i) { \
               if (GUARD) { \
-                const int r = wm * 64 + i * 16 + row; \
+                const int r = C::mrow(wm, i) + row; \
                 const i32x4 fa0 = *reinterpret_cast<const i32x4*>(&la[C::off(r, grp)]); \
                 const i32x4 fa1 = *reinterpret_cast<const i32x4*>(&la[C::off(r, 4 + grp)]); \
                 float sa[4]; \
                 _Pragma("unroll") \
-                for (int q = 0; q < 4; ++q) sa[q] = scale(wm * 64 + i * 16 + 4 * grp + q); \
+                for (int q = 0; q < 4; ++q) sa[q] = scale(C::mrow(wm, i) + 4 * grp + q); \
                 _Pragma("unroll") \
                 for (int jj = 0; jj < 4; ++jj) { \
                   const f32x4 p = F::mma128(fa0, fa1, fb0[jj], fb1[jj]); \
@@ -517,7 +546,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
               } \
             } \
           }
-          if (TM == 128 && mval == 4) {
+          if (C::NTW == 4 && mval == 4) {
             MOE_FP8_MTILES(true)
           } else {
             MOE_FP8_MTILES(i < mval)
@@ -539,7 +568,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
     // 1742 -> 1699 us staged).
     using OT = typename std::conditional<MODE == 1 && FP8, float, uint16_t>::type;
     constexpr int ES = sizeof(OT);
-    constexpr int OC = MODE == 1 ? kTN / 2 : kTN;       // output columns of the tile
+    constexpr int OC = MODE == 1 ? C::TN / 2 : C::TN;   // output columns of the tile
     constexpr int CPR = OC * ES / 16;                   // 16-byte chunks per row
     constexpr int S = (int)C::EPI_STRIDE;
     static_assert(OC * ES <= 512, "an output row of the tile fits a staging row");
@@ -550,7 +579,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
       if (i >= mval) break;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int r = wm * 64 + i * 16 + 4 * grp + q;
+        const int r = C::mrow(wm, i) + 4 * grp + q;
         uint8_t* lrow = lt + r * S;
         if (MODE == 1) {
 #pragma unroll
@@ -589,14 +618,14 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
     if (i >= mval) break;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int r = wm * 64 + i * 16 + 4 * grp + q;
+      const int r = C::mrow(wm, i) + 4 * grp + q;
       if (r >= rows) continue;
       if (MODE == 1) {
         const size_t hrow = (size_t)(gr.slot0 + row0 + r) * a.I;
 #pragma unroll
         for (int jp = 0; jp < NTW / 2; ++jp) {
           const float gv = acc[i][2 * jp][q], uv = acc[i][2 * jp + 1][q];
-          const int col = nt * (kTN / 2) + (wn * (NTW / 2) + jp) * 16 + row;
+          const int col = nt * (C::TN / 2) + (wn * (NTW / 2) + jp) * 16 + row;
           if (col < a.I) store_h<DT>(a.h, hrow + col, silu_for<DT>(gv) * uv);
         }
       } else {
@@ -604,7 +633,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
         const size_t yrow = (size_t)out_row(a, gr, row0 + r) * a.H;
 #pragma unroll
         for (int j = 0; j < NTW; ++j) {
-          const int col = nt * kTN + wn * WN + j * 16 + row;
+          const int col = nt * C::TN + wn * WN + j * 16 + row;
           if (col < a.H) store_y<DT>(ybase, yrow + col, acc[i][j][q]);
         }
       }
@@ -614,7 +643,7 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
 
 template <int DT, int MODE, bool SHARED, int TM, bool BLK, bool SW, bool BUF = false>
 hipError_t launch_fat(const char* name, unsigned grid, int ntn, const Args& a, hipStream_t st) {
-  using C = TileCfg<DT, TM>;
+  using C = TileCfg<DT, TM, tile_cols(DT, MODE, TM, SHARED)>;
   hipError_t e = moe::ensure_dynamic_lds(
       reinterpret_cast<const void*>(&ffn_fat_kernel<DT, MODE, SHARED, TM, BLK, SW, BUF>), (int)C::LDS_BYTES);
   if (e != hipSuccess) return e;
@@ -629,8 +658,7 @@ namespace moe {
 namespace ffn {
 
 template <int DT>
-hipError_t launch_tiled(int mode, bool shared, int tm, bool stream_w, unsigned grid, int ntn, const Args& a,
-                        hipStream_t st) {
+hipError_t launch_tiled(int mode, bool shared, int tm, bool stream_w, int tiles, const Args& a, hipStream_t st) {
   static const char* const kName[2][2][2] = {                  // [mode - 1][shared][tm == 128]
       {{"ffn_gemm1_tiled", "ffn_gemm1_tiled128"}, {"ffn_gemm1_shared_tiled", "ffn_gemm1_shared_tiled128"}},
       {{"ffn_gemm2_tiled", "ffn_gemm2_tiled128"}, {"ffn_gemm2_shared_tiled", "ffn_gemm2_shared_tiled128"}}};
@@ -638,18 +666,20 @@ hipError_t launch_tiled(int mode, bool shared, int tm, bool stream_w, unsigned g
   // fp8 scale blocks of 4 slices need the slice count K / 128 to be a multiple of 4
   const bool blk = DT == MOE_FP8_E4M3 && (((mode == 1 ? a.H : a.I) / 128) & 3) == 0;
   constexpr bool FP8 = DT == MOE_FP8_E4M3;
+  const int ntn = tile_ntn(DT, mode, tm, shared, a.I, a.H);
+  const unsigned grid = (unsigned)tiles * (unsigned)ntn;
   // buffer-resource loads (bf16 256-row tiles, fp8 tiles) need 32-bit
   // offsets into the activations (x, or h; fp8: their codes and scales) and
   // into one expert's weights
   const size_t esz = DT == MOE_BF16 ? 2 : 1;
   const size_t act_bytes = mode == 1 ? (size_t)a.T * a.H * esz : (size_t)(a.P + a.T) * a.I * esz;
-  // (fp8 256-row tiles sit at the register limit: the buffer form spills there)
-  const bool buf = (DT == MOE_BF16 ? tm == 256 : FP8 && tm == 128) && act_bytes <= 0xffffffffu &&
-                   (size_t)2 * a.I * a.H * esz <= 0xffffffffu;
-#define MOE_BUFV(TMV) ((DT == MOE_BF16 && TMV == 256) || (FP8 && TMV == 128))
+  // (fp8 256-row tiles 256 columns wide sit at the register limit: the buffer form spills there)
+  const bool buf = (DT == MOE_BF16 ? tm == 256 : FP8 && (tm == 128 || tile_cols(DT, mode, tm, shared) == 128)) &&
+                   act_bytes <= 0xffffffffu && (size_t)2 * a.I * a.H * esz <= 0xffffffffu;
+#define MOE_BUFV(M, TMV, S) ((DT == MOE_BF16 && TMV == 256) || (FP8 && (TMV == 128 || tile_cols(DT, M, TMV, S) == 128)))
 #define MOE_TLB(M, S, TMV, SWV) \
-  (buf ? (FP8 && blk ? launch_fat<DT, M, S, TMV, FP8, SWV, MOE_BUFV(TMV)>(name, grid, ntn, a, st) \
-                     : launch_fat<DT, M, S, TMV, false, SWV, MOE_BUFV(TMV)>(name, grid, ntn, a, st)) \
+  (buf ? (FP8 && blk ? launch_fat<DT, M, S, TMV, FP8, SWV, MOE_BUFV(M, TMV, S)>(name, grid, ntn, a, st) \
+                     : launch_fat<DT, M, S, TMV, false, SWV, MOE_BUFV(M, TMV, S)>(name, grid, ntn, a, st)) \
        : (FP8 && blk ? launch_fat<DT, M, S, TMV, FP8, SWV>(name, grid, ntn, a, st) \
                      : launch_fat<DT, M, S, TMV, false, SWV>(name, grid, ntn, a, st)))
   // the shared expert's weights are read by every row tile: always cached
@@ -663,9 +693,9 @@ hipError_t launch_tiled(int mode, bool shared, int tm, bool stream_w, unsigned g
 #undef MOE_BUFV
 }
 
-template hipError_t launch_tiled<MOE_F32>(int, bool, int, bool, unsigned, int, const Args&, hipStream_t);
-template hipError_t launch_tiled<MOE_BF16>(int, bool, int, bool, unsigned, int, const Args&, hipStream_t);
-template hipError_t launch_tiled<MOE_FP8_E4M3>(int, bool, int, bool, unsigned, int, const Args&, hipStream_t);
+template hipError_t launch_tiled<MOE_F32>(int, bool, int, bool, int, const Args&, hipStream_t);
+template hipError_t launch_tiled<MOE_BF16>(int, bool, int, bool, int, const Args&, hipStream_t);
+template hipError_t launch_tiled<MOE_FP8_E4M3>(int, bool, int, bool, int, const Args&, hipStream_t);
 
 }  // namespace ffn
 }  // namespace moe
