@@ -410,6 +410,32 @@ def test_expert_ffn_fp8_tile_bound(sizes):
     _log(f"[expert_ffn tile bound {sizes}] y_sorted err {e}")
 
 
+@pytest.mark.parametrize("sizes,shared", [([255, 240, 208, 193, 192, 176, 145, 130, 511], False),
+                                          ([300, 150, 40, 7], True)])
+def test_expert_ffn_fp8_partial_tiles(sizes, shared):
+    """fp8 256-row tiles give wave wm the 16-row M tiles wm, wm + 4, ... and
+    skip the activation loads of 8-row blocks past a partial tile's rows:
+    rests of 130..255 rows (and 511 = 256 + 255) put the last valid M tile
+    at every wave in turn.  The second case has a shared expert of 497
+    tokens: one full 256-row tile (fp8 GEMM1 on 128-column tiles) and two
+    128-row tiles for the rest, beside a partial 256-row routed tile."""
+    E, T = len(sizes), sum(sizes)
+    cfg = get_config("clustered2048_fp8").with_(name="fp8_partial_tiles", routing="random", T=T, H=512, E=E, k=1,
+                                                I=2048, I_shared=2048 if shared else 0)
+    inp, gin = _small_inputs(cfg)
+    sorted_pair = np.random.default_rng(7).permutation(T).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    ow = oracle.OracleWeights.from_inputs(inp)
+    xa = oracle.prepare_activations(inp.x.double().numpy(), ow.fp8, ow.block)
+    ref_ys, ref_sh = oracle.expert_ffn(xa, offsets, sorted_pair, 1, ow)
+    ys, ysh = moe.moe_expert_ffn(moe.cfg_from(cfg), gin.x, torch.from_numpy(offsets).to(DEV),
+                                 torch.from_numpy(sorted_pair).to(DEV), moe.Weights.from_inputs(gin))
+    torch.cuda.synchronize()
+    e = assert_outputs_close(ys, ref_ys, tol_key(cfg), "y_sorted")
+    e2 = assert_outputs_close(ysh, ref_sh, tol_key(cfg), "y_shared") if shared else None
+    _log(f"[expert_ffn fp8 partial tiles {sizes}] y_sorted err {e} y_shared err {e2}")
+
+
 @pytest.mark.parametrize("name", sorted(SMALL))
 def test_combine_small(name):
     cfg = SMALL[name]
