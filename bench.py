@@ -54,6 +54,14 @@ DEFAULT_WORKLOAD = "prefill8192_ep8"
 OTHER_WORKLOADS = ("decode16", "decode256", "clustered2048_fp8", "decode16_fp8", "decode256_fp8", "tiny_f32")
 
 
+def shared_in_lists(cfg):
+    """Whether the shared expert's tiles go into the routed tile launches: a
+    tiled shared expert without fp8 quantisation between its GEMMs whose GEMM1
+    has at least 256 tiles of 256 x 256."""
+    tiles1 = -(-cfg.T // 256) * -(-cfg.I // 128)
+    return bool(cfg.I_shared) and cfg.w_dtype != "fp8" and cfg.T > SKINNY_ROWS and tiles1 >= 256
+
+
 def kernel_models(cfg, counts):
     """Algorithmic bytes and FLOPs of each kernel per launch, from the counts.
 
@@ -94,11 +102,16 @@ def kernel_models(cfg, counts):
             items += tiled(mg, "")
     if cfg.I_shared:
         # T <= 16: the shared expert runs as two 8-row halves inside the routed
-        # streaming launch; up to 32 tokens it has a streaming launch of its own
+        # streaming launch; up to 32 tokens it has a streaming launch of its own;
+        # when its GEMM1 fills the device (bf16/fp32) its tiles join the routed lists
         if T <= HALVES_ROWS:
             items.append((T, "skinny"))
+        elif T <= SKINNY_ROWS:
+            items.append((T, "shared_skinny"))
+        elif shared_in_lists(cfg):
+            items += tiled(T, "")
         else:
-            items += [(T, "shared_skinny")] if T <= SKINNY_ROWS else tiled(T, "shared_")
+            items += tiled(T, "shared_")
     for mg, reg in items:
         if mg == 0:
             continue

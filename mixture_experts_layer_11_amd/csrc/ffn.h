@@ -13,6 +13,12 @@ namespace ffn {
 constexpr int kSkinnyRows = 32;  // groups with <= this many rows take the skinny path
 constexpr int kTileRows = 256;   // rows per full tile of the tiled grouped GEMM
 constexpr int kMidRows = 128;    // rows per tile for the rest of a group (m mod 256 rows), fp8 weights
+// The shared expert joins the routed tile lists when it is tiled, has no
+// fp8 quantisation between its GEMMs, and its GEMM1 alone has at least this
+// many 256 x 256 tiles (MI355X's CU count: it fills the device and is not
+// overlapped with the routed work, e.g. the 8192-token prefill share): one
+// launch per GEMM then covers both, without a tail between them.
+constexpr int kSharedInListTiles = 256;
 constexpr int kPlanHead = 5;     // plan: [0..2] skinny list sizes (<=8, <=16, <=32 rows), [3] 256-row tiles,
                                  // [4] 128-row tiles
 
@@ -43,6 +49,7 @@ struct Args {
   int halves;                   // T <= 16: every group in the <= 8-row list, in 8-row halves (shared expert too)
   int fat_cap;                  // capacity of the plan's 256-row tile list (the 128-row list follows it)
   int mid_rest;                 // 1: a group's last m mod 256 rows take 128-row tiles; 0: one more 256-row tile
+  int shared_tiled;             // 1: the shared expert (group E) is in the routed tile lists, no launches of its own
 };
 
 struct Group {

@@ -48,7 +48,9 @@ __global__ __launch_bounds__(512) void ffn_plan_kernel(Args a) {
   const int g = threadIdx.x;
   int m = 0;
   if (g < a.G) m = g < a.E ? a.offsets[g + 1] - a.offsets[g] : a.T;
-  build_plan(moe::PlanArgs{const_cast<int32_t*>(a.plan), a.G, a.E, a.T, a.fat_cap, a.halves, a.mid_rest}, m, wt);
+  build_plan(moe::PlanArgs{const_cast<int32_t*>(a.plan), a.G, a.E, a.T, a.fat_cap, a.halves, a.mid_rest,
+                           a.shared_tiled},
+             m, wt);
 }
 
 // The shared expert: its own launches, on the stream it is given.
@@ -101,12 +103,16 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st, bool plan
   // Otherwise at most P / 256 full tiles plus one partial tile per tiled
   // group (256 rows, or with mid_rest 128 rows), of which there are at most
   // min(E, P / (kSkinnyRows + 1)).
-  const int tiled_groups = c.T > kSkinnyRows ? (P / (kSkinnyRows + 1) < c.E ? P / (kSkinnyRows + 1) : c.E) : 0;
+  int tiled_groups = c.T > kSkinnyRows ? (P / (kSkinnyRows + 1) < c.E ? P / (kSkinnyRows + 1) : c.E) : 0;
   // With mid_rest every 256-row tile, full or partial, holds more than 128 of
   // the P rows, so there are also at most P / 129 of them (clustered2048_fp8:
   // 127 instead of 320 tiles in the grid, the rest exiting at once).
   int max_fat = tiled_groups > 0 ? P / kTileRows + tiled_groups : 0;
   if (a.mid_rest && P / (kMidRows + 1) < max_fat) max_fat = P / (kMidRows + 1);
+  if (a.shared_tiled) {   // the shared expert's ceil(T / 256) tiles join the list (never with mid_rest)
+    max_fat += moe::ceil_div(c.T, kTileRows);
+    tiled_groups += 1;
+  }
   const int max_mid = a.mid_rest ? tiled_groups : 0;
   // halves mode: the shared expert's rows [P, P + T) of h are the routed lists' too
   const int qrows = P + (a.halves && a.has_shared ? c.T : 0);
@@ -193,7 +199,7 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st, bool plan
 // the routed kernels would only add contention.
 template <int DT>
 hipError_t run_ffn(const moe_cfg& c, const Args& a, hipStream_t st, bool planned, bool fork) {
-  if (!a.has_shared || a.halves) return run_routed<DT>(c, a, st, planned, fork);
+  if (!a.has_shared || a.halves || a.shared_tiled) return run_routed<DT>(c, a, st, planned, fork);
   if (!fork) {
     hipError_t e = run_shared<DT>(c, a, st);
     return e != hipSuccess ? e : run_routed<DT>(c, a, st, planned, false);
@@ -230,8 +236,9 @@ hipError_t run_ffn(const moe_cfg& c, const Args& a, hipStream_t st, bool planned
 namespace moe {
 
 // Capacity of the 256-row tile list: at most P / 256 full tiles, plus one
-// partial tile per routed group.
-int ffn_fat_cap(const moe_cfg& c) { return c.T * c.k / kTileRows + c.E; }
+// partial tile per routed group, plus the shared expert's ceil(T / 256) tiles
+// when they join the list.
+int ffn_fat_cap(const moe_cfg& c) { return c.T * c.k / kTileRows + c.E + c.T / kTileRows + 1; }
 
 size_t ffn_plan_ints(const moe_cfg& c) {
   const int G = c.E + (c.I_shared > 0 ? 1 : 0);
@@ -248,6 +255,8 @@ PlanArgs ffn_plan_args(const moe_cfg& c, int32_t* plan) {
   p.fat_cap = ffn_fat_cap(c);
   p.halves = c.T <= 16 ? 1 : 0;
   p.mid_rest = c.w_dtype == MOE_FP8_E4M3 ? 1 : 0;   // HBM-bound medium groups: deeper pipeline on 128-row tiles
+  p.shared_tiled = c.I_shared > 0 && c.w_dtype != MOE_FP8_E4M3 && c.T > kSkinnyRows &&
+                   (long long)moe::ceil_div(c.T, kTileRows) * moe::ceil_div(c.I, kTN / 2) >= kSharedInListTiles;
   return p;
 }
 
@@ -285,6 +294,7 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const void* x, const int32_t* off
   a.fat_cap = pa.fat_cap;
   a.halves = pa.halves;
   a.mid_rest = pa.mid_rest;
+  a.shared_tiled = pa.shared_tiled;
   if (c.w_dtype == MOE_FP8_E4M3) {
     hipError_t e = launch_quant_fp8(c.T, c.H, c.quant_block, x, MOE_BF16, ws.xq, ws.xs, st);
     if (e != hipSuccess) return e;

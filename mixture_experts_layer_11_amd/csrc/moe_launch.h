@@ -44,6 +44,7 @@ hipError_t launch_route(const moe_cfg& c, const void* x, const void* wg, const f
 struct PlanArgs {
   int32_t* plan;
   int G, E, T, fat_cap, halves, mid_rest;
+  int shared_tiled;   // the shared expert's tiles join the routed tile lists
 };
 PlanArgs ffn_plan_args(const moe_cfg& c, int32_t* plan);
 

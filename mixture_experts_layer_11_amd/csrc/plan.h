@@ -21,7 +21,9 @@ constexpr int kPlanLds = 5 * 8 + 2 * 8 + 3 * 512;
 // (one 256-row tile above that, which reads the weights once).  The shared
 // expert (g == E) has launches of its own, except in halves mode (T <= 16):
 // there every group, the shared expert included, enters the <= 8-row list
-// as one or two 8-row halves, so the other lists stay empty.  The five
+// as one or two 8-row halves, so the other lists stay empty; and with
+// shared_tiled, where its tiles join the routed tile lists like a group of
+// T rows.  The five
 // per-group counts are prefix-summed over groups 0..g in each wave with
 // shuffles, then across the 8 waves through wt (one barrier).  The two tile
 // lists run in order of decreasing group size (equal sizes by group), so a
@@ -34,7 +36,7 @@ __device__ inline void build_plan(const PlanArgs& a, int m, int* wt) {
   const bool listed = m > 0 && m <= kSkinnyRows && (!shared || a.halves);
   const int cls = listed ? (a.halves || m <= 8 ? 0 : m <= 16 ? 1 : 2) : -1;
   const int nent = cls < 0 ? 0 : (a.halves ? (m + 7) / 8 : 1);   // list entries of this group
-  const bool tiled = m > kSkinnyRows && !shared;
+  const bool tiled = m > kSkinnyRows && (!shared || a.shared_tiled);
   const int rest = m % kTileRows;
   const bool rest_fat = a.mid_rest && rest > kMidRows;   // one partial 256-row tile reads the weights once
   const int tiles = tiled ? (a.mid_rest ? m / kTileRows + (rest_fat ? 1 : 0) : (m + kTileRows - 1) / kTileRows) : 0;

@@ -52,12 +52,16 @@ def test_prefill_layer_model():
     P, T, H, I, E = cfg.T * cfg.k, cfg.T, cfg.H, cfg.I, cfg.E
     assert layer["flops"] == (P + T) * 6 * H * I + 2 * T * H * E
     assert layer["bytes"] == (E + 1) * _weights_bytes(cfg) + E * H * 2 + E * 4 + 2 * T * H * 2
-    assert models["ffn_gemm1_tiled"]["flops"] == 2 * P * 2 * I * H
-    assert models["ffn_gemm1_shared_tiled"]["flops"] == 2 * T * 2 * I * H
+    # the shared expert's GEMM1 (32 x 16 tiles) fills the device: its tiles run in the routed launches
+    assert bench.shared_in_lists(cfg)
+    assert models["ffn_gemm1_tiled"]["flops"] == 2 * (P + T) * 2 * I * H
+    assert models["ffn_gemm1_shared_tiled"]["flops"] == 0
     assert models["ffn_gemm1_skinny"]["bytes"] == 0
     assert not bench.shares_device(cfg)
     assert bench.shares_device(get_config("clustered2048_fp8"))
     assert not bench.shares_device(get_config("decode256"))
+    assert not bench.shared_in_lists(get_config("decode256"))
+    assert not bench.shared_in_lists(get_config("clustered2048_fp8"))
 
 
 def test_more_than_one_gpu_is_refused():

@@ -620,10 +620,14 @@ ORACLE_WORKERS = 8
 # Mid-size layers that take every path at once: the three-kernel dispatch
 # (more than 4096 pairs), the LDS-staged router, streaming and tiled groups
 # on separate streams (a mean of 17..1023 rows per expert), the forked shared
-# expert, fp8 128-row rest tiles and both weight-scale layouts.
+# expert or one in the routed tile lists, fp8 128-row rest tiles and both
+# weight-scale layouts.
 MID = {
     "mid_zipf_bf16": get_config("prefill8192_ep8").with_(name="mid_zipf_bf16", T=4097, H=512, E=64, I=512,
                                                          I_shared=512),
+    # a shared expert whose GEMM1 fills the device (16 x 16 tiles): its tiles join the routed tile lists
+    "mid_shared_tiled_bf16": get_config("prefill8192_ep8").with_(name="mid_shared_tiled_bf16", T=4000, H=512,
+                                                                 E=64, I=2048, I_shared=2048),
     "mid_clustered_fp8": get_config("clustered2048_fp8").with_(name="mid_clustered_fp8", T=3001, H=512, E=64,
                                                                I=2048, I_shared=2048),
     "mid_fp8_tiles": get_config("decode16_fp8").with_(name="mid_fp8_tiles", routing="zipf", T=1500, H=512, E=64,
