@@ -209,6 +209,9 @@ def main(argv=None):
                 if "SQ_INSTS_MFMA" in med:
                     lines.append(f"Busy cycles per MFMA instruction: "
                                  f"{med['SQ_VALU_MFMA_BUSY_CYCLES'][0] / med['SQ_INSTS_MFMA'][0]:.1f}.")
+            if "SQ_INSTS_VALU" in med and "SQ_INSTS_MFMA" in med and med["SQ_INSTS_MFMA"][0] > 0:
+                lines.append(f"Vector ALU instructions per MFMA instruction: SQ_INSTS_VALU / SQ_INSTS_MFMA = "
+                             f"**{med['SQ_INSTS_VALU'][0] / med['SQ_INSTS_MFMA'][0]:.2f}**.")
             if bench and bench["roofline"]["unit"] == "TFLOP/s":
                 at_clock = bench["roofline"]["peak"] * mhz / 2400.0
                 lines.append(f"Peak at that clock {at_clock:.0f} TFLOP/s: the kernel runs at "
