@@ -123,6 +123,23 @@ size_t moe_workspace_bytes(const moe_cfg* cfg);
  * every other entry point uses). */
 int moe_workspace_size(const moe_cfg* cfg, size_t* bytes);
 
+/* Where the expert FFNs leave their intermediate in the workspace: the
+ * SwiGLU output h = SiLU(a W1^T) * (a W3^T) of every row (Perplexity,
+ * "GroupGEMM"), and for fp8 weights its per-row block quantisation, which
+ * the down projection reads (same article, "Quantization").  h has P + T
+ * rows of I (P = T * k): row s < offsets[E] is pair sorted_pair[s]'s, in
+ * dispatch order; rows P .. P + T - 1 are the shared expert's when
+ * I_shared > 0.  Other rows are unspecified.
+ *   h_offset   byte offset of h: bf16 for bf16 weights, fp32 otherwise
+ *   hq_offset  fp8 weights: byte offset of h's E4M3 codes [P + T, I]
+ *   hs_offset  fp8 weights: byte offset of their fp32 scales
+ *              [P + T, I / quant_block]
+ * hq_offset and hs_offset are SIZE_MAX unless the weights are fp8; all three
+ * are SIZE_MAX when T == 0.  The contents are those of the last
+ * moe_expert_ffn or moe_forward on the workspace, once it has completed.
+ * Returns MOE_ERR_INVALID_ARG for a NULL pointer, or cfg's error. */
+int moe_workspace_ffn_h(const moe_cfg* cfg, size_t* h_offset, size_t* hq_offset, size_t* hs_offset);
+
 /* Router (steps: gate GEMM, scoring, selection bias, top-k, weights; the
  * vLLM DeepSeek-V4.1-Flash article, section "Kernels", item "Mega-Gate").
  * Below 512 bf16 tokens (up to 1024 fp32 tokens) it is one launch:
@@ -182,6 +199,18 @@ int moe_quantize_fp8(int32_t rows, int32_t cols, int32_t block, const void* in, 
 int moe_expert_ffn(const moe_cfg* cfg, const void* x, const int32_t* offsets,
                    const int32_t* sorted_pair, const moe_weights* w, void* y_sorted,
                    void* y_shared, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* The expert FFNs' down projection alone (Perplexity, "GroupGEMM": the
+ * second grouped GEMM, y = h W2^T per group, and the shared expert's): the
+ * y_sorted and y_shared that moe_expert_ffn would write, computed from the h
+ * the workspace holds where moe_workspace_ffn_h places it, instead of from
+ * x.  The caller writes h there first, in that row layout; for fp8 weights
+ * the E4M3 codes and fp32 scales of h, which are used as they are (not
+ * requantised).  Other arguments as moe_expert_ffn.  For callers that
+ * produce h themselves, and to test the down projection on its own. */
+int moe_expert_ffn_down(const moe_cfg* cfg, const int32_t* offsets, const int32_t* sorted_pair,
+                        const moe_weights* w, void* y_sorted, void* y_shared, void* ws, size_t ws_bytes,
+                        void* hip_stream);
 
 /* Combine (Perplexity, "Lower latency and higher throughput with multi-node
  * DeepSeek deployment", section "Expert parallelism": the outputs of a

@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     moe_combine,
     moe_dispatch,
     moe_expert_ffn,
+    moe_expert_ffn_down,
     moe_forward,
     moe_forward_noalloc,
     moe_profile_start,
@@ -31,6 +32,7 @@ from .binding import (  # noqa: F401
     moe_route,
     moe_routing_stats,
     moe_workspace_bytes,
+    moe_workspace_ffn_h,
     status_str,
     workspace_size,
 )

@@ -20,9 +20,10 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = range(2)
 
-EXPORTS = ("moe_status_str", "moe_last_error", "moe_workspace_bytes", "moe_workspace_size", "moe_route", "moe_dispatch",
-           "moe_quantize_fp8", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_forward_noalloc", "moe_graph_capture",
-           "moe_graph_launch", "moe_graph_destroy", "moe_routing_stats", "moe_profile_start", "moe_profile_stop")
+EXPORTS = ("moe_status_str", "moe_last_error", "moe_workspace_bytes", "moe_workspace_size", "moe_workspace_ffn_h",
+           "moe_route", "moe_dispatch", "moe_quantize_fp8", "moe_expert_ffn", "moe_expert_ffn_down", "moe_combine",
+           "moe_forward", "moe_forward_noalloc", "moe_graph_capture", "moe_graph_launch", "moe_graph_destroy",
+           "moe_routing_stats", "moe_profile_start", "moe_profile_stop")
 
 
 class MoELibraryMissing(RuntimeError):
@@ -74,10 +75,12 @@ def load_library(path: str = LIB_PATH):
     lib.moe_workspace_bytes.restype = SZ
     lib.moe_workspace_bytes.argtypes = [cfgp]
     lib.moe_workspace_size.argtypes = [cfgp, ctypes.POINTER(SZ)]
+    lib.moe_workspace_ffn_h.argtypes = [cfgp, ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
     lib.moe_route.argtypes = [cfgp, P, P, P, P, P, P, SZ, P]
     lib.moe_dispatch.argtypes = [cfgp, P, P, P, P, P, P, SZ, P]
     lib.moe_quantize_fp8.argtypes = [I32, I32, I32, P, I32, P, P, P]
     lib.moe_expert_ffn.argtypes = [cfgp, P, P, P, wp, P, P, P, SZ, P]
+    lib.moe_expert_ffn_down.argtypes = [cfgp, P, P, wp, P, P, P, SZ, P]
     lib.moe_combine.argtypes = [cfgp, P, P, P, P, P, P]
     lib.moe_forward.argtypes = [cfgp, P, P, P, wp, P, P, P, P, P, SZ, P]
     lib.moe_forward_noalloc.argtypes = [cfgp, P, P, P, wp, P, P, P, P, P]
@@ -136,6 +139,15 @@ def workspace_size(cfg: MoeCfg) -> int:
 def moe_workspace_bytes(cfg: MoeCfg) -> int:
     """Workspace bytes for this layer (0 when cfg is invalid; see last_error())."""
     return int(load_library().moe_workspace_bytes(ctypes.byref(cfg)))
+
+
+def moe_workspace_ffn_h(cfg: MoeCfg):
+    """Byte offsets in the workspace of the expert FFNs' SwiGLU output h and,
+    for fp8 weights, of its codes and scales: (h, hq, hs), None where absent."""
+    offs = [ctypes.c_size_t(0) for _ in range(3)]
+    _check(load_library().moe_workspace_ffn_h(ctypes.byref(cfg), *(ctypes.byref(o) for o in offs)))
+    none = ctypes.c_size_t(-1).value
+    return tuple(None if o.value == none else o.value for o in offs)
 
 
 def alloc_workspace(cfg: MoeCfg, device="cuda") -> torch.Tensor:
@@ -251,6 +263,19 @@ def moe_expert_ffn(cfg: MoeCfg, x, offsets, sorted_pair, weights: Weights, ws=No
     w = weights.c_struct()
     _check(lib.moe_expert_ffn(ctypes.byref(cfg), _ptr(x), _ptr(offsets), _ptr(sorted_pair), ctypes.byref(w),
                               _ptr(y_sorted), _ptr(y_shared), _ptr(ws), ws.numel(), _stream(stream)))
+    return y_sorted, y_shared
+
+
+def moe_expert_ffn_down(cfg: MoeCfg, offsets, sorted_pair, weights: Weights, ws, stream=None):
+    """The down projection alone, on the h the caller wrote into ``ws`` at
+    moe_workspace_ffn_h's offsets (fp8: its codes and scales)."""
+    lib = load_library()
+    dev = ws.device
+    y_sorted = _out((cfg.T * cfg.k, cfg.H), _act_torch(cfg), dev)
+    y_shared = _out((cfg.T, cfg.H), _act_torch(cfg), dev) if cfg.I_shared > 0 else None
+    w = weights.c_struct()
+    _check(lib.moe_expert_ffn_down(ctypes.byref(cfg), _ptr(offsets), _ptr(sorted_pair), ctypes.byref(w),
+                                   _ptr(y_sorted), _ptr(y_shared), _ptr(ws), ws.numel(), _stream(stream)))
     return y_sorted, y_shared
 
 

@@ -58,8 +58,8 @@ template <int DT>
 hipError_t run_shared(const moe_cfg& c, const Args& a, hipStream_t st) {
   const int P = a.P;
   hipError_t e;
-  for (int mode = 1; mode <= 2; ++mode) {
-    if (mode == 2 && DT == MOE_FP8_E4M3) {   // its rows [P, P + T) of h
+  for (int mode = a.first_mode; mode <= 2; ++mode) {
+    if (mode == 2 && DT == MOE_FP8_E4M3 && a.first_mode == 1) {   // its rows [P, P + T) of h
       e = moe::launch_quant_fp8(c.T, c.I, a.qb, a.h + (size_t)P * c.I * 4, MOE_F32,
                                 const_cast<uint8_t*>(a.a2) + (size_t)P * c.I,
                                 const_cast<float*>(a.a2s) + (size_t)P * (c.I / a.qb), st);
@@ -116,9 +116,9 @@ hipError_t run_routed(const moe_cfg& c, const Args& a, hipStream_t st, bool plan
   const int max_mid = a.mid_rest ? tiled_groups : 0;
   // halves mode: the shared expert's rows [P, P + T) of h are the routed lists' too
   const int qrows = P + (a.halves && a.has_shared ? c.T : 0);
-  for (int mode = 1; mode <= 2; ++mode) {
+  for (int mode = a.first_mode; mode <= 2; ++mode) {
     if ((e = hook(2 * mode - 2)) != hipSuccess) return e;
-    if (mode == 2 && DT == MOE_FP8_E4M3) {
+    if (mode == 2 && DT == MOE_FP8_E4M3 && a.first_mode == 1) {
       e = moe::launch_quant_fp8(qrows, c.I, a.qb, a.h, MOE_F32, const_cast<uint8_t*>(a.a2), const_cast<float*>(a.a2s),
                                 st);
       if (e != hipSuccess) return e;
@@ -264,8 +264,11 @@ size_t ffn_h_elem_bytes(const moe_cfg& c) { return c.w_dtype == MOE_BF16 ? 2 : 4
 
 hipError_t launch_expert_ffn(const moe_cfg& c, const void* x, const int32_t* offsets,
                              const int32_t* sorted_pair, const moe_weights& w, void* y_sorted,
-                             void* y_shared, const FfnWs& ws, hipStream_t st, bool planned, bool fork) {
+                             void* y_shared, const FfnWs& ws, hipStream_t st, bool planned, bool fork,
+                             bool down_only) {
   Args a{};
+  a.first_mode = down_only ? 2 : 1;
+  if (down_only) fork = false;
   a.T = c.T;
   a.H = c.H;
   a.E = c.E;
@@ -296,8 +299,10 @@ hipError_t launch_expert_ffn(const moe_cfg& c, const void* x, const int32_t* off
   a.mid_rest = pa.mid_rest;
   a.shared_tiled = pa.shared_tiled;
   if (c.w_dtype == MOE_FP8_E4M3) {
-    hipError_t e = launch_quant_fp8(c.T, c.H, c.quant_block, x, MOE_BF16, ws.xq, ws.xs, st);
-    if (e != hipSuccess) return e;
+    if (!down_only) {
+      hipError_t e = launch_quant_fp8(c.T, c.H, c.quant_block, x, MOE_BF16, ws.xq, ws.xs, st);
+      if (e != hipSuccess) return e;
+    }
     a.a1 = ws.xq;
     a.a1s = ws.xs;
     a.a2 = ws.hq;

@@ -212,6 +212,18 @@ int moe_workspace_size(const moe_cfg* cfg, size_t* bytes) {
   return ok();
 }
 
+int moe_workspace_ffn_h(const moe_cfg* cfg, size_t* h_offset, size_t* hq_offset, size_t* hs_offset) {
+  int s = check_cfg(cfg);
+  if (s) return s;
+  if (!h_offset || !hq_offset || !hs_offset) return fail(MOE_ERR_INVALID_ARG, "an offset pointer is NULL");
+  const Layout L = layout(*cfg);
+  const bool any = cfg->T > 0, fp8 = any && cfg->w_dtype == MOE_FP8_E4M3;
+  *h_offset = any ? L.h : SIZE_MAX;
+  *hq_offset = fp8 ? L.hq : SIZE_MAX;
+  *hs_offset = fp8 ? L.hs : SIZE_MAX;
+  return ok();
+}
+
 int moe_route(const moe_cfg* cfg, const void* x, const void* w_gate, const float* sel_bias, int32_t* topk_idx,
               float* topk_w, void* ws, size_t ws_bytes, void* hip_stream) {
   int s = check_cfg(cfg);
@@ -274,13 +286,16 @@ int moe_quantize_fp8(int32_t rows, int32_t cols, int32_t block, const void* in, 
   return e == hipSuccess ? ok() : hip_fail(e, "moe_quantize_fp8");
 }
 
-int moe_expert_ffn(const moe_cfg* cfg, const void* x, const int32_t* offsets, const int32_t* sorted_pair,
-                   const moe_weights* w, void* y_sorted, void* y_shared, void* ws, size_t ws_bytes,
-                   void* hip_stream) {
+namespace {
+
+int expert_ffn_call(const moe_cfg* cfg, const void* x, const int32_t* offsets, const int32_t* sorted_pair,
+                    const moe_weights* w, void* y_sorted, void* y_shared, void* ws, size_t ws_bytes,
+                    void* hip_stream, bool down_only) {
+  const char* what = down_only ? "moe_expert_ffn_down" : "moe_expert_ffn";
   int s = check_cfg(cfg);
   if (s) return s;
   if (cfg->T == 0) return ok();
-  NEED_PTR(x);
+  if (!down_only) NEED_PTR(x);
   NEED_PTR(offsets);
   NEED_PTR(sorted_pair);
   NEED_PTR(y_sorted);
@@ -293,8 +308,23 @@ int moe_expert_ffn(const moe_cfg* cfg, const void* x, const int32_t* offsets, co
   Layout L;
   if ((s = check_ws(*cfg, ws, ws_bytes, &L))) return s;
   hipError_t e = moe::launch_expert_ffn(*cfg, x, offsets, sorted_pair, *w, y_sorted, y_shared, ffn_ws(ws, L),
-                                        static_cast<hipStream_t>(hip_stream));
-  return e == hipSuccess ? ok() : hip_fail(e, "moe_expert_ffn");
+                                        static_cast<hipStream_t>(hip_stream), false, true, down_only);
+  return e == hipSuccess ? ok() : hip_fail(e, what);
+}
+
+}  // namespace
+
+int moe_expert_ffn(const moe_cfg* cfg, const void* x, const int32_t* offsets, const int32_t* sorted_pair,
+                   const moe_weights* w, void* y_sorted, void* y_shared, void* ws, size_t ws_bytes,
+                   void* hip_stream) {
+  return expert_ffn_call(cfg, x, offsets, sorted_pair, w, y_sorted, y_shared, ws, ws_bytes, hip_stream, false);
+}
+
+int moe_expert_ffn_down(const moe_cfg* cfg, const int32_t* offsets, const int32_t* sorted_pair,
+                        const moe_weights* w, void* y_sorted, void* y_shared, void* ws, size_t ws_bytes,
+                        void* hip_stream) {
+  return expert_ffn_call(cfg, nullptr, offsets, sorted_pair, w, y_sorted, y_shared, ws, ws_bytes, hip_stream,
+                         true);
 }
 
 int moe_combine(const moe_cfg* cfg, const void* y_sorted, const void* y_shared, const int32_t* pair_slot,

@@ -73,11 +73,13 @@ struct FfnWs {
 size_t ffn_plan_ints(const moe_cfg& c);
 size_t ffn_h_elem_bytes(const moe_cfg& c);
 // With fork = false every launch stays on st: no side stream is created or
-// used (the entry point that allocates nothing).
+// used (the entry point that allocates nothing).  With down_only the GEMM2
+// stage alone runs, on the h already in ws (fp8: its codes and scales, not
+// requantised); x is not read and fork is ignored.
 hipError_t launch_expert_ffn(const moe_cfg& c, const void* x, const int32_t* offsets,
                              const int32_t* sorted_pair, const moe_weights& w, void* y_sorted,
                              void* y_shared, const FfnWs& ws, hipStream_t st, bool planned = false,
-                             bool fork = true);
+                             bool fork = true, bool down_only = false);
 
 // ---- side stream (streams.cpp): forked from and joined back to the caller's stream
 struct SideStream {

@@ -19,5 +19,6 @@ from .moe import (  # noqa: F401
     route,
     routing_stats,
     swiglu_ffn,
+    swiglu_hidden,
     to_f64,
 )

@@ -196,16 +196,21 @@ class OracleWeights:
         return OracleWeights(cfg.E, expert, shared, fp8, blk)
 
 
+def swiglu_hidden(a, w1, w3):
+    """One expert's SwiGLU output h = SiLU(a W1^T) * (a W3^T), SiLU(z) = z sigmoid(z)."""
+    a = np.asarray(a, dtype=np.float64)
+    g = a @ w1.T
+    u = a @ w3.T
+    return g / (1.0 + np.exp(-g)) * u
+
+
 def swiglu_ffn(a, w1, w3, w2, quant_h: bool = False, block: int = 128):
-    """One expert: h = SiLU(a W1^T) * (a W3^T); y = h W2^T, SiLU(z) = z sigmoid(z).
+    """One expert: h = SiLU(a W1^T) * (a W3^T); y = h W2^T.
 
     With ``quant_h`` the SwiGLU output is block-quantised per row per
     ``block`` before the down projection ([PPLX] "Quantization", SiLU kernel).
     """
-    a = np.asarray(a, dtype=np.float64)
-    g = a @ w1.T
-    u = a @ w3.T
-    h = g / (1.0 + np.exp(-g)) * u
+    h = swiglu_hidden(a, w1, w3)
     if quant_h:
         h = quantize_rows_fp8(h, block)[2]
     return h @ w2.T

@@ -92,6 +92,35 @@ def test_invalid_configs_rejected(kw, code):
     assert moe.last_error()
 
 
+@pytest.mark.parametrize("name", sorted(CONFIGS))
+def test_workspace_ffn_h_regions(name):
+    """h (and for fp8 its codes and scales) lie inside the workspace, apart."""
+    c = CONFIGS[name]
+    cfg = B.cfg_from(c)
+    h, hq, hs = moe.moe_workspace_ffn_h(cfg)
+    rows = c.T * c.k + (c.T if c.I_shared else 0)
+    esz = 2 if c.w_dtype == "bf16" else 4
+    regions = [(h, rows * c.I * esz)]
+    if c.w_dtype == "fp8":
+        regions += [(hq, rows * c.I), (hs, rows * (c.I // c.quant_block) * 4)]
+    else:
+        assert hq is None and hs is None
+    regions.sort()
+    assert all(off % 256 == 0 for off, _ in regions)
+    for (a, n), (b, _) in zip(regions, regions[1:]):
+        assert a + n <= b
+    assert regions[-1][0] + regions[-1][1] <= moe.moe_workspace_bytes(cfg)
+
+
+def test_workspace_ffn_h_errors():
+    lib = moe.load_library()
+    assert moe.moe_workspace_ffn_h(_cfg(T=0)) == (None, None, None)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_workspace_ffn_h(ctypes.byref(_cfg()), ctypes.byref(n), None, ctypes.byref(n)) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_workspace_ffn_h(ctypes.byref(_cfg(k=0)), ctypes.byref(n), ctypes.byref(n),
+                                   ctypes.byref(n)) == B.MOE_ERR_INVALID_ARG
+
+
 def test_workspace_bytes_null_cfg_and_tiny_layer():
     lib = moe.load_library()
     assert lib.moe_workspace_bytes(None) == 0 and "cfg" in moe.last_error()
@@ -126,6 +155,13 @@ def test_argument_errors_before_any_launch():
     _, need8 = _ws_status(cfg8)
     w8 = B.MoeWeights(fake, None, fake, None, fake, fake, fake, fake)
     assert lib.moe_expert_ffn(byref(cfg8), fake, fake, fake, byref(w8), fake, fake, fake, need8, None) == B.MOE_ERR_INVALID_ARG
+    # down projection alone: x is not an argument; the same checks as moe_expert_ffn otherwise
+    wf = B.MoeWeights(fake, None, fake, None, fake, None, fake, None)
+    assert lib.moe_expert_ffn_down(byref(cfg), None, fake, byref(wf), fake, fake, fake, need, None) == B.MOE_ERR_INVALID_ARG
+    assert "offsets" in moe.last_error()
+    assert lib.moe_expert_ffn_down(byref(cfg), fake, fake, byref(w), fake, fake, fake, need, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_ffn_down(byref(cfg), fake, fake, byref(wf), fake, fake, fake, need - 1, None) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_expert_ffn_down(byref(cfg8), fake, fake, byref(w8), fake, fake, fake, need8, None) == B.MOE_ERR_INVALID_ARG
     # combine: bad pointers
     assert lib.moe_combine(byref(cfg), None, None, fake, fake, fake, None) == B.MOE_ERR_INVALID_ARG
     # quantiser: bad block / shape
@@ -141,6 +177,7 @@ def test_zero_tokens_is_a_no_op():
     assert lib.moe_route(byref(cfg), None, None, None, None, None, None, 0, None) == B.MOE_OK
     assert lib.moe_dispatch(byref(cfg), None, None, None, None, None, None, 0, None) == B.MOE_OK
     assert lib.moe_combine(byref(cfg), None, None, None, None, None, None) == B.MOE_OK
+    assert lib.moe_expert_ffn_down(byref(cfg), None, None, None, None, None, None, 0, None) == B.MOE_OK
     assert lib.moe_forward(byref(cfg), None, None, None, None, None, None, None, None, None, 0, None) == B.MOE_OK
     assert lib.moe_quantize_fp8(0, 128, 128, None, B.MOE_BF16, None, None, None) == B.MOE_OK
 

@@ -436,6 +436,125 @@ def test_expert_ffn_fp8_partial_tiles(sizes, shared):
     _log(f"[expert_ffn fp8 partial tiles {sizes}] y_sorted err {e} y_shared err {e2}")
 
 
+# The expert FFN's two GEMMs one at a time.  GEMM1 + SwiGLU: the h that
+# moe_expert_ffn leaves in the workspace (moe_workspace_ffn_h) against the
+# oracle's h, and for fp8 its codes and scales against the oracle's h within
+# the rounding of E4M3.  GEMM2: the oracle's h (its bf16 or fp32 rounding, or
+# for fp8 the oracle's codes and scales of it) written into a fresh workspace,
+# then moe_expert_ffn_down, against the oracle's product of that same h with
+# W2.  Fed the same h, GEMM2 must agree to the output's own rounding, also at
+# I = 256, where in the whole layer one h code rounding the other way (fp32
+# vs fp64 h) moves a y row visibly.
+FFN_STAGES = ["small_fp8", "t12_fp8", "t20_fp8", "small_fp8_tiles", "fp8_k_not_4x", "fp8_rest_tiles", "small_bf16",
+              "t16_e4_halves_bf16", "t24_bf16", "t600_e32_bf16", "k_eq_E_bf16", "tiny_f32", "t20_f32"]
+
+# GEMM2 on a given h: fp32 accumulation, then one rounding to the output
+# type.  bf16 keeps 8 significant bits, so that rounding moves an element by
+# at most 2^-8 of its value: per element (relative to max(|o|, rms(o)))
+# 2^-8 plus 1/16 of it for the fp32 sums, and 2^-8 in Frobenius norm.  fp32
+# outputs stay within the fp32 bounds.
+GEMM2_TOL = {"bf16": (2.0 ** -8 * 1.0625, 2.0 ** -8), "f32": (1e-4, 1e-5)}
+
+
+def _h_fp32_bound(a, w1, w3):
+    """Per-element bound on an fp32 h = SiLU(g) * u, g = a W1^T, u = a W3^T,
+    against exact arithmetic: a K-term fp32 sum in any order is within
+    K 2^-24 of the sum of its terms' magnitudes (plus one rounding per scale
+    multiply, hence K + 2), and the error of g and u reaches h through
+    |SiLU'(g)| |u| and |SiLU(g)|; SiLU's own roundings add a few ulps of h."""
+    g, u = a @ w1.T, a @ w3.T
+    ga, ua = np.abs(a) @ np.abs(w1).T, np.abs(a) @ np.abs(w3).T
+    s = 1.0 / (1.0 + np.exp(-g))
+    dsilu = s * (1.0 + g * (1.0 - s))
+    gamma = (a.shape[1] + 2) * 2.0 ** -24
+    return gamma * (np.abs(dsilu) * ga * np.abs(u) + np.abs(g * s) * ua) + 2.0 ** -20 * np.abs(g * s * u)
+
+
+def _ws_view(ws, off, rows, cols, dtype):
+    n = rows * cols * torch.empty((), dtype=dtype).element_size()
+    return ws[off:off + n].view(dtype).reshape(rows, cols)
+
+
+@pytest.mark.parametrize("name", FFN_STAGES)
+def test_expert_ffn_gemm1_and_gemm2_apart(name):
+    cfg = SMALL[name]
+    inp, gin = _small_inputs(cfg)
+    ow = oracle.OracleWeights.from_inputs(inp)
+    x = oracle.to_f64(inp.x)
+    r = oracle.route(x, oracle.to_f64(inp.wg), oracle.to_f64(inp.bias), cfg.k, cfg.score,
+                     n_group=cfg.n_group, topk_group=cfg.topk_group)
+    d = oracle.dispatch(r["idx"], cfg.E)
+    xa = oracle.prepare_activations(x, ow.fp8, ow.block)
+    T, k, I, P, qb = cfg.T, cfg.k, cfg.I, cfg.T * cfg.k, cfg.quant_block
+    rows = P + (T if cfg.I_shared else 0)
+
+    # (rows of h, tokens, weights) per routed group, then the shared expert
+    parts = []
+    for e in range(cfg.E):
+        lo, hi = int(d["offsets"][e]), int(d["offsets"][e + 1])
+        if hi > lo:
+            parts.append((slice(lo, hi), np.asarray(d["sorted_pair"][lo:hi]) // k, ow.expert(e)))
+    if cfg.I_shared:
+        parts.append((slice(P, P + T), np.arange(T), ow.shared()))
+    used = np.zeros(rows, dtype=bool)
+    h_ref = np.zeros((rows, I))
+    h_bound = np.zeros((rows, I))
+    for sl, toks, (w1, w3, _) in parts:
+        used[sl] = True
+        h_ref[sl] = oracle.swiglu_hidden(xa[toks], w1, w3)
+        h_bound[sl] = _h_fp32_bound(xa[toks], w1, w3)
+
+    mc = moe.cfg_from(cfg)
+    wts = moe.Weights.from_inputs(gin)
+    off = torch.from_numpy(d["offsets"].astype(np.int32)).to(DEV)
+    sp = torch.from_numpy(d["sorted_pair"].astype(np.int32)).to(DEV)
+    h_off, hq_off, hs_off = moe.moe_workspace_ffn_h(mc)
+    h_dt = torch.bfloat16 if cfg.w_dtype == "bf16" else torch.float32
+
+    # GEMM1 + SwiGLU (and for fp8 the quantisation of h)
+    ws = moe.alloc_workspace(mc, DEV)
+    moe.moe_expert_ffn(mc, gin.x, off, sp, wts, ws=ws)
+    torch.cuda.synchronize()
+    h_gpu = to_np(_ws_view(ws, h_off, rows, I, h_dt))[used]
+    if cfg.w_dtype == "bf16":   # h rounded once to bf16
+        eh = assert_outputs_close(h_gpu, h_ref[used], "bf16", "h")
+    else:
+        ratio = np.abs(h_gpu - h_ref[used]) / np.maximum(h_bound[used], 1e-300)
+        eh = (float(ratio.max()), output_errors(h_gpu, h_ref[used]))
+        assert eh[0] <= 1.0, f"h beyond its fp32 accumulation bound: worst error / bound {eh[0]:.3e}, {eh[1]}"
+    if ow.fp8:
+        # E4M3 keeps 4 significant bits (rounding within 2^-4 of a normal
+        # value) and steps by 2^-9 below 2^-6, in units of the block scale
+        codes = to_np(_ws_view(ws, hq_off, rows, I, torch.uint8))[used]
+        scales = to_np(_ws_view(ws, hs_off, rows, I // qb, torch.float32))[used]
+        deq = oracle.e4m3_decode(codes) * np.repeat(scales, qb, axis=1)
+        ref_scale = np.repeat(oracle.quantize_rows_fp8(h_ref[used], qb)[1], qb, axis=1)
+        qbound = 2.0 ** -4 * np.abs(h_ref[used]) + 1.07 * h_bound[used] + 2.0 ** -10 * 1.01 * ref_scale
+        qr = float((np.abs(deq - h_ref[used]) / qbound).max())
+        assert qr <= 1.0, f"h codes and scales beyond E4M3 rounding of h: worst error / bound {qr:.3e}"
+
+    # GEMM2 alone on the oracle's h
+    ws2 = moe.alloc_workspace(mc, DEV)
+    y_ref = np.zeros((rows, cfg.H))
+    if ow.fp8:
+        codes, scales, h_in = oracle.quantize_rows_fp8(h_ref, qb)
+        _ws_view(ws2, hq_off, rows, I, torch.uint8).copy_(torch.from_numpy(codes))
+        _ws_view(ws2, hs_off, rows, I // qb, torch.float32).copy_(torch.from_numpy(scales.astype(np.float32)))
+    else:
+        h_t = torch.from_numpy(h_ref).to(h_dt)
+        _ws_view(ws2, h_off, rows, I, h_dt).copy_(h_t)
+        h_in = h_t.double().numpy()
+    for sl, _, (_, _, w2) in parts:
+        y_ref[sl] = h_in[sl] @ w2.T
+    ys, ysh = moe.moe_expert_ffn_down(mc, off, sp, wts, ws2)
+    torch.cuda.synchronize()
+    y_gpu = to_np(ys) if not cfg.I_shared else np.concatenate([to_np(ys), to_np(ysh)])
+    el, fr = output_errors(y_gpu[used], y_ref[used])
+    tol = GEMM2_TOL[cfg.act_dtype]
+    assert el <= tol[0] and fr <= tol[1], f"GEMM2 on the oracle's h: elementwise {el:.3e}, Frobenius {fr:.3e}, tol {tol}"
+    _log(f"[ffn gemm1/gemm2 {name}] h err {eh} GEMM2 err ({el:.3e}, {fr:.3e})")
+
+
 @pytest.mark.parametrize("name", sorted(SMALL))
 def test_combine_small(name):
     cfg = SMALL[name]

@@ -334,6 +334,20 @@ def test_swiglu_quantises_h_per_row_block():
     assert not np.allclose(y, h, rtol=1e-6)                   # quantisation really happened
 
 
+def test_swiglu_hidden_is_the_dense_gated_product():
+    """h alone, against torch's SiLU and linear layers; and y = h W2^T."""
+    rng = np.random.default_rng(17)
+    I, H = 48, 16
+    a = rng.normal(size=(5, H))
+    w1, w3 = rng.normal(size=(I, H)), rng.normal(size=(I, H))
+    w2 = rng.normal(size=(H, I))
+    h = oracle.swiglu_hidden(a, w1, w3)
+    np.testing.assert_allclose(h, _dense_swiglu_torch(a, w1, w3, np.eye(I)), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(oracle.swiglu_ffn(a, w1, w3, w2), h @ w2.T, rtol=1e-12, atol=1e-14)
+    # the gate, not the up projection, goes through SiLU
+    assert not np.allclose(h, oracle.swiglu_hidden(a, w3, w1), rtol=1e-3)
+
+
 def test_fp8_weights_dequantise_per_row_block():
     cfg = get_config("tiny_f32").with_(w_dtype="fp8", act_dtype="bf16", T=2, E=2, k=1, H=256, I=128)
     inp = make_inputs(cfg, "cpu")
