@@ -118,19 +118,21 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // SiLU on the hardware exp2 and reciprocal (about 1 ulp each, a few
 // instructions instead of ~25 for the IEEE expf and division), for outputs
-// rounded to bf16 afterwards: its error is some 10^-7 relative against the
-// 2^-9 of the rounding.  Saturates like silu: g -> -inf gives -0, +inf gives g.
+// rounded to bf16 or E4M3 afterwards: its error is some 10^-7 relative
+// against the 2^-9 or 2^-4 of the rounding (and against the ~10^-5 with
+// which the fp8 matrix instructions sum g and u).  Saturates like silu:
+// g -> -inf gives -0, +inf gives g.
 __device__ __forceinline__ float silu_fast(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504088896341f * g));
 }
 
-// The SwiGLU activation for an output of dtype DT: the fast form where the
-// result is rounded to bf16, the IEEE one where it stays fp32 (the fp32
-// layer, and the fp8 layer's h, which is block-quantised next).
+// The SwiGLU activation for weights of dtype DT: the fast form where h is
+// rounded to bf16 or block-quantised to E4M3 next, the IEEE one where h
+// stays fp32 (the fp32 layer).
 template <int DT>
 __device__ __forceinline__ float silu_for(float g) {
-  if constexpr (DT == MOE_BF16) return silu_fast(g);
-  else return silu(g);
+  if constexpr (DT == MOE_F32) return silu(g);
+  else return silu_fast(g);
 }
 
 // ------------------------------------------------------------------ host-side launch helpers
