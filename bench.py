@@ -68,7 +68,8 @@ def kernel_models(cfg, counts):
     Bytes count what the operation must move at least once: the weights of
     the groups it serves (with fp8 scales), the activation rows it reads and
     the outputs it writes.  h is bf16 for bf16 weights and fp32 otherwise (the
-    fp8 layer reads h as e4m3 codes plus scales in the down projection).
+    fp8 layer reads h as e4m3 codes plus scales in the down projection, and
+    its routed tiles write those codes and scales instead of h).
     """
     T, H, E, k, I = cfg.T, cfg.H, cfg.E, cfg.k, cfg.I
     fp8 = cfg.w_dtype == "fp8"
@@ -82,6 +83,9 @@ def kernel_models(cfg, counts):
     sc13 = (2 * I // br) * (H // qb) * 4 if fp8 else 0
     sc2 = (H // br) * (I // qb) * 4 if fp8 else 0
     groups = [int(c) for c in counts]
+    # fp8 with more than 16 rows per routed expert on average (and T > 32):
+    # the routed tiles quantise h in GEMM1's epilogue
+    tile_quant = fp8 and T > SKINNY_ROWS and (T * k) // E > SKINNY_ROWS // 2
     regions = ("skinny", "tiled", "tiled128", "shared_skinny", "shared_tiled", "shared_tiled128")
     m = {f"ffn_gemm{g}_{r}": {"bytes": 0, "flops": 0} for g in (1, 2) for r in regions}
     # (rows, region): a group of > 32 rows takes 256-row tiles; with fp8
@@ -116,7 +120,8 @@ def kernel_models(cfg, counts):
         if mg == 0:
             continue
         g1, g2 = m[f"ffn_gemm1_{reg}"], m[f"ffn_gemm2_{reg}"]
-        g1["bytes"] += 2 * I * H * wb + sc13 + mg * H * a1b + mg * I * hb_out + (mg * H // qb * 4 if fp8 else 0)
+        h_out = mg * I + mg * (I // qb) * 4 if tile_quant and reg in ("tiled", "tiled128") else mg * I * hb_out
+        g1["bytes"] += 2 * I * H * wb + sc13 + mg * H * a1b + h_out + (mg * H // qb * 4 if fp8 else 0)
         g1["flops"] += 2 * mg * 2 * I * H
         g2["bytes"] += H * I * wb + sc2 + mg * I * a2b + mg * H * ab + (mg * I // qb * 4 if fp8 else 0)
         g2["flops"] += 2 * mg * H * I

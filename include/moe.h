@@ -129,7 +129,10 @@ int moe_workspace_size(const moe_cfg* cfg, size_t* bytes);
  * the down projection reads (same article, "Quantization").  h has P + T
  * rows of I (P = T * k): row s < offsets[E] is pair sorted_pair[s]'s, in
  * dispatch order; rows P .. P + T - 1 are the shared expert's when
- * I_shared > 0.  Other rows are unspecified.
+ * I_shared > 0.  Other rows are unspecified.  With fp8 weights the codes
+ * and scales are what the down projection reads; h itself is then scratch
+ * (routed groups of more than 32 rows quantise their rows inside GEMM1 and
+ * never write them to h).
  *   h_offset   byte offset of h: bf16 for bf16 weights, fp32 otherwise
  *   hq_offset  fp8 weights: byte offset of h's E4M3 codes [P + T, I]
  *   hs_offset  fp8 weights: byte offset of their fp32 scales

@@ -51,6 +51,7 @@ struct Args {
   int mid_rest;                 // 1: a group's last m mod 256 rows take 128-row tiles; 0: one more 256-row tile
   int shared_tiled;             // 1: the shared expert (group E) is in the routed tile lists, no launches of its own
   int first_mode;               // host side: 1 runs GEMM1 then GEMM2; 2 runs GEMM2 alone on the h in place
+  int tile_quant;               // fp8: routed GEMM1 tiles write h's codes and scales instead of h
 };
 
 struct Group {

@@ -601,6 +601,49 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
     __syncthreads();
     const int ncols = MODE == 1 ? a.I : a.H;            // row length of h or y (a multiple of 8)
     const int col0 = nt * OC;
+    if constexpr (FP8 && MODE == 1 && !SHARED) {
+      if (a.tile_quant) {
+        // A routed fp8 tile's 128 h columns are one quantisation block of each
+        // row (I is a multiple of 128): the tile writes the E4M3 codes and the
+        // block's scale, as the quantiser would from the same fp32 values, and
+        // h itself never goes to memory.  8 lanes per row, 16 values each.
+        static_assert(OC == 128, "one 128-column quantisation block per tile row");
+        const int bpr = a.I >> 7;                         // blocks per row of h
+        uint8_t* qbase = const_cast<uint8_t*>(a.a2) + (size_t)(gr.slot0 + row0) * a.I + col0;
+        float* sbase = const_cast<float*>(a.a2s) + (size_t)(gr.slot0 + row0) * bpr + nt;
+        for (int id0 = 0; id0 < rows * 8; id0 += 512) {   // the same trip count for every lane (shuffles)
+          const int id = id0 + tid, r = id >> 3, part = id & 7;
+          const bool ok = r < rows;
+          float v[16];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const f32x4 w = ok ? *reinterpret_cast<const f32x4*>(lt + r * S + part * 64 + c * 16)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[4 * c + q] = w[q];
+          }
+          float amax = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+          for (int o = 4; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+          if (ok) {
+            const float scale = amax == 0.f ? 1.0f : amax / 448.0f;
+            uint32_t w4[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              w4[c] = 0;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) w4[c] |= f32_to_e4m3(v[4 * c + q] / scale) << (8 * q);
+            }
+            const i32x4 codes = {(int)w4[0], (int)w4[1], (int)w4[2], (int)w4[3]};
+            __builtin_nontemporal_store(codes, reinterpret_cast<i32x4*>(qbase + (size_t)r * a.I + part * 16));
+            if (part == 0) sbase[(size_t)r * bpr] = scale;
+          }
+        }
+        return;
+      }
+    }
     uint8_t* obase = MODE == 1 ? a.h + (size_t)(gr.slot0 + row0) * ncols * ES
                                : (gr.routed ? a.y_sorted : a.y_shared) + (size_t)out_row(a, gr, row0) * ncols * ES;
     for (int id = tid; id < rows * CPR; id += 512) {

@@ -64,6 +64,28 @@ def test_prefill_layer_model():
     assert not bench.shared_in_lists(get_config("clustered2048_fp8"))
 
 
+def test_fp8_routed_tiles_write_h_codes_and_scales():
+    """fp8: a routed group of 33..128 rows takes one 128-row tile, whose GEMM1
+    writes h's E4M3 codes and one fp32 scale per 128 values; a streaming
+    group writes fp32 h (quantised by a separate launch); the shared expert's
+    own tiles write fp32 h."""
+    cfg = get_config("clustered2048_fp8")
+    H, I, qb = cfg.H, cfg.I, cfg.quant_block
+    w13 = 2 * I * H + (2 * I) * (H // qb) * 4            # codes and 1 x 128 scales
+    counts = [100, 20] + [0] * (cfg.E - 2)
+    models, _ = bench.kernel_models(cfg.with_(I_shared=0), counts)
+    assert models["ffn_gemm1_tiled128"]["bytes"] == w13 + 100 * H + 100 * H // qb * 4 + 100 * I + 100 * I // qb * 4
+    assert models["ffn_gemm1_skinny"]["bytes"] == w13 + 20 * H + 20 * H // qb * 4 + 20 * I * 4
+    models, _ = bench.kernel_models(cfg, [0] * cfg.E)
+    T = cfg.T
+    assert models["ffn_gemm1_shared_tiled"]["bytes"] == w13 + T * H + T * H // qb * 4 + T * I * 4
+    # a few rows per expert on average (decode256_fp8): any tile writes fp32 h
+    dcfg = get_config("decode256_fp8").with_(I_shared=0)
+    models, _ = bench.kernel_models(dcfg, [100] + [0] * (dcfg.E - 1))
+    w13d = 2 * I * H + (2 * I // dcfg.w_block_rows) * (H // qb) * 4
+    assert models["ffn_gemm1_tiled128"]["bytes"] == w13d + 100 * H + 100 * H // qb * 4 + 100 * I * 4
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)

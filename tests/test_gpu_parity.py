@@ -74,6 +74,10 @@ SMALL = {
                                                            E=4, k=2, I=2048, I_shared=2048),
     "fp8_full_and_rest": get_config("decode16_fp8").with_(name="fp8_full_and_rest", T=700, H=512, E=4, k=2,
                                                          I=2048, I_shared=2048),
+    # fp8 with a few rows per expert on average (P / E = 6) but skewed routing: the groups above 32
+    # rows take tiles that write fp32 h, quantised with every other row by one launch
+    "fp8_few_rows_skewed": get_config("clustered2048_fp8").with_(name="fp8_few_rows_skewed", routing="zipf", T=100,
+                                                                H=512, E=64, k=4, I=256, I_shared=256),
     # 512+ bf16 tokens: the LDS-staged router with K split in two, tiled and streaming groups
     "t600_e32_bf16": get_config("decode16").with_(name="t600_e32_bf16", routing="zipf", T=600, H=2048, E=32, k=4,
                                                   I=256, I_shared=256),
@@ -445,7 +449,8 @@ def test_expert_ffn_fp8_partial_tiles(sizes, shared):
 # W2.  Fed the same h, GEMM2 must agree to the output's own rounding, also at
 # I = 256, where in the whole layer one h code rounding the other way (fp32
 # vs fp64 h) moves a y row visibly.
-FFN_STAGES = ["small_fp8", "t12_fp8", "t20_fp8", "small_fp8_tiles", "fp8_k_not_4x", "fp8_rest_tiles", "small_bf16",
+FFN_STAGES = ["small_fp8", "t12_fp8", "t20_fp8", "small_fp8_tiles", "fp8_k_not_4x", "fp8_rest_tiles",
+              "fp8_few_rows_skewed", "small_bf16",
               "t16_e4_halves_bf16", "t24_bf16", "t600_e32_bf16", "k_eq_E_bf16", "tiny_f32", "t20_f32"]
 
 # GEMM2 on a given h: fp32 accumulation, then one rounding to the output
@@ -518,10 +523,12 @@ def test_expert_ffn_gemm1_and_gemm2_apart(name):
     h_gpu = to_np(_ws_view(ws, h_off, rows, I, h_dt))[used]
     if cfg.w_dtype == "bf16":   # h rounded once to bf16
         eh = assert_outputs_close(h_gpu, h_ref[used], "bf16", "h")
-    else:
+    elif cfg.w_dtype == "f32":
         ratio = np.abs(h_gpu - h_ref[used]) / np.maximum(h_bound[used], 1e-300)
         eh = (float(ratio.max()), output_errors(h_gpu, h_ref[used]))
         assert eh[0] <= 1.0, f"h beyond its fp32 accumulation bound: worst error / bound {eh[0]:.3e}, {eh[1]}"
+    else:   # fp8: the codes and scales below are the output (tiled groups never write h itself)
+        eh = None
     if ow.fp8:
         # E4M3 keeps 4 significant bits (rounding within 2^-4 of a normal
         # value) and steps by 2^-9 below 2^-6, in units of the block scale
@@ -532,6 +539,11 @@ def test_expert_ffn_gemm1_and_gemm2_apart(name):
         qbound = 2.0 ** -4 * np.abs(h_ref[used]) + 1.07 * h_bound[used] + 2.0 ** -10 * 1.01 * ref_scale
         qr = float((np.abs(deq - h_ref[used]) / qbound).max())
         assert qr <= 1.0, f"h codes and scales beyond E4M3 rounding of h: worst error / bound {qr:.3e}"
+        # the scales themselves: amax / 448 of h, within h's fp32 error
+        ref_s = oracle.quantize_rows_fp8(h_ref[used], qb)[1]
+        amax_bound = np.max((h_bound[used]).reshape(-1, I // qb, qb), axis=2) / 448.0
+        assert np.all(np.abs(scales - ref_s) <= 1.01 * amax_bound + 2.0 ** -23 * ref_s), "h scales"
+        eh = ("codes / E4M3 bound", qr)
 
     # GEMM2 alone on the oracle's h
     ws2 = moe.alloc_workspace(mc, DEV)
