@@ -518,8 +518,14 @@ def test_expert_ffn_gemm1_and_gemm2_apart(name):
 
     # GEMM1 + SwiGLU (and for fp8 the quantisation of h)
     ws = moe.alloc_workspace(mc, DEV)
-    moe.moe_expert_ffn(mc, gin.x, off, sp, wts, ws=ws)
+    ys_full, ysh_full = moe.moe_expert_ffn(mc, gin.x, off, sp, wts, ws=ws)
+    # the down projection alone on the h that call left runs the same kernels: the same bits
+    ys_down, ysh_down = moe.moe_expert_ffn_down(mc, off, sp, wts, ws)
     torch.cuda.synchronize()
+    valid = int(d["offsets"][-1])
+    assert torch.equal(ys_down[:valid], ys_full[:valid])
+    if cfg.I_shared:
+        assert torch.equal(ysh_down, ysh_full)
     h_gpu = to_np(_ws_view(ws, h_off, rows, I, h_dt))[used]
     if cfg.w_dtype == "bf16":   # h rounded once to bf16
         eh = assert_outputs_close(h_gpu, h_ref[used], "bf16", "h")
