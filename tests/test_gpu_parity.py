@@ -614,6 +614,48 @@ def test_forward_small(name):
     _log(f"[forward {name}] near-ties={near} excluded={len(mism)} err={err}")
 
 
+def _random_configs(n, seed=2024):
+    """n layers drawn from a seeded generator across the accepted shapes:
+    1..300 tokens, H and I of several multiples of 64 (of 128 for fp8, with
+    I >= 1024 there, where one h code rounding the other way stays within the
+    fp8 bound), 1..64 experts, k up to 8, with or without a shared expert,
+    random or Zipf routing, and all three weight dtypes (fp8 in both scale
+    layouts).  Every draw takes whichever streaming / tiled paths its group
+    sizes call for."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        kind = ["bf16", "fp8", "fp8_tiles", "f32"][i % 4]
+        base = {"bf16": "decode16", "fp8": "clustered2048_fp8", "fp8_tiles": "decode16_fp8", "f32": "tiny_f32"}[kind]
+        fp8 = kind.startswith("fp8")
+        E = int(rng.integers(1, 65))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.choice([int(rng.integers(1, 33)), int(rng.integers(33, 301))]))
+        H = int(rng.choice([256, 384, 512, 768, 1024])) if not fp8 else int(rng.choice([256, 512, 768, 1024]))
+        I = int(rng.choice([128, 192, 256, 384, 512])) if not fp8 else int(rng.choice([1024, 1152, 2048]))
+        out.append(get_config(base).with_(name=f"rand{i}_{kind}", routing=str(rng.choice(["random", "zipf"])),
+                                          T=T, H=H, E=E, k=k, I=I, I_shared=int(rng.choice([0, I]))))
+    return out
+
+
+RANDOM_LAYERS = _random_configs(24)
+
+
+@pytest.mark.parametrize("cfg", RANDOM_LAYERS, ids=[c.name for c in RANDOM_LAYERS])
+def test_forward_random_layers(cfg):
+    _log(f"[forward random] {cfg.name}: T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} I={cfg.I} "
+         f"I_shared={cfg.I_shared} {cfg.w_dtype} {cfg.routing}")
+    inp, gin = _small_inputs(cfg)
+    ref = oracle.forward(inp)
+    y, idx, w, counts = moe.moe_forward(moe.cfg_from(cfg), gin.x, gin.wg, gin.bias, moe.Weights.from_inputs(gin),
+                                        return_routing=True)
+    torch.cuda.synchronize()
+    near, mism = compare_routing(idx, w, ref["route"], cfg.k)
+    keep = np.setdiff1d(np.arange(cfg.T), mism)
+    err = assert_outputs_close(to_np(y)[keep], ref["y"][keep], tol_key(cfg), "y")
+    _log(f"[forward random {cfg.name}] near-ties={near} excluded={len(mism)} err={err}")
+
+
 @pytest.mark.parametrize("name", ["tiny_f32", "small_bf16", "small_fp8", "t16_e4_halves_bf16", "t600_e32_bf16"])
 def test_forward_matches_stages_bitwise(name):
     """Up to 4096 pairs moe_forward builds the FFN work lists inside its
