@@ -87,6 +87,33 @@ SMALL = {
 }
 
 
+def _random_configs(n, seed=2024):
+    """n layers drawn from a seeded generator across the accepted shapes:
+    1..300 tokens, H and I of several multiples of 64 (of 128 for fp8, with
+    I >= 1024 there, where one h code rounding the other way stays within the
+    fp8 bound), 1..64 experts, k up to 8, with or without a shared expert,
+    random or Zipf routing, and all three weight dtypes (fp8 in both scale
+    layouts).  Every draw takes whichever streaming / tiled paths its group
+    sizes call for."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        kind = ["bf16", "fp8", "fp8_tiles", "f32"][i % 4]
+        base = {"bf16": "decode16", "fp8": "clustered2048_fp8", "fp8_tiles": "decode16_fp8", "f32": "tiny_f32"}[kind]
+        fp8 = kind.startswith("fp8")
+        E = int(rng.integers(1, 65))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.choice([int(rng.integers(1, 33)), int(rng.integers(33, 301))]))
+        H = int(rng.choice([256, 384, 512, 768, 1024])) if not fp8 else int(rng.choice([256, 512, 768, 1024]))
+        I = int(rng.choice([128, 192, 256, 384, 512])) if not fp8 else int(rng.choice([1024, 1152, 2048]))
+        out.append(get_config(base).with_(name=f"rand{i}_{kind}", routing=str(rng.choice(["random", "zipf"])),
+                                          T=T, H=H, E=E, k=k, I=I, I_shared=int(rng.choice([0, I]))))
+    return out
+
+
+RANDOM_LAYERS = _random_configs(24)
+
+
 def _small_inputs(cfg):
     inp = make_inputs(cfg, "cpu")
     gpu = make_inputs(cfg, "cpu")
@@ -480,9 +507,13 @@ def _ws_view(ws, off, rows, cols, dtype):
     return ws[off:off + n].view(dtype).reshape(rows, cols)
 
 
-@pytest.mark.parametrize("name", FFN_STAGES)
-def test_expert_ffn_gemm1_and_gemm2_apart(name):
-    cfg = SMALL[name]
+def _ffn_stage_cases():
+    return [SMALL[n] for n in FFN_STAGES] + RANDOM_LAYERS[::3]
+
+
+@pytest.mark.parametrize("cfg", _ffn_stage_cases(), ids=[c.name for c in _ffn_stage_cases()])
+def test_expert_ffn_gemm1_and_gemm2_apart(cfg):
+    name = cfg.name
     inp, gin = _small_inputs(cfg)
     ow = oracle.OracleWeights.from_inputs(inp)
     x = oracle.to_f64(inp.x)
@@ -612,33 +643,6 @@ def test_forward_small(name):
         np.testing.assert_array_equal(to_np(counts), ref["dispatch"]["counts"])
     err = assert_outputs_close(to_np(y)[keep], ref["y"][keep], tol_key(cfg), "y")
     _log(f"[forward {name}] near-ties={near} excluded={len(mism)} err={err}")
-
-
-def _random_configs(n, seed=2024):
-    """n layers drawn from a seeded generator across the accepted shapes:
-    1..300 tokens, H and I of several multiples of 64 (of 128 for fp8, with
-    I >= 1024 there, where one h code rounding the other way stays within the
-    fp8 bound), 1..64 experts, k up to 8, with or without a shared expert,
-    random or Zipf routing, and all three weight dtypes (fp8 in both scale
-    layouts).  Every draw takes whichever streaming / tiled paths its group
-    sizes call for."""
-    rng = np.random.default_rng(seed)
-    out = []
-    for i in range(n):
-        kind = ["bf16", "fp8", "fp8_tiles", "f32"][i % 4]
-        base = {"bf16": "decode16", "fp8": "clustered2048_fp8", "fp8_tiles": "decode16_fp8", "f32": "tiny_f32"}[kind]
-        fp8 = kind.startswith("fp8")
-        E = int(rng.integers(1, 65))
-        k = int(rng.integers(1, min(E, 8) + 1))
-        T = int(rng.choice([int(rng.integers(1, 33)), int(rng.integers(33, 301))]))
-        H = int(rng.choice([256, 384, 512, 768, 1024])) if not fp8 else int(rng.choice([256, 512, 768, 1024]))
-        I = int(rng.choice([128, 192, 256, 384, 512])) if not fp8 else int(rng.choice([1024, 1152, 2048]))
-        out.append(get_config(base).with_(name=f"rand{i}_{kind}", routing=str(rng.choice(["random", "zipf"])),
-                                          T=T, H=H, E=E, k=k, I=I, I_shared=int(rng.choice([0, I]))))
-    return out
-
-
-RANDOM_LAYERS = _random_configs(24)
 
 
 @pytest.mark.parametrize("cfg", RANDOM_LAYERS, ids=[c.name for c in RANDOM_LAYERS])
