@@ -718,13 +718,16 @@ def test_forward_on_user_stream_is_ordered():
         assert_outputs_close(to_np(y)[keep], ref["y"][keep], tol_key(cfg), "y")
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "small_bf16", "t24_bf16", "small_fp8", "t600_e32_bf16", "fp8_k_not_4x"])
-def test_graph_replays_match_eager(name):
+GRAPH_CASES = [SMALL[n] for n in ("tiny_f32", "small_bf16", "t24_bf16", "small_fp8", "t600_e32_bf16",
+                                   "fp8_k_not_4x")] + RANDOM_LAYERS[2::5]
+
+
+@pytest.mark.parametrize("cfg", GRAPH_CASES, ids=[c.name for c in GRAPH_CASES])
+def test_graph_replays_match_eager(cfg):
     """A captured whole-layer graph, replayed several times with eager work
     and synchronisations in between, gives the eager result bit for bit
     (the layer is deterministic), and follows a change of routing: the
     per-expert counts are read on the device at every launch."""
-    cfg = SMALL[name]
     inp, gin = _small_inputs(cfg)
     mc = moe.cfg_from(cfg)
     w = moe.Weights.from_inputs(gin)
