@@ -317,6 +317,36 @@ def test_dispatch_exact(T, E, k):
         np.testing.assert_array_equal(to_np(g), ref[name], err_msg=name)
 
 
+def _random_dispatch_shapes(n, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        E = int(rng.integers(1, 257))
+        k = int(rng.integers(1, min(E, 32) + 1))
+        T = int(rng.integers(1, 20000 // k + 2))
+        out.append((T, E, k, bool(rng.random() < 0.5)))
+    return out
+
+
+@pytest.mark.parametrize("T,E,k,skew", _random_dispatch_shapes(16))
+def test_dispatch_random_shapes(T, E, k, skew):
+    """Seeded random shapes on both sides of the one-workgroup limit (4096
+    pairs), with uniform or skewed expert choice (a few experts taking most
+    pairs), bit-exact against the oracle's dispatch."""
+    rng = np.random.default_rng(T * 131 + E * 7 + k)
+    if skew:   # distinct experts per token, drawn with Zipf-like weights
+        p = 1.0 / np.arange(1, E + 1) ** 1.2
+        idx = np.stack([rng.choice(E, size=k, replace=False, p=p / p.sum()) for _ in range(T)])
+    else:
+        idx = _distinct_topk(rng, T, E, k)
+    cfg = moe.make_cfg(T, 128, E, k, 64, 64)
+    got = moe.moe_dispatch(cfg, torch.from_numpy(idx.astype(np.int32)).to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.dispatch(idx, E)
+    for name, g in zip(("counts", "offsets", "sorted_pair", "pair_slot"), got):
+        np.testing.assert_array_equal(to_np(g), ref[name], err_msg=name)
+
+
 def test_dispatch_maximum_pairs():
     """The largest call the library accepts, T * k = 2^24 pairs (E = 256,
     k = 8), against the definitions the oracle's loops are pinned to (too
