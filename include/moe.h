@@ -57,7 +57,7 @@ typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
 
 typedef struct {
   int32_t T;           /* tokens, >= 0 */
-  int32_t H;           /* hidden size; multiple of 64 (of quant_block for FP8) */
+  int32_t H;           /* hidden size; multiple of 128 */
   int32_t E;           /* routed experts in this call, 1..256 */
   int32_t k;           /* experts per token, 1..min(E, 32) */
   int32_t I;           /* routed-expert intermediate size; multiple of 64 (quant_block for FP8) */

@@ -203,6 +203,41 @@ def test_route_many_tokens(name):
     _route_check(cfg, x, wg, bias)
 
 
+def _random_router_cfgs(n, seed=31):
+    """Router shapes on every kernel's side of its limits: 1..3000 tokens
+    (the one-launch router below 512 bf16 / 1024 fp32 tokens, the LDS-staged
+    or 16-token kernels above), E up to 256 (with expert groups when E has a
+    divisor that allows them), k up to 8, sigmoid or softmax, H from 256 to
+    4096."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        f32 = i % 3 == 2
+        E = int(rng.integers(2, 257))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.integers(1, 512)) if i % 2 == 0 else int(rng.integers(512, 3001))
+        H = 128 * int(rng.integers(2, 33))
+        score = str(rng.choice(["sigmoid", "softmax"]))
+        ng = [g for g in (2, 4, 8) if E % g == 0 and E // g >= 2 and k <= (E // g) * max(1, g // 2)]
+        n_group = int(rng.choice(ng)) if ng and rng.random() < 0.4 else 1
+        topk_group = max(1, n_group // 2)
+        base = get_config("tiny_f32") if f32 else get_config("decode16")
+        out.append(base.with_(name=f"route_rand{i}", routing=str(rng.choice(["random", "zipf"])), T=T, H=H, E=E,
+                              k=k, score=score, n_group=n_group, topk_group=topk_group))
+    return out
+
+
+ROUTER_RANDOM = _random_router_cfgs(18)
+
+
+@pytest.mark.parametrize("cfg", ROUTER_RANDOM, ids=[c.name for c in ROUTER_RANDOM])
+def test_route_random_shapes(cfg):
+    _log(f"[route random] {cfg.name}: T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} {cfg.score} {cfg.act_dtype} "
+         f"groups {cfg.n_group}/{cfg.topk_group}")
+    x, wg, bias = make_router_inputs(cfg, "cpu")
+    _route_check(cfg, x, wg, bias)
+
+
 @pytest.mark.parametrize("name", ["decode16", "decode256"])
 def test_route_one_launch_leaves_counters_zero(name):
     """The one-launch router counts finished workgroups per token tile in the
