@@ -506,6 +506,35 @@ def test_expert_ffn_fp8_tile_bound(sizes):
     _log(f"[expert_ffn tile bound {sizes}] y_sorted err {e}")
 
 
+BOUNDARY_SIZES = [1, 8, 9, 16, 17, 32, 33, 64, 127, 128, 129, 255, 256, 257, 511, 513, 0]
+
+
+@pytest.mark.parametrize("kind", ["bf16", "f32", "fp8", "fp8_tiles"])
+def test_expert_ffn_group_size_boundaries(kind):
+    """One group at every row-count boundary of the work lists (the 8 / 16 /
+    32-row streaming classes, 128-row rest tiles, 256-row tiles and their
+    partial tails) and an empty group, k = 1, with a shared expert of all
+    their rows, in each weight dtype."""
+    sizes = BOUNDARY_SIZES
+    E, T = len(sizes), sum(sizes)
+    base = {"bf16": "decode16", "f32": "tiny_f32", "fp8": "clustered2048_fp8", "fp8_tiles": "decode16_fp8"}[kind]
+    I = 2048 if kind.startswith("fp8") else 256
+    cfg = get_config(base).with_(name=f"boundaries_{kind}", routing="random", T=T, H=512, E=E, k=1, I=I, I_shared=I)
+    _log(f"[expert_ffn boundaries {kind}] T={T} E={E}")
+    inp, gin = _small_inputs(cfg)
+    sorted_pair = np.random.default_rng(11).permutation(T).astype(np.int32)
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    ow = oracle.OracleWeights.from_inputs(inp)
+    xa = oracle.prepare_activations(inp.x.double().numpy(), ow.fp8, ow.block)
+    ref_ys, ref_sh = oracle.expert_ffn(xa, offsets, sorted_pair, 1, ow)
+    ys, ysh = moe.moe_expert_ffn(moe.cfg_from(cfg), gin.x, torch.from_numpy(offsets).to(DEV),
+                                 torch.from_numpy(sorted_pair).to(DEV), moe.Weights.from_inputs(gin))
+    torch.cuda.synchronize()
+    e = assert_outputs_close(ys, ref_ys, tol_key(cfg), "y_sorted")
+    e2 = assert_outputs_close(ysh, ref_sh, tol_key(cfg), "y_shared")
+    _log(f"[expert_ffn boundaries {kind}] y_sorted err {e} y_shared err {e2}")
+
+
 @pytest.mark.parametrize("sizes,shared", [([255, 240, 208, 193, 192, 176, 145, 130, 511], False),
                                           ([300, 150, 40, 7], True)])
 def test_expert_ffn_fp8_partial_tiles(sizes, shared):
