@@ -1,8 +1,9 @@
 """moe_forward_noalloc, the entry point for callers that cannot allocate,
 against moe_forward (which takes a workspace): the same kernels, so the same
 bits.  Two calls in a row on the same scratch, the second on a smaller
-input, for a bf16 and an fp8 decode layer; and a layer above the scratch's
-fixed size is refused before anything is enqueued."""
+input, for a bf16 and an fp8 decode layer and for a bf16 and an fp8 layer
+that takes every FFN path; and a layer above the scratch's fixed size is
+refused before anything is enqueued."""
 
 import ctypes
 
@@ -60,12 +61,15 @@ def test_noalloc_equals_forward_twice_second_smaller(name, small_T):
     torch.cuda.empty_cache()
 
 
-def test_noalloc_small_layers_with_shared_fork_paths():
+@pytest.mark.parametrize("base", ["decode16", "clustered2048_fp8"])
+def test_noalloc_small_layers_with_shared_fork_paths(base):
     """A layer whose moe_forward forks the shared expert and the tiled groups
     onto side streams; the no-allocation call keeps everything on one stream
-    and must still give the same bits."""
-    cfg = get_config("decode16").with_(name="noalloc_both", routing="zipf", T=600, H=1024, E=32, k=4, I=256,
-                                       I_shared=256)
+    and must still give the same bits.  In fp8 the first call's routed tiles
+    quantise h in their epilogue (75 rows per expert on average) and the
+    second call's do not (12.5)."""
+    cfg = get_config(base).with_(name=f"noalloc_both_{base}", routing="zipf", T=600, H=1024, E=32, k=4, I=256,
+                                 I_shared=256)
     inp = make_inputs(cfg, DEV)
     _check_pair(cfg, inp, inp.x)
     _check_pair(cfg.with_(T=100), inp, inp.x[:100].contiguous())
