@@ -40,10 +40,11 @@ __global__ __launch_bounds__(256) void dispatch_count_kernel(const int32_t* __re
 // TPE threads per expert (1024 / TPE experts per pass) each own a contiguous
 // run of segments: they total it (8 loads in flight), the runs' totals are
 // scanned in LDS, then each thread writes its segments' bases.
+template <bool PLAN>
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __restrict__ seg_counts, int nseg,
                                                              int E, int tpe, int32_t* __restrict__ seg_base,
                                                              int32_t* __restrict__ counts,
-                                                             int32_t* __restrict__ offsets) {
+                                                             int32_t* __restrict__ offsets, moe::PlanArgs pa) {
   __shared__ int part[1024];
   __shared__ int tot[256];
   const int e = threadIdx.x / tpe;     // expert of this thread (E * tpe <= 1024)
@@ -104,6 +105,14 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(const int32_t* __re
   }
   if (threadIdx.x < E) offsets[threadIdx.x] = threadIdx.x == 0 ? 0 : tot[threadIdx.x - 1];
   if (threadIdx.x == 0) offsets[E] = tot[E - 1];
+  if constexpr (PLAN) {   // the FFN's work lists from the totals (tot[] now holds their inclusive scan)
+    __shared__ int wt[moe::ffn::kPlanLds];
+    const int g = threadIdx.x;
+    int m = 0;   // group g's rows: expert g's total, or all T tokens for the shared expert
+    if (g < E) m = tot[g] - (g == 0 ? 0 : tot[g - 1]);
+    else if (g < pa.G) m = pa.T;
+    moe::ffn::build_plan(pa, m, wt);
+  }
 }
 
 __global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* __restrict__ idx, int P, int E,
@@ -255,10 +264,16 @@ hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, int32_t* counts
   if (e != hipSuccess) return e;
   int tpe = 1;                       // threads per expert in the scan
   while (tpe * 2 * c.E <= 1024 && tpe * 2 <= nseg) tpe *= 2;
-  MOE_LAUNCH("dispatch_scan", dispatch_scan_kernel, dim3(1), dim3(1024), 0, st, seg_counts, nseg, c.E, tpe, seg_base,
-             counts, offsets);
+  if (plan) {   // the scan holds the per-expert totals: it also builds the FFN plan
+    MOE_LAUNCH("dispatch_scan", dispatch_scan_kernel<true>, dim3(1), dim3(1024), 0, st, seg_counts, nseg, c.E, tpe,
+               seg_base, counts, offsets, *plan);
+  } else {
+    MOE_LAUNCH("dispatch_scan", dispatch_scan_kernel<false>, dim3(1), dim3(1024), 0, st, seg_counts, nseg, c.E, tpe,
+               seg_base, counts, offsets, PlanArgs{});
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (plan && planned) *planned = true;
   MOE_LAUNCH("dispatch_scatter", dispatch_scatter_kernel, dim3(nseg), dim3(64), 0, st, idx, P, c.E, offsets, seg_base,
                      sorted_pair, pair_slot);
   return hipGetLastError();

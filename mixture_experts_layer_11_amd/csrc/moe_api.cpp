@@ -379,7 +379,7 @@ int forward_on(const moe_cfg* cfg, const void* x, const void* w_gate, const floa
   if (e != hipSuccess) return hip_fail(e, "moe_forward/route");
   const moe::FfnWs fws = ffn_ws(ws, L);
   const moe::PlanArgs pa = moe::ffn_plan_args(*cfg, fws.plan);
-  bool planned = false;   // the one-workgroup dispatch also builds the FFN plan
+  bool planned = false;   // the dispatch also builds the FFN plan
   e = moe::launch_dispatch(*cfg, idx, counts, offsets, sorted, slot, at<int32_t>(ws, L.seg), st, &pa, &planned);
   if (e != hipSuccess) return hip_fail(e, "moe_forward/dispatch");
   e = moe::launch_expert_ffn(*cfg, x, offsets, sorted, *w, ys, ysh, fws, st, planned, fork);

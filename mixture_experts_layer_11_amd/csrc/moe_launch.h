@@ -51,8 +51,8 @@ PlanArgs ffn_plan_args(const moe_cfg& c, int32_t* plan);
 // ---- dispatch
 constexpr int kDispatchSeg = 256;  // pairs per scatter segment (one wave each)
 size_t dispatch_ws_bytes(const moe_cfg& c);
-// With plan given, the one-workgroup path (up to 4096 pairs) also builds the
-// FFN plan from its counts and sets *planned.
+// With plan given, the one-workgroup path (up to 4096 pairs) or, above it,
+// the scan kernel also builds the FFN plan from the counts and sets *planned.
 hipError_t launch_dispatch(const moe_cfg& c, const int32_t* idx, int32_t* counts, int32_t* offsets,
                            int32_t* sorted_pair, int32_t* pair_slot, int32_t* seg_ws, hipStream_t st,
                            const PlanArgs* plan = nullptr, bool* planned = nullptr);

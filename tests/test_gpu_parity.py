@@ -74,6 +74,11 @@ SMALL = {
                                                            E=4, k=2, I=2048, I_shared=2048),
     "fp8_full_and_rest": get_config("decode16_fp8").with_(name="fp8_full_and_rest", T=700, H=512, E=4, k=2,
                                                          I=2048, I_shared=2048),
+    # more than 4096 pairs: the three-kernel dispatch, whose scan builds moe_forward's plan
+    "many_pairs_fp8": get_config("clustered2048_fp8").with_(name="many_pairs_fp8", routing="zipf", T=1100, H=512,
+                                                           E=32, k=4, I=1024, I_shared=1024),
+    "many_pairs_bf16": get_config("decode16").with_(name="many_pairs_bf16", routing="random", T=1100, H=512,
+                                                   E=64, k=4, I=256, I_shared=256),
     # fp8 with a few rows per expert on average (P / E = 6) but skewed routing: the groups above 32
     # rows take tiles that write fp32 h, quantised with every other row by one launch
     "fp8_few_rows_skewed": get_config("clustered2048_fp8").with_(name="fp8_few_rows_skewed", routing="zipf", T=100,
@@ -754,14 +759,15 @@ def test_forward_random_layers(cfg):
     _log(f"[forward random {cfg.name}] near-ties={near} excluded={len(mism)} err={err}")
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "small_bf16", "small_fp8", "t16_e4_halves_bf16", "t600_e32_bf16"])
+@pytest.mark.parametrize("name", ["tiny_f32", "small_bf16", "small_fp8", "t16_e4_halves_bf16", "t600_e32_bf16",
+                                  "many_pairs_fp8", "many_pairs_bf16"])
 def test_forward_matches_stages_bitwise(name):
-    """Up to 4096 pairs moe_forward builds the FFN work lists inside its
-    one-workgroup dispatch; the stage entry points build them in the FFN's own
-    plan kernel.  Both must give the same bits (t600_e32_bf16, 2400 pairs,
-    also takes the LDS-staged router)."""
+    """moe_forward builds the FFN work lists inside its dispatch (up to 4096
+    pairs in the one-workgroup kernel, above that in the scan kernel); the
+    stage entry points build them in the FFN's own plan kernel.  Both must
+    give the same bits (t600_e32_bf16, 2400 pairs, also takes the LDS-staged
+    router; the many_pairs layers, 4400 pairs, the three-kernel dispatch)."""
     cfg = SMALL[name]
-    assert cfg.T * cfg.k <= 4096
     _, gin = _small_inputs(cfg)
     mc = moe.cfg_from(cfg)
     wts = moe.Weights.from_inputs(gin)
