@@ -243,8 +243,8 @@ __global__ __launch_bounds__(512, 1) void ffn_fat_kernel(Args a, int ntn) {
   // matrix and one expert's weights below 4 GB) the direct loads go through
   // buffer resources instead: the A base is the activation matrix, the B
   // base this group's weights, with per-lane 32-bit offsets.
-  static_assert(!BUF || (DT == MOE_BF16 && TM == 256) || (FP8 && (TM == 128 || C::TN == 128)),
-                "buffer loads: bf16 256-row tiles and fp8 tiles 128 rows or 128 columns wide");
+  static_assert(!BUF || (DT == MOE_BF16 && TM == 256) || FP8,
+                "buffer loads: bf16 256-row tiles and fp8 tiles");
   const __amdgpu_buffer_rsrc_t rsa =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(asrc), 0, (int)0xffffffffu, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsb =
@@ -719,10 +719,9 @@ hipError_t launch_tiled(int mode, bool shared, int tm, bool stream_w, int tiles,
   // into one expert's weights
   const size_t esz = DT == MOE_BF16 ? 2 : 1;
   const size_t act_bytes = mode == 1 ? (size_t)a.T * a.H * esz : (size_t)(a.P + a.T) * a.I * esz;
-  // (fp8 256-row tiles 256 columns wide sit at the register limit: the buffer form spills there)
-  const bool buf = (DT == MOE_BF16 ? tm == 256 : FP8 && (tm == 128 || tile_cols(DT, mode, tm, shared) == 128)) &&
+  const bool buf = (DT == MOE_BF16 ? tm == 256 : FP8) &&
                    act_bytes <= 0xffffffffu && (size_t)2 * a.I * a.H * esz <= 0xffffffffu;
-#define MOE_BUFV(M, TMV, S) ((DT == MOE_BF16 && TMV == 256) || (FP8 && (TMV == 128 || tile_cols(DT, M, TMV, S) == 128)))
+#define MOE_BUFV(M, TMV, S) ((DT == MOE_BF16 && TMV == 256) || FP8)
 #define MOE_TLB(M, S, TMV, SWV) \
   (buf ? (FP8 && blk ? launch_fat<DT, M, S, TMV, FP8, SWV, MOE_BUFV(M, TMV, S)>(name, grid, ntn, a, st) \
                      : launch_fat<DT, M, S, TMV, false, SWV, MOE_BUFV(M, TMV, S)>(name, grid, ntn, a, st)) \
